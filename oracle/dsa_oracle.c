@@ -1,0 +1,372 @@
+/*
+ * dsa_oracle.c -- plain fp64 reference for the DSA path (see dsa_oracle.h
+ * for the sources [R], [M], [S]).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the library.  Every function is the
+ * plain definition written out with nested loops in fp64; nothing is blocked,
+ * fused or reordered.  Query rows are spread over threads, each row is
+ * computed start-to-finish by one thread in a fixed order, so the result does
+ * not depend on the thread count.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -shared -fPIC -pthread -lm
+ */
+#include "dsa_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Element decoders, written from the bit layouts.                           */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 mantissa bits. */
+static double bf16_value(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int m = h & 0x7f;
+    double v;
+    if (e == 0xff)
+        v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -126 - 7);              /* subnormal: m/128 * 2^-126 */
+    else
+        v = ldexp(1.0 + (double)m / 128.0, e - 127);
+    return sign ? -v : v;
+}
+
+/* OCP FP8 E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no
+ * infinities, S.1111.111 is NaN, largest finite value 448. */
+static double e4m3_value(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xf;
+    int m = c & 0x7;
+    double v;
+    if (e == 0xf && m == 0x7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -6 - 3);                /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+void oref_bf16_to_f64(const uint16_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = bf16_value(src[i]);
+}
+
+void oref_e4m3_to_f64(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = e4m3_value(src[i]);
+}
+
+/* Element i of an array of the given encoding, as fp64. */
+static double elem(int dtype, const void *base, int64_t i)
+{
+    switch (dtype) {
+    case OREF_F32: return (double)((const float *)base)[i];
+    case OREF_BF16: return bf16_value(((const uint16_t *)base)[i]);
+    default: return e4m3_value(((const uint8_t *)base)[i]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cache addressing.  Paged layout: fixed-size token pages reached through a  */
+/* per-sequence page table ([S] section 5.3: page size 64).                  */
+/* ------------------------------------------------------------------------ */
+
+int64_t oref_cache_row(const oref_rows *rows, int32_t b, int64_t s)
+{
+    if (rows->page_table) {
+        int64_t page = rows->page_table[(int64_t)b * rows->max_pages + s / rows->page_size];
+        return page * rows->page_size + s % rows->page_size;
+    }
+    return rows->seq_start[b] + s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A tiny fork/join helper: thread t handles list items i with i % T == t.   */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*row_fn)(void *ctx, int32_t i);
+typedef struct { row_fn fn; void *ctx; int32_t n, t, T; } worker_arg;
+
+static void *worker(void *p)
+{
+    worker_arg *a = (worker_arg *)p;
+    for (int32_t i = a->t; i < a->n; i += a->T) a->fn(a->ctx, i);
+    return NULL;
+}
+
+static void run_rows(row_fn fn, void *ctx, int32_t n, int n_threads)
+{
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > 256) n_threads = 256;
+    if (n_threads > n) n_threads = n > 0 ? n : 1;
+    if (n_threads == 1) {
+        for (int32_t i = 0; i < n; ++i) fn(ctx, i);
+        return;
+    }
+    pthread_t th[256];
+    worker_arg args[256];
+    for (int t = 0; t < n_threads; ++t) {
+        args[t] = (worker_arg){fn, ctx, n, t, n_threads};
+        pthread_create(&th[t], NULL, worker, &args[t]);
+    }
+    for (int t = 0; t < n_threads; ++t) pthread_join(th[t], NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lightning indexer ([R] ①):                                                */
+/*   I[t,s] = sum_j w[t,j] * ReLU(q[t,j,:] . k[s,:])                         */
+/* over the preceding tokens s of the query's sequence (self included).      */
+/* One key per token, shared by all indexer heads (k carries no head index). */
+/* FP8 inputs are dequantised literally: value = decode(code) * scale, with  */
+/* a scale per (row, head) for q and per cache row for k.                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int dtype, H, D;
+    const void *q; const float *q_scale; const float *w;
+    const void *k; const float *k_scale;
+    const oref_rows *rows; const int32_t *which;
+    double *out; int64_t ld;
+} idx_ctx;
+
+static void indexer_row(void *p, int32_t i)
+{
+    const idx_ctx *c = (const idx_ctx *)p;
+    const int32_t r = c->which[i];
+    const int32_t b = c->rows->row_seq[r];
+    const int64_t n = c->rows->row_len[r];
+    const int H = c->H, D = c->D;
+    double *qv = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *kv = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int j = 0; j < H; ++j) {
+        double sq = (c->dtype == OREF_E4M3) ? (double)c->q_scale[(int64_t)r * H + j] : 1.0;
+        for (int d = 0; d < D; ++d)
+            qv[j * D + d] = elem(c->dtype, c->q, ((int64_t)r * H + j) * D + d) * sq;
+    }
+    for (int64_t s = 0; s < n; ++s) {
+        int64_t row = oref_cache_row(c->rows, b, s);
+        double sk = (c->dtype == OREF_E4M3) ? (double)c->k_scale[row] : 1.0;
+        for (int d = 0; d < D; ++d) kv[d] = elem(c->dtype, c->k, row * D + d) * sk;
+        double x = 0.0;
+        for (int j = 0; j < H; ++j) {
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += qv[j * D + d] * kv[d];
+            double relu = dot > 0.0 ? dot : 0.0;
+            x += (double)c->w[(int64_t)r * H + j] * relu;
+        }
+        c->out[(int64_t)i * c->ld + s] = x;
+    }
+    free(qv);
+    free(kv);
+}
+
+int oref_indexer(int dtype, int n_heads, int head_dim,
+                 const void *q, const float *q_scale, const float *w,
+                 const void *k, const float *k_scale,
+                 const oref_rows *rows, const int32_t *which, int32_t n_which,
+                 double *out, int64_t ld, int n_threads)
+{
+    if (dtype < OREF_F32 || dtype > OREF_E4M3 || n_heads <= 0 || head_dim <= 0) return 1;
+    if (dtype == OREF_E4M3 && (!q_scale || !k_scale)) return 1;
+    idx_ctx c = {dtype, n_heads, head_dim, q, q_scale, w, k, k_scale, rows, which, out, ld};
+    run_rows(indexer_row, &c, n_which, n_threads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fine-grained token selection ([R] ②; [M] "Indexer-selected sparse         */
+/* attention": k is capped at the row length, indices are int32).           */
+/* Order positions by score descending, then position ascending (the lower   */
+/* position wins a tie; -0 and +0 compare equal as doubles), keep the first  */
+/* k_eff = min(k, n).  The result is a set; it is written in ascending       */
+/* position order and padded with -1.                                        */
+/* ------------------------------------------------------------------------ */
+
+typedef struct { double v; int32_t pos; } scored;
+
+static int by_score_then_pos(const void *a, const void *b)
+{
+    const scored *x = (const scored *)a, *y = (const scored *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int ascending_i32(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+int oref_topk_row(const double *x, int64_t n, int32_t k, int32_t *out)
+{
+    int64_t keff = n < k ? n : k;
+    scored *all = (scored *)malloc(sizeof(scored) * (size_t)(n > 0 ? n : 1));
+    for (int64_t s = 0; s < n; ++s) { all[s].v = x[s]; all[s].pos = (int32_t)s; }
+    qsort(all, (size_t)n, sizeof(scored), by_score_then_pos);
+    for (int64_t i = 0; i < keff; ++i) out[i] = all[i].pos;
+    qsort(out, (size_t)keff, sizeof(int32_t), ascending_i32);
+    for (int64_t i = keff; i < k; ++i) out[i] = -1;
+    free(all);
+    return (int)keff;
+}
+
+typedef struct {
+    const double *x; const float *xf; int64_t ld; const int32_t *len; int32_t k; int32_t *out;
+} topk_ctx;
+
+static void topk_row_job(void *p, int32_t r)
+{
+    const topk_ctx *c = (const topk_ctx *)p;
+    int64_t n = c->len[r];
+    if (c->x) {
+        oref_topk_row(c->x + (int64_t)r * c->ld, n, c->k, c->out + (int64_t)r * c->k);
+    } else {
+        double *row = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        for (int64_t s = 0; s < n; ++s) row[s] = (double)c->xf[(int64_t)r * c->ld + s];
+        oref_topk_row(row, n, c->k, c->out + (int64_t)r * c->k);
+        free(row);
+    }
+}
+
+int oref_topk_rows(const double *x, int64_t ld, const int32_t *len, int32_t n_rows,
+                   int32_t k, int32_t *out, int n_threads)
+{
+    if (k <= 0) return 1;
+    topk_ctx c = {x, NULL, ld, len, k, out};
+    run_rows(topk_row_job, &c, n_rows, n_threads);
+    return 0;
+}
+
+int oref_topk_rows_f32(const float *x, int64_t ld, const int32_t *len, int32_t n_rows,
+                       int32_t k, int32_t *out, int n_threads)
+{
+    if (k <= 0) return 1;
+    topk_ctx c = {NULL, x, ld, len, k, out};
+    run_rows(topk_row_job, &c, n_rows, n_threads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention in MQA mode ([R], MLA-based implementation: every latent entry  */
+/* is shared by all query heads; [M] "Multi-head latent attention": the      */
+/* entry is the kv_lora_rank latent followed by the RoPE key).  Keys are the */
+/* full d_qk-wide entries, values are the first d_v dims (the latent).  Plain */
+/* softmax with no sink term and no output gate ([M] "Learnable attention    */
+/* sink", "Gated attention output": both absent).                            */
+/*   z_s = scale * q_h . C_s ;  o_h = sum_s softmax(z)_s * C_s[0:d_v] ;      */
+/*   lse_h = ln sum_s exp(z_s)                                              */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int dtype, H, Dqk, Dv; double scale;
+    const void *q; const void *kv; const int32_t *idx; int32_t k;
+    const oref_rows *rows; const int32_t *which;
+    double *out; double *lse;
+} mla_ctx;
+
+static void attend_row(const mla_ctx *c, int32_t i, const int64_t *pos, int64_t n_pos)
+{
+    const int32_t r = c->which[i];
+    const int32_t b = c->rows->row_seq[r];
+    const int H = c->H, Dqk = c->Dqk, Dv = c->Dv;
+    double *ent = (double *)malloc(sizeof(double) * (size_t)(n_pos > 0 ? n_pos : 1) * Dqk);
+    double *z = (double *)malloc(sizeof(double) * (size_t)(n_pos > 0 ? n_pos : 1));
+    double *qh = (double *)malloc(sizeof(double) * (size_t)Dqk);
+    for (int64_t e = 0; e < n_pos; ++e) {
+        int64_t row = oref_cache_row(c->rows, b, pos[e]);
+        for (int d = 0; d < Dqk; ++d) ent[e * Dqk + d] = elem(c->dtype, c->kv, row * Dqk + d);
+    }
+    for (int h = 0; h < H; ++h) {
+        double *o = c->out + ((int64_t)i * H + h) * Dv;
+        for (int d = 0; d < Dqk; ++d) qh[d] = elem(c->dtype, c->q, ((int64_t)r * H + h) * Dqk + d);
+        if (n_pos == 0) {
+            for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+            if (c->lse) c->lse[(int64_t)i * H + h] = -INFINITY;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int64_t e = 0; e < n_pos; ++e) {
+            double dot = 0.0;
+            for (int d = 0; d < Dqk; ++d) dot += qh[d] * ent[e * Dqk + d];
+            z[e] = c->scale * dot;
+            if (z[e] > m) m = z[e];
+        }
+        double l = 0.0;
+        for (int64_t e = 0; e < n_pos; ++e) {
+            z[e] = exp(z[e] - m);                    /* unnormalised weight e^{z-m} */
+            l += z[e];
+        }
+        for (int d = 0; d < Dv; ++d) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < n_pos; ++e) acc += z[e] * ent[e * Dqk + d];
+            o[d] = acc / l;
+        }
+        if (c->lse) c->lse[(int64_t)i * H + h] = m + log(l);
+    }
+    free(ent);
+    free(z);
+    free(qh);
+}
+
+/* idx entries that are negative or not below the row length are skipped;
+ * duplicates (never produced by top-k) would be counted once per occurrence. */
+static void sparse_row(void *p, int32_t i)
+{
+    const mla_ctx *c = (const mla_ctx *)p;
+    const int32_t r = c->which[i];
+    const int64_t n = c->rows->row_len[r];
+    int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (size_t)c->k);
+    int64_t n_pos = 0;
+    for (int32_t j = 0; j < c->k; ++j) {
+        int64_t s = c->idx[(int64_t)r * c->k + j];
+        if (s >= 0 && s < n) pos[n_pos++] = s;
+    }
+    attend_row(c, i, pos, n_pos);
+    free(pos);
+}
+
+static void dense_row(void *p, int32_t i)
+{
+    const mla_ctx *c = (const mla_ctx *)p;
+    const int64_t n = c->rows->row_len[c->which[i]];
+    int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+    for (int64_t s = 0; s < n; ++s) pos[s] = s;
+    attend_row(c, i, pos, n);
+    free(pos);
+}
+
+int oref_sparse_mla(int dtype, int n_heads, int d_qk, int d_v, double scale,
+                    const void *q, const void *kv, const int32_t *idx, int32_t k,
+                    const oref_rows *rows, const int32_t *which, int32_t n_which,
+                    double *out, double *lse, int n_threads)
+{
+    if (dtype < OREF_F32 || dtype > OREF_BF16 || n_heads <= 0 || d_qk <= 0 || d_v <= 0 ||
+        d_v > d_qk || k <= 0)
+        return 1;
+    mla_ctx c = {dtype, n_heads, d_qk, d_v, scale, q, kv, idx, k, rows, which, out, lse};
+    run_rows(sparse_row, &c, n_which, n_threads);
+    return 0;
+}
+
+int oref_dense_mqa(int dtype, int n_heads, int d_qk, int d_v, double scale,
+                   const void *q, const void *kv,
+                   const oref_rows *rows, const int32_t *which, int32_t n_which,
+                   double *out, double *lse, int n_threads)
+{
+    if (dtype < OREF_F32 || dtype > OREF_BF16 || n_heads <= 0 || d_qk <= 0 || d_v <= 0 ||
+        d_v > d_qk)
+        return 1;
+    mla_ctx c = {dtype, n_heads, d_qk, d_v, scale, q, kv, NULL, 0, rows, which, out, lse};
+    run_rows(dense_row, &c, n_which, n_threads);
+    return 0;
+}
