@@ -1,0 +1,164 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * The path has three stages, each an entry point below:
+ *   1. lightning indexer: I[t,s] = sum_j w[t,j] * ReLU(q^I[t,j,:] . k^I[s,:]) over the
+ *      preceding tokens s of the query's sequence;
+ *   2. fine-grained token selection: the top-k positions of each score row;
+ *   3. MLA in MQA mode over only the selected entries: every query head attends to
+ *      the same latent cache entries (latent || RoPE key), values are the latent part.
+ * Sources, by page title and section:
+ *   "DeepSeek-V3.2 技术报告摘要" (summary of the V3.2 technical report), section 1,
+ *     "关键设计：DeepSeek Sparse Attention (DSA)": ① Lightning Indexer (the formula,
+ *     FP8 support), ② Fine-grained Token Selection, and the paragraph on the MLA-based
+ *     implementation (MQA mode, one latent entry shared by all query heads);
+ *   "DeepSeek-V3.2 -- Model techniques map", table "Checked in its code", rows
+ *     "Indexer-selected sparse attention" (k = min(index_topk, row length), int32
+ *     indices [B,S,topk]), "Multi-head latent attention" (entry = 512 latent + 64
+ *     RoPE), "Partial RoPE" (192-d q/k head), "Learnable attention sink" and "Gated
+ *     attention output" (both absent);
+ *   "DeepSeek-V3.2" (model docs), section 1 "Model Introduction" (64 indexer heads x
+ *     128, index_topk 2048, 128 heads) and section 5.3 "Rollout & SGLang" (bf16 cache,
+ *     page size 64);
+ *   "DeepSeek-V3.2-Exp" README, section "开源内核" (open kernels): an indexer-logits
+ *     kernel with a paged version, separate from the sparse attention kernel.
+ *
+ * Conventions for every entry point
+ *   - Tensors are row-major, contiguous, in device memory unless marked "host".
+ *   - The caller owns every buffer, workspace included (sized by the *_workspace_size
+ *     queries).  The library allocates nothing, keeps no state between calls and
+ *     holds no pointer after it returns.  The dsa_rows struct is read on the host
+ *     during the call only.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream) and the call returns after launch: inputs must stay alive until the
+ *     stream has passed the work.  No host synchronisation, no device-to-host read,
+ *     so a sequence of calls can be captured into a HIP graph.
+ *   - Errors: the return value is a dsa_status; 0 is success.  All argument checks
+ *     run on the host before anything is enqueued, so on an error nothing is
+ *     launched.  A failed launch returns DSA_ERR_HIP.  Device-side contract breaches
+ *     (a row_len beyond the cache, a page id out of range, a row_seq beyond num_seqs)
+ *     are not checked and give undefined results.
+ *   - num_rows == 0 is a valid empty call: DSA_OK, nothing launched.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_PAGE_SIZE 64     /* tokens per cache page in the paged layout */
+#define DSA_MAX_TOPK 2048    /* largest supported k (index_topk of the model) */
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent layout */
+    DSA_ERR_UNSUPPORTED = 2,   /* valid request this build has no kernel for */
+    DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
+    DSA_ERR_HIP = 4            /* a HIP launch failed */
+} dsa_status;
+
+typedef enum {
+    DSA_F32 = 0,               /* IEEE binary32 */
+    DSA_BF16 = 1,              /* bfloat16 */
+    DSA_FP8_E4M3 = 2           /* OCP FP8 E4M3FN codes plus fp32 scales */
+} dsa_dtype;
+
+/* A ragged batch of query rows.  Query row r belongs to sequence row_seq[r] and sees
+ * that sequence's positions 0 .. row_len[r]-1 (causal, its own token included: a
+ * decode row has row_len = context length, prefill row t of a sequence has t+1).
+ * The cache layout is either contiguous or paged:
+ *   contiguous: position s of sequence b is cache row seq_start[b] + s;
+ *   paged:      it is row page_table[b*max_pages + s/64]*64 + s%64 of a [pages,64,..]
+ *               cache (64-token pages reached through a per-sequence page table). */
+typedef struct dsa_rows {
+    int32_t        num_rows;     /* host: R >= 0 */
+    int32_t        num_seqs;     /* host: B >= 1 */
+    const int32_t *row_seq;      /* [R] sequence of each row, in [0, B) */
+    const int32_t *row_len;      /* [R] visible length, 1 <= row_len[r] <= max_row_len */
+    int32_t        max_row_len;  /* host: >= every row_len; sizes grids, bounds ld */
+    const int64_t *seq_start;    /* [B] contiguous layout, NULL for paged */
+    const int32_t *page_table;   /* [B, max_pages] paged layout, NULL for contiguous */
+    int32_t        max_pages;    /* host: paged only, >= ceil(max_row_len / 64) */
+    int32_t        page_size;    /* host: paged only, must be DSA_PAGE_SIZE */
+} dsa_rows;
+
+/* Human-readable name of a status code (static storage). */
+const char *dsa_status_string(int status);
+/* DSA_ABI_VERSION of the loaded library. */
+int dsa_abi_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * Stage 1: lightning-indexer scores ("DeepSeek-V3.2 技术报告摘要", section 1, DSA ①).
+ *   logits[r, s] = sum_{j<H} w[r,j] * ReLU(q[r,j,:] . k[cache row of s,:])  for s < row_len[r]
+ * q       [R, H, D]  in `dtype` (f32, bf16, or e4m3 codes)
+ * q_scale [R, H] f32 dequantisation scale of q (fp8 only, else NULL): q = code * q_scale
+ * k       contiguous: [cache rows, D]; paged: [pages, 64, D]  in `dtype`
+ * k_scale contiguous: [cache rows]; paged: [pages, 64]  f32 (fp8 only, else NULL)
+ * w       [R, H] f32 head weights
+ * logits  [R, ld_logits] f32 output; entries s >= row_len[r] are not written.
+ * Supported: f32 with 1 <= H <= 64, 1 <= D <= 256; bf16 and fp8 with (H, D) = (64, 128).
+ * dsa_indexer_logits needs rows->seq_start, dsa_indexer_logits_paged rows->page_table. */
+int dsa_indexer_logits(const dsa_rows *rows, int dtype, int n_heads, int head_dim,
+                       const void *q, const float *q_scale,
+                       const void *k, const float *k_scale,
+                       const float *w, float *logits, int64_t ld_logits, void *stream);
+int dsa_indexer_logits_paged(const dsa_rows *rows, int dtype, int n_heads, int head_dim,
+                             const void *q, const float *q_scale,
+                             const void *k, const float *k_scale,
+                             const float *w, float *logits, int64_t ld_logits, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Stage 2: top-k token selection ("DeepSeek-V3.2 技术报告摘要", section 1, DSA ②;
+ * "Model techniques map", "Indexer-selected sparse attention": k capped at the row
+ * length, int32 indices).
+ * For each row r with n = row_len[r] valid scores logits[r, 0..n): the k_eff = min(k, n)
+ * positions with the largest scores, ties broken toward the lower position, -0 == +0.
+ * idx [R, k] int32 output: the selected positions in ascending order, then -1 padding.
+ * Scores must be finite (NaN and infinities are not supported).  1 <= k <= 2048.
+ * ws / ws_bytes: device scratch of at least dsa_topk_workspace_size(R, max_row_len, k)
+ * bytes (may be NULL when that is 0); its contents need no initialisation. */
+size_t dsa_topk_workspace_size(int num_rows, int max_row_len, int k);
+int dsa_topk(const float *logits, int64_t ld_logits, const int32_t *row_len, int num_rows,
+             int max_row_len, int k, int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Stage 3: MLA in MQA mode over the selected entries ("DeepSeek-V3.2 技术报告摘要",
+ * section 1, MLA-based implementation; "Model techniques map", "Multi-head latent
+ * attention", "Learnable attention sink", "Gated attention output").
+ * For row r, head h, and the valid entries s of idx[r,:] (0 <= s < row_len[r];
+ * negative or larger entries are skipped):
+ *   z_s = softmax_scale * q[r,h,:] . C[s,:]          (C = the d_qk-wide cache entry)
+ *   out[r,h,:] = sum_s softmax(z)_s * C[s, 0:d_v]    (values = first d_v dims)
+ *   lse[r,h]   = ln sum_s exp(z_s)
+ * A row with no valid entry gets out = 0 and lse = -inf.  No sink, no gate.
+ * q   [R, H, d_qk] in `dtype`;  kv contiguous [cache rows, d_qk] / paged [pages, 64, d_qk]
+ * idx [R, k] int32 positions (e.g. from dsa_topk);  out [R, H, d_v] in `dtype`
+ * lse [R, H] f32 natural-log sum-exp, or NULL.
+ * Supported: f32 with 1 <= H <= 128, d_v <= d_qk <= 256;
+ *            bf16 with H = 64 or 128, d_qk = 576, d_v = 512.  1 <= k <= 2048.
+ * The decode entry points split the selections over several workgroups for few-row
+ * batches and need ws of dsa_sparse_mla_workspace_size(R, H, d_v, k) bytes;
+ * dsa_sparse_mla_prefill never splits and takes ws = NULL, ws_bytes = 0. */
+size_t dsa_sparse_mla_workspace_size(int num_rows, int n_heads, int d_v, int k);
+int dsa_sparse_mla_decode(const dsa_rows *rows, int dtype, int n_heads, int d_qk, int d_v,
+                          float softmax_scale, const void *q, const void *kv,
+                          const int32_t *idx, int k, void *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+int dsa_sparse_mla_decode_paged(const dsa_rows *rows, int dtype, int n_heads, int d_qk, int d_v,
+                                float softmax_scale, const void *q, const void *kv,
+                                const int32_t *idx, int k, void *out, float *lse,
+                                void *ws, size_t ws_bytes, void *stream);
+int dsa_sparse_mla_prefill(const dsa_rows *rows, int dtype, int n_heads, int d_qk, int d_v,
+                           float softmax_scale, const void *q, const void *kv,
+                           const int32_t *idx, int k, void *out, float *lse,
+                           void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,256 @@
+"""Python binding of libdsa.so, the MI355X DeepSeek Sparse Attention hot path.
+
+Thin ctypes marshalling over the C ABI in ``include/dsa.h``: each function checks the
+torch tensors it is given (device, dtype, contiguity), passes raw device pointers and
+the current HIP stream, and raises ``RuntimeError`` on a non-zero status.  All the
+work runs in the HIP kernels of ``csrc/``; nothing here computes.
+
+Build the library with ``python -m sparse_attention_08_amd.build`` (or
+``__graft_entry__.build()``); importing this module without it fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+PAGE_SIZE = 64
+MAX_TOPK = 2048
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+          4: "DSA_ERR_HIP"}
+
+
+class DsaRows(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32),
+                ("row_seq", ctypes.c_void_p),
+                ("row_len", ctypes.c_void_p),
+                ("max_row_len", ctypes.c_int32),
+                ("seq_start", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libdsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m sparse_attention_08_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    rows_p = ctypes.POINTER(DsaRows)
+    lib.dsa_status_string.argtypes = [i32]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_abi_version.argtypes = []
+    lib.dsa_abi_version.restype = i32
+    for name in ("dsa_indexer_logits", "dsa_indexer_logits_paged"):
+        f = getattr(lib, name)
+        f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]
+        f.restype = i32
+    lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
+    lib.dsa_topk_workspace_size.restype = sz
+    lib.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.dsa_topk.restype = i32
+    lib.dsa_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dsa_sparse_mla_workspace_size.restype = sz
+    for name in ("dsa_sparse_mla_decode", "dsa_sparse_mla_decode_paged", "dsa_sparse_mla_prefill"):
+        f = getattr(lib, name)
+        f.argtypes = [rows_p, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        f.restype = i32
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().dsa_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load_library().dsa_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise RuntimeError(f"{what}: {status_string(status)}")
+
+
+def _stream() -> Optional[int]:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP8_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+class Rows:
+    """A ragged batch of query rows (device arrays plus the host-side sizes).
+
+    Row r belongs to sequence ``row_seq[r]`` and sees positions ``0 .. row_len[r]-1``.
+    Give ``seq_start`` for a contiguous cache or ``page_table`` for a 64-token paged cache.
+    """
+
+    def __init__(self, row_seq: torch.Tensor, row_len: torch.Tensor, max_row_len: int, num_seqs: int,
+                 seq_start: Optional[torch.Tensor] = None, page_table: Optional[torch.Tensor] = None,
+                 page_size: int = PAGE_SIZE):
+        self.row_seq = _dev(row_seq, "row_seq", (torch.int32,))
+        self.row_len = _dev(row_len, "row_len", (torch.int32,))
+        self.seq_start = None if seq_start is None else _dev(seq_start, "seq_start", (torch.int64,))
+        self.page_table = None if page_table is None else _dev(page_table, "page_table", (torch.int32,))
+        self.max_row_len = int(max_row_len)
+        self.num_seqs = int(num_seqs)
+        self.page_size = int(page_size)
+        self.max_pages = 0 if self.page_table is None else int(self.page_table.shape[-1])
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.row_seq.shape[0])
+
+    @property
+    def paged(self) -> bool:
+        return self.page_table is not None
+
+    def struct(self) -> DsaRows:
+        return DsaRows(self.num_rows, self.num_seqs, _ptr(self.row_seq), _ptr(self.row_len),
+                       self.max_row_len, _ptr(self.seq_start), _ptr(self.page_table), self.max_pages,
+                       self.page_size if self.paged else 0)
+
+
+# --------------------------------------------------------------------------- stage 1
+
+def _indexer(paged: bool, rows: Rows, q, w, k, logits, q_scale=None, k_scale=None):
+    lib = load_library()
+    _dev(q, "q")
+    _dev(k, "k")
+    _dev(w, "w", (torch.float32,))
+    _dev(logits, "logits", (torch.float32,))
+    if q_scale is not None:
+        _dev(q_scale, "q_scale", (torch.float32,))
+    if k_scale is not None:
+        _dev(k_scale, "k_scale", (torch.float32,))
+    if q.dim() != 3:
+        raise ValueError("q must be [R, H, D]")
+    st = rows.struct()
+    fn = lib.dsa_indexer_logits_paged if paged else lib.dsa_indexer_logits
+    s = fn(ctypes.byref(st), dtype_code(q), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(q_scale),
+           _ptr(k), _ptr(k_scale), _ptr(w), _ptr(logits), int(logits.shape[-1]), _stream())
+    _check(s, "dsa_indexer_logits_paged" if paged else "dsa_indexer_logits")
+    return logits
+
+
+def indexer_logits(rows: Rows, q, w, k, logits, q_scale=None, k_scale=None):
+    """Lightning-indexer scores into ``logits`` [R, ld] (contiguous key cache)."""
+    return _indexer(False, rows, q, w, k, logits, q_scale, k_scale)
+
+
+def indexer_logits_paged(rows: Rows, q, w, k, logits, q_scale=None, k_scale=None):
+    """Lightning-indexer scores into ``logits`` [R, ld] (64-token paged key cache)."""
+    return _indexer(True, rows, q, w, k, logits, q_scale, k_scale)
+
+
+# --------------------------------------------------------------------------- stage 2
+
+def topk_workspace_size(num_rows: int, max_row_len: int, k: int) -> int:
+    return int(load_library().dsa_topk_workspace_size(int(num_rows), int(max_row_len), int(k)))
+
+
+def topk(logits, row_len, k: int, max_row_len: int, idx=None, ws=None):
+    """Top-k positions per row (ascending, -1 padded) into ``idx`` [R, k] int32."""
+    lib = load_library()
+    _dev(logits, "logits", (torch.float32,))
+    _dev(row_len, "row_len", (torch.int32,))
+    R = int(logits.shape[0])
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=logits.device)
+    _dev(idx, "idx", (torch.int32,))
+    need = topk_workspace_size(R, max_row_len, k)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    s = lib.dsa_topk(_ptr(logits), int(logits.shape[-1]), _ptr(row_len), R, int(max_row_len), int(k),
+                     _ptr(idx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check(s, "dsa_topk")
+    return idx
+
+
+# --------------------------------------------------------------------------- stage 3
+
+def sparse_mla_workspace_size(num_rows: int, n_heads: int, d_v: int, k: int) -> int:
+    return int(load_library().dsa_sparse_mla_workspace_size(int(num_rows), int(n_heads), int(d_v),
+                                                             int(k)))
+
+
+def _mla(name: str, rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None, ws=None):
+    lib = load_library()
+    _dev(q, "q", (torch.float32, torch.bfloat16))
+    _dev(kv, "kv", (q.dtype,))
+    _dev(idx, "idx", (torch.int32,))
+    if q.dim() != 3:
+        raise ValueError("q must be [R, H, d_qk]")
+    R, H, Dqk = (int(x) for x in q.shape)
+    k = int(idx.shape[-1])
+    if out is None:
+        out = torch.empty((R, H, d_v), dtype=q.dtype, device=q.device)
+    _dev(out, "out", (q.dtype,))
+    if lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    if name != "dsa_sparse_mla_prefill":
+        need = sparse_mla_workspace_size(R, H, d_v, k)
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        ws = None
+    st = rows.struct()
+    s = getattr(lib, name)(ctypes.byref(st), dtype_code(q), H, Dqk, int(d_v), float(scale), _ptr(q),
+                           _ptr(kv), _ptr(idx), k, _ptr(out), _ptr(lse), _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check(s, name)
+    return out
+
+
+def sparse_mla_decode(rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None, ws=None):
+    """Sparse MLA (MQA mode) over idx entries, contiguous latent cache; returns out [R,H,d_v]."""
+    return _mla("dsa_sparse_mla_decode", rows, q, kv, idx, scale, d_v, out, lse, ws)
+
+
+def sparse_mla_decode_paged(rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None,
+                            ws=None):
+    """Sparse MLA (MQA mode) over idx entries, 64-token paged latent cache."""
+    return _mla("dsa_sparse_mla_decode_paged", rows, q, kv, idx, scale, d_v, out, lse, ws)
+
+
+def sparse_mla_prefill(rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None):
+    """Sparse MLA (MQA mode) for many query rows (prefill), contiguous latent cache."""
+    return _mla("dsa_sparse_mla_prefill", rows, q, kv, idx, scale, d_v, out, lse, None)

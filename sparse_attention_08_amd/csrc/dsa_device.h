@@ -1,0 +1,74 @@
+// dsa_device.h -- device-side helpers shared by the DSA kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kPage = 64;          // tokens per cache page
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Where query rows find their cache: contiguous (seq_start) or 64-token pages.
+struct RowsDev {
+  const int32_t *row_seq;
+  const int32_t *row_len;
+  const int64_t *seq_start;   // contiguous layout, else nullptr
+  const int32_t *page_table;  // paged layout, else nullptr
+  int32_t max_pages;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ int64_t cache_row(const RowsDev &rows, int b, int64_t s) {
+  if constexpr (PAGED) {
+    int64_t page = rows.page_table[(int64_t)b * rows.max_pages + (s >> 6)];
+    return page * kPage + (s & (kPage - 1));
+  } else {
+    return rows.seq_start[b] + s;
+  }
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key),
+// with -0 folded onto +0 so the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+}  // namespace dsa

@@ -1,0 +1,47 @@
+// dsa_launch.h -- host-side launchers of the DSA kernels.  Arguments arrive here
+// already validated by the C ABI layer (dsa_api.cpp); these functions only size
+// grids and enqueue kernels, and return the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct RowsHost {
+  int32_t num_rows;
+  int32_t num_seqs;
+  const int32_t *row_seq;
+  const int32_t *row_len;
+  int32_t max_row_len;
+  const int64_t *seq_start;
+  const int32_t *page_table;
+  int32_t max_pages;
+};
+
+// ---- indexer ----
+hipError_t launch_indexer_f32(const RowsHost &rows, bool paged, int H, int D, const float *q,
+                              const float *k, const float *w, float *logits, int64_t ld,
+                              hipStream_t stream);
+// bf16 / fp8 e4m3 with (H, D) = (64, 128), MFMA path
+hipError_t launch_indexer_mfma(const RowsHost &rows, bool paged, bool fp8, const void *q,
+                               const float *q_scale, const void *k, const float *k_scale,
+                               const float *w, float *logits, int64_t ld, hipStream_t stream);
+
+// ---- top-k ----
+size_t topk_workspace_bytes(int num_rows, int max_row_len, int k);
+hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,
+                       int max_row_len, int k, int32_t *idx, void *ws, hipStream_t stream);
+
+// ---- sparse MLA ----
+int mla_num_splits(int num_rows, int n_heads, int k);
+size_t mla_workspace_bytes(int num_rows, int n_heads, int d_v, int k);
+hipError_t launch_mla_f32(const RowsHost &rows, bool paged, int H, int Dqk, int Dv, float scale,
+                          const float *q, const float *kv, const int32_t *idx, int k, float *out,
+                          float *lse, hipStream_t stream);
+// bf16 with d_qk = 576, d_v = 512, H % 16 == 0; splits == 1 writes out/lse directly.
+hipError_t launch_mla_bf16(const RowsHost &rows, bool paged, int H, float scale, const void *q,
+                           const void *kv, const int32_t *idx, int k, void *out, float *lse,
+                           int splits, void *ws, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,136 @@
+"""The C ABI of libdsa.so, checked without a GPU: it loads, exports every function that
+include/dsa.h declares, and rejects bad arguments on the host before any HIP call.
+
+Only argument combinations that fail validation (or are empty) are passed here, so no
+kernel is ever launched; the fake device pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_08_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dsa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "dsa_indexer_logits" in names and "dsa_sparse_mla_decode_paged" in names
+    for n in names:
+        assert hasattr(lib, n), f"libdsa.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert dsa.abi_version() == 1
+    assert dsa.status_string(0) == "DSA_OK"
+    for s in (1, 2, 3, 4):
+        assert dsa.status_string(s).startswith(dsa.STATUS[s])
+    assert "unknown" in dsa.status_string(99)
+
+
+def _rows(num_rows=2, num_seqs=2, max_row_len=100, paged=False, page_size=64, max_pages=None,
+          seq_start=True, page_table=None, row_ptrs=True):
+    if max_pages is None:
+        max_pages = (max_row_len + 63) // 64 if paged else 0
+    return dsa.DsaRows(num_rows, num_seqs, FAKE if row_ptrs else None, FAKE if row_ptrs else None,
+                       max_row_len, FAKE if (seq_start and not paged) else None,
+                       FAKE if (paged or page_table) else None, max_pages, page_size if paged else 0)
+
+
+def _idx(lib, rows, dtype=1, H=64, D=128, ld=100, qs=None, ks=None, paged=False, ptrs=True):
+    fn = lib.dsa_indexer_logits_paged if paged else lib.dsa_indexer_logits
+    p = FAKE if ptrs else None
+    return fn(ctypes.byref(rows) if rows is not None else None, dtype, H, D, p, qs, p, ks, p, p, ld,
+              None)
+
+
+def test_indexer_validation(lib):
+    assert _idx(lib, None) == INVALID
+    assert _idx(lib, _rows(num_rows=0)) == OK                       # empty batch: nothing launched
+    assert _idx(lib, _rows(row_ptrs=False)) == INVALID
+    assert _idx(lib, _rows(num_seqs=0)) == INVALID
+    assert _idx(lib, _rows(max_row_len=0)) == INVALID
+    assert _idx(lib, _rows(), ld=99) == INVALID                     # ld < max_row_len
+    assert _idx(lib, _rows(), dtype=7) == INVALID
+    assert _idx(lib, _rows(), H=0) == INVALID
+    assert _idx(lib, _rows(), ptrs=False) == INVALID
+    assert _idx(lib, _rows(), dtype=2) == INVALID                   # fp8 without scales
+    assert _idx(lib, _rows(), dtype=2, qs=FAKE) == INVALID          # fp8 missing k scale
+    assert _idx(lib, _rows(), dtype=1, qs=FAKE, ks=FAKE) == INVALID  # scales only for fp8
+    assert _idx(lib, _rows(), dtype=1, H=32, D=128) == UNSUPPORTED
+    assert _idx(lib, _rows(), dtype=2, H=64, D=64, qs=FAKE, ks=FAKE) == UNSUPPORTED
+    assert _idx(lib, _rows(), dtype=0, H=65, D=32) == UNSUPPORTED
+    # layout must match the entry point
+    assert _idx(lib, _rows(page_table=True)) == INVALID             # both layouts given
+    assert _idx(lib, _rows(seq_start=False)) == INVALID             # neither
+    assert _idx(lib, _rows(paged=True), paged=True, dtype=9) == INVALID
+    assert _idx(lib, _rows(), paged=True) == INVALID                # contiguous rows, paged call
+    assert _idx(lib, _rows(paged=True, page_size=32), paged=True) == INVALID
+    assert _idx(lib, _rows(paged=True, max_row_len=200, max_pages=3), paged=True) == INVALID
+    assert _idx(lib, _rows(paged=True, num_rows=0), paged=True) == OK
+
+
+def test_topk_validation(lib):
+    f = lib.dsa_topk
+    assert f(FAKE, 100, FAKE, 4, 100, 0, FAKE, None, 0, None) == INVALID       # k = 0
+    assert f(FAKE, 100, FAKE, 4, 100, 2049, FAKE, None, 0, None) == INVALID    # k > 2048
+    assert f(FAKE, 99, FAKE, 4, 100, 16, FAKE, None, 0, None) == INVALID       # ld < max_row_len
+    assert f(None, 100, FAKE, 4, 100, 16, FAKE, None, 0, None) == INVALID
+    assert f(FAKE, 100, FAKE, -1, 100, 16, FAKE, None, 0, None) == INVALID
+    assert f(FAKE, 100, FAKE, 0, 100, 16, FAKE, None, 0, None) == OK           # empty batch
+    assert f(FAKE, 100, FAKE, 4, 0, 16, FAKE, None, 0, None) == INVALID
+    assert dsa.topk_workspace_size(4, 100, 0) == 0
+
+
+def _mla(lib, rows, name="dsa_sparse_mla_decode", dtype=1, H=128, Dqk=576, Dv=512, scale=0.07,
+         k=2048, ws=None, ws_bytes=0, ptrs=True):
+    p = FAKE if ptrs else None
+    return getattr(lib, name)(ctypes.byref(rows), dtype, H, Dqk, Dv, scale, p, p, p, k, p, None, ws,
+                              ws_bytes, None)
+
+
+def test_mla_validation(lib):
+    r8 = _rows(num_rows=8, num_seqs=8)
+    assert _mla(lib, r8, k=0) == INVALID
+    assert _mla(lib, r8, k=2049) == INVALID
+    assert _mla(lib, r8, Dv=600) == INVALID                         # d_v > d_qk
+    assert _mla(lib, r8, scale=float("nan")) == INVALID
+    assert _mla(lib, r8, scale=float("inf")) == INVALID
+    assert _mla(lib, r8, ptrs=False) == INVALID
+    assert _mla(lib, r8, H=96) == UNSUPPORTED
+    assert _mla(lib, r8, Dqk=512) == UNSUPPORTED
+    assert _mla(lib, r8, dtype=2) == UNSUPPORTED                    # no fp8 attention
+    assert _mla(lib, r8, dtype=0, H=129, Dqk=80, Dv=64) == UNSUPPORTED
+    # eight rows split the 2048 slots over several workgroups: a workspace is required
+    need = dsa.sparse_mla_workspace_size(8, 128, 512, 2048)
+    assert need > 0
+    assert _mla(lib, r8) == WORKSPACE
+    assert _mla(lib, r8, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    assert _mla(lib, _rows(num_rows=0)) == OK
+    assert _mla(lib, _rows(), name="dsa_sparse_mla_decode_paged") == INVALID   # layout mismatch
+    assert _mla(lib, _rows(paged=True), name="dsa_sparse_mla_prefill") == INVALID
+
+
+def test_workspace_queries_are_consistent():
+    # few rows: split partials (fp32 [R, splits, H, d_v + 1]); many rows: no split
+    few = dsa.sparse_mla_workspace_size(8, 128, 512, 2048)
+    assert few % (4 * 8 * 128 * 513) == 0
+    assert dsa.sparse_mla_workspace_size(4096, 128, 512, 2048) == 0
+    assert dsa.sparse_mla_workspace_size(0, 128, 512, 2048) == 0

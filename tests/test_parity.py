@@ -1,0 +1,231 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle on the same seeded bytes.
+
+Tolerances: indexer and attention outputs max-abs-relative <= 1e-5 (fp32) / 2e-2
+(bf16, fp8 indexer); top-k index sets bit-exact, both when fed the oracle's scores
+rounded to fp32 and on the GPU's own scores.  Attention is compared on the same index
+set on both sides.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_08_amd as dsa
+import workloads
+from helpers import (TOL, dev_rows, gpu_indexer, gpu_mla, oracle_indexer, oracle_mla, raw, say,
+                     valid_logits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _check_indexer(wl, which, tol):
+    say(f"indexer {wl.name} rows={list(which)[:6]}")
+    g = gpu_indexer(wl).cpu().numpy()
+    ref = oracle_indexer(wl, which=which)
+    lens = wl.row_len.cpu().numpy()
+    gv = valid_logits(g[list(which)], lens, which)
+    rv = valid_logits(ref, lens, which)
+    err = oracle.max_abs_rel(gv, rv)
+    assert err <= tol, f"indexer err {err}"
+    # nothing written beyond a row's length
+    for i, r in enumerate(which):
+        assert np.all(np.isnan(g[r, lens[r]:])), "wrote past row_len"
+    return g, ref, err
+
+
+def _check_topk_on_oracle_scores(wl, ref_scores, which):
+    """GPU top-k fed the oracle's scores rounded to fp32 == oracle top-k on that array."""
+    lens = wl.row_len.cpu().numpy()[list(which)]
+    x32 = np.nan_to_num(ref_scores, nan=0.0).astype(np.float32)
+    say(f"topk on oracle scores {wl.name}")
+    logits = torch.from_numpy(x32).to(DEV)
+    rl = torch.from_numpy(lens.astype(np.int32)).to(DEV)
+    got = dsa.topk(logits, rl, wl.topk, int(lens.max())).cpu().numpy()
+    exp = oracle.topk(x32, lens, wl.topk)
+    assert np.array_equal(got, exp)
+
+
+def _check_topk_on_gpu_scores(wl, g_logits):
+    say(f"topk on gpu scores {wl.name}")
+    lens = wl.row_len.cpu().numpy()
+    got = dsa.topk(torch.from_numpy(g_logits).to(DEV), wl.row_len, wl.topk, wl.max_row_len)
+    exp = oracle.topk(np.nan_to_num(g_logits, nan=0.0).astype(np.float32), lens, wl.topk)
+    assert np.array_equal(got.cpu().numpy(), exp)
+    return got
+
+
+def _check_mla(wl, idx_dev, which, tol):
+    say(f"mla {wl.name} rows={list(which)[:6]}")
+    out, lse = gpu_mla(wl, idx_dev)
+    o = out.float().cpu().numpy()[list(which)]
+    l = lse.cpu().numpy()[list(which)]
+    ref_o, ref_l = oracle_mla(wl, idx_dev.cpu().numpy(), which=which)
+    err = oracle.max_abs_rel(o, ref_o)
+    assert err <= tol, f"attention err {err}"
+    lerr = oracle.max_abs_rel(l, ref_l)
+    assert lerr <= tol, f"lse err {lerr}"
+    return out, lse, err
+
+
+# ------------------------------------------------------------------------ tiny fp32 prefill
+
+def test_c1_tiny_fp32_prefill_full():
+    wl = workloads.config(1).to(DEV)
+    which = list(range(wl.num_rows))
+    g, ref, _ = _check_indexer(wl, which, TOL["f32"])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g)
+    _check_mla(wl, idx, which, TOL["f32"])
+    # rows with at most k predecessors select everything: sparse == dense causal MQA
+    short = list(range(64))
+    out, _ = gpu_mla(wl, idx)
+    dense, _ = oracle.dense_mqa("f32", raw(wl.q), raw(wl.kv), oracle.Rows(
+        np.zeros(256), np.arange(1, 257), seq_start=np.zeros(1)), wl.scale, wl.D_v, which=short)
+    assert oracle.max_abs_rel(out.cpu().numpy()[short], dense) <= TOL["f32"]
+
+
+# ------------------------------------------------------------------------ small ragged decode
+
+RAGGED = [1, 17, 100, 2047, 2048, 2049, 3000, 5001]
+
+
+@pytest.mark.parametrize("idx_dtype,paged", [("bf16", False), ("fp8", False), ("bf16", True),
+                                             ("fp8", True)])
+def test_ragged_decode(idx_dtype, paged):
+    wl = workloads.decode(RAGGED, idx_dtype=idx_dtype, paged=paged, seed=77, device=DEV,
+                          name=f"ragged_{idx_dtype}_{'paged' if paged else 'contig'}")
+    which = list(range(wl.num_rows))
+    g, ref, _ = _check_indexer(wl, which, TOL[idx_dtype])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g)
+    _check_mla(wl, idx, which, TOL["bf16"])
+
+
+def test_paged_physical_permutation_is_bit_identical():
+    wl = workloads.decode([700, 130, 64, 2100], paged=True, seed=31, device=DEV, name="perm")
+    g1 = gpu_indexer(wl)
+    idx = dsa.topk(g1, wl.row_len, wl.topk, wl.max_row_len)
+    o1, l1 = gpu_mla(wl, idx)
+    P = wl.kv.shape[0]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5)).to(DEV)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(P, device=DEV)
+    wl2 = workloads.Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+    # physical page p moves to slot inv[p]
+    wl2.kv = wl.kv[perm].contiguous()
+    wl2.k_idx = wl.k_idx[perm].contiguous()
+    pt = wl.page_table.clone()
+    pt[pt >= 0] = inv[pt[pt >= 0].long()].to(torch.int32)
+    wl2.page_table = pt
+    say("paged permutation")
+    g2 = gpu_indexer(wl2)
+    idx2 = dsa.topk(g2, wl2.row_len, wl2.topk, wl2.max_row_len)
+    o2, l2 = gpu_mla(wl2, idx2)
+    assert torch.equal(torch.nan_to_num(g1, nan=-1.0), torch.nan_to_num(g2, nan=-1.0))
+    assert torch.equal(idx, idx2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------------ full-size configs
+
+@pytest.mark.parametrize("cfg,which", [(2, [0, 17, 63]), (4, [0, 5]), (5, [0, 1, 9, 31])])
+def test_full_decode_configs_sampled(cfg, which):
+    wl = workloads.config(cfg, device=DEV)
+    say(f"full config {cfg} ({wl.name}), sampled rows {which}")
+    g, ref, _ = _check_indexer(wl, which, TOL[wl.idx_dtype])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g.copy())
+    _check_mla(wl, idx, which, TOL["bf16"])
+    del wl
+    torch.cuda.empty_cache()
+
+
+def test_c3_prefill_16k_sampled():
+    wl = workloads.config(3, device=DEV)
+    which = [0, 1, 63, 64, 2046, 2047, 2048, 2049, 9000, 16383]
+    g, ref, _ = _check_indexer(wl, which, TOL["bf16"])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    say("c3 topk all rows")
+    idx = dsa.topk(torch.from_numpy(g).to(DEV), wl.row_len, wl.topk, wl.max_row_len)
+    lens = wl.row_len.cpu().numpy()
+    exp = oracle.topk(np.nan_to_num(g[which], nan=0.0).astype(np.float32), lens[which], wl.topk)
+    assert np.array_equal(idx.cpu().numpy()[which], exp)
+    _check_mla(wl, idx, which, TOL["bf16"])
+    del wl, g
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------ determinism, edges
+
+def test_two_runs_bitwise_equal():
+    wl = workloads.decode([3000, 9000, 40000], idx_dtype="fp8", seed=3, device=DEV, name="det")
+    say("determinism")
+    outs = []
+    for _ in range(2):
+        g = gpu_indexer(wl)
+        idx = dsa.topk(g, wl.row_len, wl.topk, wl.max_row_len)
+        o, l = gpu_mla(wl, idx)
+        outs.append((torch.nan_to_num(g, nan=-1.0), idx, o, l))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def _topk_case(x: np.ndarray, lens, k):
+    xs = torch.from_numpy(x.astype(np.float32)).to(DEV)
+    rl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    got = dsa.topk(xs, rl, k, int(max(lens))).cpu().numpy()
+    exp = oracle.topk(x.astype(np.float32), np.array(lens), k)
+    assert np.array_equal(got, exp)
+
+
+def test_topk_edge_cases():
+    say("topk edges")
+    n = 40000   # beyond the LDS-staged size: streamed passes
+    rng = np.random.default_rng(0)
+    for k in (1, 7, 2048):
+        rows = np.zeros((6, n), dtype=np.float32)
+        rows[0] = 3.5                                          # all equal
+        rows[1] = np.arange(n, dtype=np.float32)               # strictly increasing
+        rows[2] = rng.integers(-3, 4, size=n)                  # heavy ties
+        rows[2][rows[2] == 0] = np.where(rng.random(int((rows[2] == 0).sum())) < 0.5, -0.0, 0.0)
+        rows[3] = -np.abs(rng.standard_normal(n))              # all negative
+        rows[4] = np.where(rng.random(n) < 0.01, 1.0, 0.0)     # sparse ones among zeros
+        rows[5] = rng.standard_normal(n)
+        _topk_case(rows, [n, n, n, 5000, 30000, 1], k)
+        _topk_case(rows[:, :3000], [3000, 2048, 2049, 1, 17, 3000], k)
+
+
+def test_mla_skips_invalid_and_empty_selections():
+    wl = workloads.decode([50, 3000], seed=9, device=DEV, name="mla_edges")
+    idx = torch.full((2, 2048), -1, dtype=torch.int32, device=DEV)
+    idx[0, :10] = torch.tensor([3, -1, 49, 50, 1000, 0, 7, -5, 7, 2], dtype=torch.int32)  # dup 7
+    idx[1, 100:140] = torch.arange(2960, 3000, dtype=torch.int32)
+    rows = dev_rows(wl)
+    say("mla invalid/dup entries")
+    out, lse = gpu_mla(wl, idx)
+    ref_o, ref_l = oracle_mla(wl, idx.cpu().numpy())
+    assert oracle.max_abs_rel(out.float().cpu().numpy(), ref_o) <= TOL["bf16"]
+    assert oracle.max_abs_rel(lse.cpu().numpy(), ref_l) <= TOL["bf16"]
+    empty = torch.full((2, 64), -1, dtype=torch.int32, device=DEV)
+    o2 = torch.empty((2, wl.H, wl.D_v), dtype=torch.bfloat16, device=DEV)
+    l2 = torch.empty((2, wl.H), dtype=torch.float32, device=DEV)
+    dsa.sparse_mla_decode(rows, wl.q, wl.kv, empty, wl.scale, wl.D_v, out=o2, lse=l2)
+    assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
+
+
+def test_prefill_and_decode_entry_points_agree():
+    """Many-row (no split) and few-row (split + combine) attention give the same answer."""
+    wl = workloads.decode([2500, 4000, 9000], seed=12, device=DEV, name="agree")
+    g = gpu_indexer(wl)
+    idx = dsa.topk(g, wl.row_len, wl.topk, wl.max_row_len)
+    rows = dev_rows(wl)
+    say("decode vs prefill entry")
+    a = dsa.sparse_mla_decode(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v)
+    b = dsa.sparse_mla_prefill(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v)
+    ref, _ = oracle_mla(wl, idx.cpu().numpy())
+    assert oracle.max_abs_rel(a.float().cpu().numpy(), ref) <= TOL["bf16"]
+    assert oracle.max_abs_rel(b.float().cpu().numpy(), ref) <= TOL["bf16"]
