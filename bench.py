@@ -1,0 +1,285 @@
+"""Benchmark of the DSA decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: lightning indexer -> top-k -> sparse
+MLA (MQA mode, split-K + combine) for every query row.  The default workload is the
+128K-context decode batch: 8 sequences x 131072 tokens, fp8 e4m3 indexer with per-token
+scales, top-2048, bf16 latent cache 576/512, 128 heads.
+
+Timing: inputs are resident in HBM; before every timed step a 1 GiB read evicts L2 and
+the Infinity Cache (outside the timed region), then HIP events on the launch stream
+bracket the step.  The timed step is the three stages captured once in a HIP graph and
+replayed (--no-graph: eager launches); an eager pass with events between the stages
+gives the per-stage attribution.  value = rows (tokens) / mean step time.
+
+Prints ONE JSON line.  --config selects another of the five workloads for diagnostics.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode tokens/s at 128K ctx; indexer+topk+sparse-MLA % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {"indexer_mfma_kernel": "sparse_attention_08_amd/csrc/indexer.hip",
+                  "mla_bf16_kernel": "sparse_attention_08_amd/csrc/mla.hip",
+                  "topk_rows_kernel": "sparse_attention_08_amd/csrc/topk.hip"}
+
+
+def source_hash(kernel: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--cpu-rows", type=int, default=None, help="rows in the oracle sample")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time eager launches only (default: the step is captured in a HIP graph)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl, lens):
+    """Per-step algorithmic HBM bytes: indexer inputs + keys, gathered entries, q and out."""
+    elt_i = 1 if wl.idx_dtype == "fp8" else (4 if wl.idx_dtype == "f32" else 2)
+    elt_m = 4 if wl.mla_dtype == "f32" else 2
+    key_b = wl.D_I * elt_i + (4 if wl.idx_dtype == "fp8" else 0)
+    per_row_idx = wl.H_I * wl.D_I * elt_i + (wl.H_I * 4 if wl.idx_dtype == "fp8" else 0) + wl.H_I * 4
+    idx_b = sum(per_row_idx + key_b * n for n in lens)
+    mla_b = sum(min(n, wl.topk) * wl.D_qk * elt_m + wl.H * (wl.D_qk + wl.D_v) * elt_m for n in lens)
+    return idx_b, mla_b
+
+
+def algorithmic_flops(wl, lens):
+    idx_f = sum(2 * wl.H_I * wl.D_I * n for n in lens)
+    mla_f = sum(2 * wl.H * (wl.D_qk + wl.D_v) * min(n, wl.topk) for n in lens)
+    return idx_f, mla_f
+
+
+def pmc_traffic(kernel: str, units: float):
+    """HBM bytes per launch from a committed counter summary, or None when it is missing or
+    was taken on a different version of the kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("source_sha") != source_hash(kernel):
+            return None
+        return float(d["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl_host, n_rows: int):
+    """The fp64 oracle (as it stands) on the first n_rows rows of the same batch."""
+    import numpy as np
+
+    import oracle
+    from workloads import raw_numpy as raw
+    oracle.build()
+    h = wl_host.host_rows()
+    rows = oracle.Rows(h["row_seq"], h["row_len"], seq_start=h["seq_start"],
+                       page_table=h["page_table"], page_size=h["page_size"])
+    which = list(range(n_rows))
+    threads = max(1, min(n_rows, os.cpu_count() or 1, 16))
+    q_i, k_i, w = raw(wl_host.q_idx), raw(wl_host.k_idx), raw(wl_host.w)
+    q_s, k_s = raw(wl_host.q_scale), raw(wl_host.k_scale)
+    q, kv = raw(wl_host.q), raw(wl_host.kv)
+    t0 = time.perf_counter()
+    scores = oracle.indexer(wl_host.idx_dtype, q_i, w, k_i, rows, q_scale=q_s, k_scale=k_s,
+                            which=which, n_threads=threads)
+    lens = h["row_len"][which]
+    sel = oracle.topk(np.nan_to_num(scores, nan=0.0), lens, wl_host.topk, n_threads=threads)
+    full_idx = np.full((wl_host.num_rows, wl_host.topk), -1, dtype=np.int32)
+    full_idx[which] = sel
+    oracle.sparse_mla(wl_host.mla_dtype, q, kv, full_idx, rows, wl_host.scale, wl_host.D_v,
+                      which=which, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} of {wl_host.num_rows} decode rows of the same workload "
+                      f"(full context each), indexer + top-k + sparse MLA in fp64, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is a single-GPU "
+              f"build and measures no multi-GPU configuration.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_attention_08_amd as dsa
+    import workloads
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    wl = workloads.config(args.config, device=dev)
+    rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, seq_start=wl.seq_start,
+                    page_table=wl.page_table)
+    R, lens = wl.num_rows, wl.row_len.cpu().tolist()
+    logits = torch.empty((R, wl.max_row_len), dtype=torch.float32, device=dev)
+    idx = torch.empty((R, wl.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((R, wl.H, wl.D_v), dtype=wl.q.dtype, device=dev)
+    lse = torch.empty((R, wl.H), dtype=torch.float32, device=dev)
+    tk_ws_n = dsa.topk_workspace_size(R, wl.max_row_len, wl.topk)
+    tk_ws = torch.zeros(max(tk_ws_n, 1), dtype=torch.uint8, device=dev)   # zeroed once
+    prefill = wl.mode == "prefill"
+    ml_ws_n = 0 if prefill else dsa.sparse_mla_workspace_size(R, wl.H, wl.D_v, wl.topk)
+    ml_ws = torch.empty(max(ml_ws_n, 1), dtype=torch.uint8, device=dev)
+    idx_fn = dsa.indexer_logits_paged if wl.paged else dsa.indexer_logits
+
+    def stage_indexer():
+        idx_fn(rows, wl.q_idx, wl.w, wl.k_idx, logits, q_scale=wl.q_scale, k_scale=wl.k_scale)
+
+    def stage_topk():
+        dsa.topk(logits, wl.row_len, wl.topk, wl.max_row_len, idx=idx, ws=tk_ws)
+
+    def stage_mla():
+        if prefill:
+            dsa.sparse_mla_prefill(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=lse)
+        elif wl.paged:
+            dsa.sparse_mla_decode_paged(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=lse,
+                                        ws=ml_ws)
+        else:
+            dsa.sparse_mla_decode(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=lse, ws=ml_ws)
+
+    # 1 GiB that every timed step first reads (a read leaves no dirty lines behind to be
+    # written back during the timed kernels), evicting L2 and the Infinity Cache
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        stage_indexer(); stage_topk(); stage_mla()
+    torch.cuda.synchronize()
+
+    def step():
+        stage_indexer(); stage_topk(); stage_mla()
+
+    # eager launches, with per-stage attribution
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush is not None:
+            flush_sink = flush.sum()
+        e = ev[i]
+        e[0].record(); stage_indexer()
+        e[1].record(); stage_topk()
+        e[2].record(); stage_mla()
+        e[3].record()
+    torch.cuda.synchronize()
+    eager_ms = [e[0].elapsed_time(e[3]) for e in ev]
+    idx_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    topk_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    mla_ms = [e[2].elapsed_time(e[3]) for e in ev]
+
+    # the same step captured once in a HIP graph and replayed (the serving launch mode)
+    run = step
+    mode = "eager"
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+        mode = "hip_graph"
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush_sink = flush.sum()
+        gev[i][0].record(); run(); gev[i][1].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    step_ms = [e[0].elapsed_time(e[1]) for e in gev]
+    mean = statistics.fmean(step_ms)
+
+    # back-to-back steps with warm caches, for reference
+    torch.cuda.synchronize()
+    w0 = torch.cuda.Event(enable_timing=True); w1 = torch.cuda.Event(enable_timing=True)
+    w0.record()
+    for _ in range(args.steps):
+        run()
+    w1.record()
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    idx_b, mla_b = algorithmic_bytes(wl, lens)
+    idx_f, mla_f = algorithmic_flops(wl, lens)
+    idx_mean = statistics.fmean(idx_ms)
+    if prefill:
+        flops = idx_f + mla_f
+        roof = {"bound": "mfma", "achieved": flops / (mean * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        roof["kernel"] = "whole path (indexer + top-k + sparse MLA), algorithmic flops"
+    else:
+        achieved = idx_b / (idx_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic("indexer_mfma_kernel", R),
+                "kernel": "indexer_mfma_kernel",
+                "algorithmic_bytes_per_launch": idx_b}
+    res = {
+        "metric": METRIC,
+        "value": R / (mean * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8": "fp8_e4m3+bf16", "bf16": "bf16", "f32": "f32"}[wl.idx_dtype],
+        "data": "synthetic (seeded N(0,1) activations, U(0,1)/8 head weights; no trained weights)",
+        "config": {"workload": wl.name, "batch": R, "context": max(lens), "index_topk": wl.topk,
+                   "indexer_heads": wl.H_I, "indexer_dim": wl.D_I, "mla_heads": wl.H,
+                   "d_qk": wl.D_qk, "d_v": wl.D_v, "parallelism": "single GPU",
+                   "cache_flushed_between_steps": flush is not None},
+        "roofline": roof,
+        "path": {"algorithmic_bytes_per_step": idx_b + mla_b,
+                 "hbm_frac_of_step": (idx_b + mla_b) / (mean * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "algorithmic_flops_per_step": idx_f + mla_f,
+                 "launch_mode": mode,
+                 "eager_ms_per_step": statistics.fmean(eager_ms),
+                 "stage_ms": {"indexer": idx_mean, "topk": statistics.fmean(topk_ms),
+                              "sparse_mla": statistics.fmean(mla_ms)},
+                 "step_ms_median": statistics.median(step_ms), "step_ms_min": min(step_ms),
+                 "warm_back_to_back_ms_per_step": warm_ms,
+                 "wall_s_timed_loop_incl_flushes": t_wall},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        del logits, out, lse, flush, run
+        if not args.no_graph:
+            del graph
+        torch.cuda.empty_cache()
+        n_cpu = args.cpu_rows or min(R, 8)
+        res["cpu_baseline"] = cpu_baseline(wl, n_cpu)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

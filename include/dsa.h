@@ -121,7 +121,8 @@ int dsa_indexer_logits_paged(const dsa_rows *rows, int dtype, int n_heads, int h
  * idx [R, k] int32 output: the selected positions in ascending order, then -1 padding.
  * Scores must be finite (NaN and infinities are not supported).  1 <= k <= 2048.
  * ws / ws_bytes: device scratch of at least dsa_topk_workspace_size(R, max_row_len, k)
- * bytes (may be NULL when that is 0); its contents need no initialisation. */
+ * bytes (may be NULL when that is 0); its contents need no initialisation.  Calls that
+ * share one workspace must not run concurrently. */
 size_t dsa_topk_workspace_size(int num_rows, int max_row_len, int k);
 int dsa_topk(const float *logits, int64_t ld_logits, const int32_t *row_len, int num_rows,
              int max_row_len, int k, int32_t *idx, void *ws, size_t ws_bytes, void *stream);

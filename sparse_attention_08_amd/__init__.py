@@ -198,7 +198,7 @@ def topk(logits, row_len, k: int, max_row_len: int, idx=None, ws=None):
     _dev(idx, "idx", (torch.int32,))
     need = topk_workspace_size(R, max_row_len, k)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=logits.device)   # zero before first use
     s = lib.dsa_topk(_ptr(logits), int(logits.shape[-1]), _ptr(row_len), R, int(max_row_len), int(k),
                      _ptr(idx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check(s, "dsa_topk")

@@ -66,6 +66,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Butterfly partners across lane rows with gfx950's VALU lane swaps (no LDS round trip):
+// the value of lane l ^ 16, and of lane l ^ 32.  Called with both operands equal, the
+// swap leaves lane l's own value in one half of the result and the partner's in the
+// other, always in (lower lane, upper lane) order.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
   return lane ? (~0ull >> (64 - lane)) : 0ull;

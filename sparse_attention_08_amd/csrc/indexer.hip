@@ -78,51 +78,185 @@ hipError_t launch_indexer_f32(const RowsHost &rh, bool paged, int H, int D, cons
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
 
+
+
+// A group is 8 KB of keys: 64 fp8 keys or 32 bf16 keys (U = 4 or 2 MFMA tiles of 16).
+// Each wave streams its span of keys through a private ring of kDepth LDS slots, filled
+// by direct global->LDS loads (global_load_lds_dwordx4: lane l of an instruction lands
+// at slot + 1024*j + 16*l), so keys never pass through VGPRs and kDepth-1 groups are in
+// flight while one is multiplied.  Each load instruction covers 1 KB of whole cache
+// lines.  Inside a slot, key k's 16-byte chunk x is stored at chunk x ^ (k & 7): the
+// MFMA operand reads (8 keys at the same logical chunk per LDS cycle) hit 8 distinct
+// bank groups.  The swizzle is applied on the global side, by choosing which chunk
+// each lane fetches.
+#ifndef DSA_IDX_DEPTH
+#define DSA_IDX_DEPTH 4
+#endif
+#ifndef DSA_IDX_WAVES
+#define DSA_IDX_WAVES 4
+#endif
+#ifndef DSA_IDX_BLOCKS
+#define DSA_IDX_BLOCKS 512
+#endif
+constexpr int kGroupBytes = 8192;
+constexpr int kDepth = DSA_IDX_DEPTH;       // LDS slots per wave (kDepth-1 groups in flight)
+constexpr int kIdxWaves = DSA_IDX_WAVES;
+
 template <bool FP8>
-struct KeyFrag {
-  static constexpr int kChunks = FP8 ? 2 : 4;   // 16-byte chunks a lane loads per key
-  i32x4 c[kChunks];
+struct IdxCfg {
+  static constexpr int kRowBytes = kIdxDim * (FP8 ? 1 : 2);   // 128 / 256
+  static constexpr int kKeys = kGroupBytes / kRowBytes;        // 64 / 32 keys per group
+  static constexpr int kTiles = kKeys / 16;                    // 4 / 2 MFMA tiles
+  static constexpr int kChunks = kRowBytes / 64;               // 16-byte chunks per lane per key
+  static constexpr int kSlotBytes = kGroupBytes + (FP8 ? 256 : 0);   // keys (+ 64 scales)
 };
 
-template <bool FP8, bool PAGED>
-__device__ __forceinline__ void load_key(KeyFrag<FP8> &f, float &ks, const uint8_t *__restrict__ k,
-                                         const float *__restrict__ k_scale, const RowsDev &rows,
-                                         int b, int64_t s, int g) {
-  constexpr int kRowBytes = kIdxDim * (FP8 ? 1 : 2);
-  const int64_t crow = cache_row<PAGED>(rows, b, s);
-  const i32x4 *p = reinterpret_cast<const i32x4 *>(k + crow * kRowBytes + g * (kRowBytes / 4));
-#pragma unroll
-  for (int i = 0; i < KeyFrag<FP8>::kChunks; ++i) f.c[i] = __builtin_nontemporal_load(p + i);
-  if constexpr (FP8) ks = k_scale[crow];
+typedef void __attribute__((address_space(3))) *lds_void_ptr;
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory operations and
+// leaves the export and LDS/scalar counters unconstrained (gfx9 field layout).
+constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 4, 0, 0);
 }
 
-template <bool FP8, bool PAGED, int U>
-__global__ __launch_bounds__(256) void indexer_mfma_kernel(
+// Issues the loads of the group starting at key s0 into `slot` (clamped into the span,
+// so a look-ahead past its end re-reads keys that are already in cache).  base_row:
+// contiguous layout, cache row of position 0; paged layout: lane i of page_lane holds
+// the page of position 64*(p0 + i).  A group never crosses a 64-token page.
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__restrict__ k,
+                                            const float *__restrict__ k_scale, int64_t base_row,
+                                            int page_lane, int64_t p0, int64_t s0, int64_t s_last,
+                                            int lane) {
+  using C = IdxCfg<FP8>;
+  s0 = min<int64_t>(s0, s_last & ~(int64_t)(C::kKeys - 1));
+  int64_t row0;
+  if constexpr (PAGED) {
+    const int page = __builtin_amdgcn_readlane(page_lane, (int)((s0 >> 6) - p0));
+    row0 = (int64_t)page * kPage + (s0 & 63);
+  } else {
+    row0 = base_row + s0;
+  }
+  const int last = (int)(s_last - s0);   // last valid key offset inside the group
+#pragma unroll
+  for (int j = 0; j < kGroupBytes / 1024; ++j) {
+    const int pos = 1024 * j + 16 * lane;             // byte position inside the slot
+    const int key = pos / C::kRowBytes;
+    const int chunk = (pos % C::kRowBytes) >> 4;      // physical chunk
+    const int src_chunk = chunk ^ (key & 7);          // logical chunk stored there
+    const int kk = min(key, last);
+    dma16(k + (row0 + kk) * C::kRowBytes + 16 * src_chunk, slot + 1024 * j);
+  }
+  if constexpr (FP8) dma4(k_scale + row0 + min(lane, last), slot + kGroupBytes);
+}
+
+// MFMA + fused epilogue for the group in `slot`; returns in lane (g, c) the score of key
+// 16g + c of the group (for bf16 only lanes with g < 2 carry one).
+template <bool FP8>
+__device__ __forceinline__ float consume_group(const uint8_t *slot,
+                                               const i32x4 (&qf)[4][IdxCfg<FP8>::kChunks],
+                                               const float (&wt)[4][4], int lane) {
+  using C = IdxCfg<FP8>;
+  const int c = lane & 15, g = lane >> 4;
+  float mine = 0.f;
+#pragma unroll
+  for (int u = 0; u < C::kTiles; ++u) {
+    const int key = 16 * u + c;
+    i32x4 kf[C::kChunks];
+#pragma unroll
+    for (int i = 0; i < C::kChunks; ++i) {
+      const int chunk = (g * C::kChunks + i) ^ (key & 7);
+      kf[i] = *reinterpret_cast<const i32x4 *>(slot + key * C::kRowBytes + 16 * chunk);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (FP8) {
+        const i32x8 a = __builtin_shufflevector(qf[hb][0], qf[hb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const i32x8 bb = __builtin_shufflevector(kf[0], kf[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, acc[hb], 0, 0, 0, 127, 0, 127);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[hb][t]),
+                                                            __builtin_bit_cast(bf16x8, kf[t]),
+                                                            acc[hb], 0, 0, 0);
+      }
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], fmaxf(acc[hb][i], 0.f), v);
+    v = sum_xor32(sum_xor16(v));   // sum over the 4 lane rows: all 64 heads
+    if (g == u) mine = v;
+  }
+  if constexpr (FP8) mine *= reinterpret_cast<const float *>(slot + kGroupBytes)[lane];
+  return mine;
+}
+
+template <bool FP8, bool PAGED>
+__global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
     RowsDev rows, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, const float *__restrict__ w,
     float *__restrict__ logits, int64_t ld, int keys_per_wave) {
-  constexpr int kElt = FP8 ? 1 : 2;
-  constexpr int kRowBytes = kIdxDim * kElt;
+  using C = IdxCfg<FP8>;
+  constexpr int kQChunks = kIdxHeads * C::kRowBytes / 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t idx_smem[];
+  uint8_t *smem = idx_smem;
+  i32x4 *q_lds = reinterpret_cast<i32x4 *>(smem);
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r];
-  const int64_t s_begin = ((int64_t)blockIdx.x * 4 + wave) * keys_per_wave;
-  if (s_begin >= len) return;
+  const int64_t blk_begin = (int64_t)blockIdx.x * kIdxWaves * keys_per_wave;
+  if (blk_begin >= len) return;
+  const int64_t s_begin = blk_begin + (int64_t)wave * keys_per_wave;
+  const bool active = s_begin < len;
   const int64_t s_end = min<int64_t>(s_begin + keys_per_wave, len);
+  const int64_t s_last = s_end - 1;
   const int b = rows.row_seq[r];
-
-  // Query operand: head 16*hb + c, dims [32g, 32g+32).
-  i32x4 qf[4][KeyFrag<FP8>::kChunks];
+  uint8_t *ring = smem + kQChunks * 16 + wave * kDepth * C::kSlotBytes;
+  int64_t base_row = 0;
+  int page_lane = 0;
+  const int64_t p0 = s_begin >> 6;
+  // loads per group: kGroupBytes/1024 key instructions (+1 scale instruction for fp8)
+  constexpr int kLoads = kGroupBytes / 1024 + (FP8 ? 1 : 0);
+  if (active) {
+    if constexpr (PAGED) {
+      const int64_t np = ((s_last >> 6) - p0) + 1;   // pages this span touches (<= 64)
+      if (lane < np) page_lane = rows.page_table[(int64_t)b * rows.max_pages + p0 + lane];
+    } else {
+      base_row = rows.seq_start[b];
+    }
+    // the first kDepth-1 key groups start streaming before the query block is loaded
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const i32x4 *p = reinterpret_cast<const i32x4 *>(
-        q + ((int64_t)r * kIdxHeads + hb * 16 + c) * kRowBytes + g * (kRowBytes / 4));
-#pragma unroll
-    for (int i = 0; i < KeyFrag<FP8>::kChunks; ++i) qf[hb][i] = p[i];
+    for (int d = 0; d < kDepth - 1; ++d)
+      issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, page_lane, p0,
+                              s_begin + (int64_t)d * C::kKeys, s_last, lane);
   }
-  // Head weights for the result rows this lane holds: heads 16*hb + 4g + i.
+  {
+    const i32x4 *qg = reinterpret_cast<const i32x4 *>(q + (int64_t)r * kIdxHeads * C::kRowBytes);
+    for (int i = threadIdx.x; i < kQChunks; i += kIdxWaves * kWave) q_lds[i] = qg[i];
+  }
+  __syncthreads();
+  if (!active) return;
+
+  // q operand of head 16*hb + c, dims [32g, 32g+32) (fp8) / [64g, 64g+64) (bf16)
+  i32x4 qf[4][C::kChunks];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int i = 0; i < C::kChunks; ++i)
+      qf[hb][i] = q_lds[(hb * 16 + c) * (C::kRowBytes / 16) + g * C::kChunks + i];
+  // head weights of the result rows this lane holds: heads 16*hb + 4g + i
   float wt[4][4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb)
@@ -131,96 +265,66 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
       const int64_t hj = (int64_t)r * kIdxHeads + hb * 16 + 4 * g + i;
       wt[hb][i] = FP8 ? w[hj] * q_scale[hj] : w[hj];
     }
-
-  KeyFrag<FP8> cur[U], nxt[U];
-  float cur_s[U], nxt_s[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t s = min<int64_t>(s_begin + 16 * u + c, s_end - 1);
-    load_key<FP8, PAGED>(cur[u], cur_s[u], k, k_scale, rows, b, s, g);
-  }
   float *out = logits + (int64_t)r * ld;
-  for (int64_t s0 = s_begin; s0 < s_end; s0 += 16 * U) {
-    const bool more = s0 + 16 * U < s_end;
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t s = min<int64_t>(s0 + 16 * U + 16 * u + c, s_end - 1);
-        load_key<FP8, PAGED>(nxt[u], nxt_s[u], k, k_scale, rows, b, s, g);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f32x4 acc[4];
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-          const i32x8 a = __builtin_shufflevector(qf[hb][0], qf[hb][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const i32x8 bb =
-              __builtin_shufflevector(cur[u].c[0], cur[u].c[1], 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, acc[hb], 0, 0, 0, 127,
-                                                                     0, 127);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, qf[hb][t]), __builtin_bit_cast(bf16x8, cur[u].c[t]),
-                acc[hb], 0, 0, 0);
-        }
-      }
-      float v = 0.f;
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], fmaxf(acc[hb][i], 0.f), v);
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      if constexpr (FP8) v *= cur_s[u];
-      const int64_t s = s0 + 16 * u + c;
-      if (g == 0 && s < s_end) out[s] = v;
-    }
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        cur[u] = nxt[u];
-        cur_s[u] = nxt_s[u];
-      }
-    }
+  const int n_groups = (int)((s_end - s_begin + C::kKeys - 1) / C::kKeys);
+  for (int i = 0; i < n_groups; ++i) {
+    issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
+                            base_row, page_lane, p0, s_begin + (int64_t)(i + kDepth - 1) * C::kKeys,
+                            s_last, lane);
+    // group i is older than the kDepth-1 groups issued after it: loads complete in order
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
+    const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);
+    const int64_t s = s_begin + (int64_t)i * C::kKeys + lane;
+    if (lane < C::kKeys && s < s_end) out[s] = v;
   }
+  // the look-ahead loads past the span must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+}
+
+size_t indexer_lds_bytes(bool fp8) {
+  return fp8 ? (size_t)kIdxHeads * IdxCfg<true>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<true>::kSlotBytes
+             : (size_t)kIdxHeads * IdxCfg<false>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<false>::kSlotBytes;
+}
+
+template <bool FP8, bool PAGED>
+static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const RowsDev &rows,
+                             const uint8_t *q8, const float *q_scale, const uint8_t *k8,
+                             const float *k_scale, const float *w, float *logits, int64_t ld,
+                             int kpw) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&indexer_mfma_kernel<FP8, PAGED>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  indexer_mfma_kernel<FP8, PAGED><<<grid, kIdxWaves * kWave, shm, stream>>>(
+      rows, q8, q_scale, k8, k_scale, w, logits, ld, kpw);
+  return hipGetLastError();
 }
 
 hipError_t launch_indexer_mfma(const RowsHost &rh, bool paged, bool fp8, const void *q,
                                const float *q_scale, const void *k, const float *k_scale,
                                const float *w, float *logits, int64_t ld, hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
-  // Aim for ~4096+ waves (16 per CU on 256 CUs); spans are whole 16-key tiles.
+  // One workgroup per CU at a time (the LDS rings fill most of the CU's 160 KB); size the
+  // spans for about two rounds of 256 workgroups; spans are whole 64-key multiples.
   const int64_t total = (int64_t)rh.num_rows * rh.max_row_len;
-  int64_t kpw = (total + 8191) / 8192;
+  constexpr int64_t kBlocksTarget = DSA_IDX_BLOCKS;
+  int64_t kpw = (total + kIdxWaves * kBlocksTarget - 1) / (kIdxWaves * kBlocksTarget);
   kpw = ((kpw + 63) / 64) * 64;
   if (kpw < 64) kpw = 64;
-  if (kpw > 2048) kpw = 2048;
-  const int64_t per_block = 4 * kpw;
+  if (kpw > 4096) kpw = 4096;   // a span touches at most 64 pages (one per lane)
+  const int64_t per_block = kIdxWaves * kpw;
   dim3 grid((unsigned)((rh.max_row_len + per_block - 1) / per_block), rh.num_rows);
+  const size_t shm = indexer_lds_bytes(fp8);
   const uint8_t *q8 = static_cast<const uint8_t *>(q);
   const uint8_t *k8 = static_cast<const uint8_t *>(k);
-  if (fp8) {
-    if (paged)
-      indexer_mfma_kernel<true, true, 4><<<grid, 256, 0, stream>>>(rows, q8, q_scale, k8, k_scale,
-                                                                   w, logits, ld, (int)kpw);
-    else
-      indexer_mfma_kernel<true, false, 4><<<grid, 256, 0, stream>>>(rows, q8, q_scale, k8, k_scale,
-                                                                    w, logits, ld, (int)kpw);
-  } else {
-    if (paged)
-      indexer_mfma_kernel<false, true, 2><<<grid, 256, 0, stream>>>(rows, q8, q_scale, k8, k_scale,
-                                                                    w, logits, ld, (int)kpw);
-    else
-      indexer_mfma_kernel<false, false, 2><<<grid, 256, 0, stream>>>(rows, q8, q_scale, k8,
-                                                                     k_scale, w, logits, ld,
-                                                                     (int)kpw);
-  }
-  return hipGetLastError();
+  if (fp8)
+    return paged ? launch_one<true, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw)
+                 : launch_one<true, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw);
+  return paged ? launch_one<false, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw)
+               : launch_one<false, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw);
 }
 
 }  // namespace dsa

@@ -2,179 +2,509 @@
 // DSA ② Fine-grained Token Selection; "DeepSeek-V3.2 -- Model techniques map",
 // "Indexer-selected sparse attention": k = min(index_topk, row length), int32 indices).
 //
-// Exact selection by radix select on order-preserving 32-bit keys: four 8-bit digit
-// passes from the most significant end find the key T of the k-th largest score and
-// how many of the scores equal to T are still needed; a final ordered pass writes
-// every position with key > T plus the lowest-positioned keys == T, in ascending
-// position order.  No floating-point arithmetic is involved, so the result is the
-// unique set defined by (score desc, position asc) and is bit-exact.
+// Exact selection on order-preserving 32-bit keys (-0 folded onto +0): a radix select
+// with digits of 12, 10 and 10 bits finds the key T of the k-th largest score and how
+// many keys equal to T are still needed; an ordered pass then writes every position
+// with key > T plus the lowest-positioned keys == T, in ascending position order.  No
+// floating-point arithmetic is involved, so the result is the unique set defined by
+// (score desc, position asc) and is bit-exact.  The first digit is 12 bits wide (sign,
+// exponent and 3 mantissa bits) so that LDS histogram atomics spread over many bins.
 //
-// One workgroup per row; when the row fits, it is staged once in LDS and every pass
-// reads LDS, otherwise the passes stream the row from L2.
+// Two schedules:
+//  * many rows (prefill): one workgroup per row, the row staged once in LDS;
+//  * few long rows (decode): each row is cut into 4096-score chunks handled by separate
+//    workgroups, in three launches and without device-wide atomics or fences:
+//    (1) per chunk, a histogram of the 12-bit digit, stored compressed (nonzero bins);
+//    (2) per chunk, every workgroup merges the row's compressed histograms in LDS, finds
+//        the digit b* that holds the k-th largest score, and keeps, in position order,
+//        the chunk's scores whose digit is >= b* (the k largest are among them);
+//    (3) per row, one workgroup gathers those few thousand survivors into LDS and runs
+//        the remaining two digits of the exact select on them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
 namespace dsa {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kTopkLdsElems = 32768;   // 128 KB of staged keys
+constexpr int kD0Bits = 12, kD1Bits = 10, kD2Bits = 10;
+constexpr int kBins = 1 << kD0Bits;        // 4096
+constexpr int kChunk = 4096;               // scores per workgroup in the few-row schedule
+constexpr int kSmallThreads = 1024;
+constexpr int kMbThreads = 256;
+constexpr int kStageElems = 28672;         // single-row schedule: up to 112 KB of staged keys
+constexpr int kSurvivorCap = 10240;        // survivors selected in LDS (80 KB)
+constexpr int kMaxChunks = 256;            // chunked schedule handles rows up to 1M scores
 
-struct TopkShared {
-  uint32_t hist[kTopkWaves][256];   // per-wave digit histograms
-  uint32_t wave_cnt[2][kTopkWaves];
+// ------------------------------------------------------------------------------------
+// block-wide helpers
+// ------------------------------------------------------------------------------------
+template <int NT>
+struct BlockScratch {
+  uint32_t hist[kBins];
+  uint32_t wsum[NT / kWave];
+  uint32_t wcnt[2][NT / kWave];
   uint32_t prefix, mask;
   int32_t need;
+  uint32_t flag;
 };
 
-// Histogram of the digit at `shift` over keys matching (key & mask) == prefix, then the
-// digit holding the need-th largest key; updates prefix/mask/need in shared memory.
-template <bool STAGED>
-__device__ void radix_pass(TopkShared &sh, const uint32_t *keys, const float *row, int n,
-                           int shift) {
+// Exclusive prefix sum over the block's threads of v; returns it and the block total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
+                                                    BlockScratch<NT> &sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kTopkWaves * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) sh.wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    const uint32_t s = sh.wsum[w];
+    before += (w < wave) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + inc - v;
+}
+
+// One radix digit: histogram of digit (key >> shift) & (2^BITS - 1) over the keys that
+// match (key & mask) == prefix, then the digit holding the need-th largest key.
+template <int NT, int BITS, class Acc>
+__device__ void radix_digit(const Acc &acc, int n, int shift, BlockScratch<NT> &sh) {
+  constexpr int NB = 1 << BITS;
+  constexpr int PER = NB / NT;             // consecutive bins owned per thread
+  static_assert(NB % NT == 0, "bins must split evenly");
+  for (int i = threadIdx.x; i < NB; i += NT) sh.hist[i] = 0;
   __syncthreads();
   const uint32_t prefix = sh.prefix, mask = sh.mask;
-  for (int i = threadIdx.x; i < n; i += kTopkThreads) {
-    const uint32_t u = STAGED ? keys[i] : order_key(row[i]);
-    if ((u & mask) == prefix) atomicAdd(&sh.hist[wave][(u >> shift) & 255u], 1u);
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t u = acc.key(i);
+    if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & (NB - 1)], 1u);
   }
   __syncthreads();
-  // fold the per-wave histograms into wave 0's row
-  for (int d = threadIdx.x; d < 256; d += kTopkThreads) {
-    uint32_t s = 0;
-    for (int w = 0; w < kTopkWaves; ++w) s += sh.hist[w][d];
-    sh.hist[0][d] = s;
+  // thread t owns bins NB-1-PER*t-j (j < PER): descending digit order across threads
+  uint32_t c[PER], tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = sh.hist[NB - 1 - PER * threadIdx.x - j];
+    tot += c[j];
   }
+  uint32_t all;
+  const uint32_t before = block_excl_scan<NT>(tot, all, sh);
+  const int32_t need = sh.need;
   __syncthreads();
-  if (wave == 0) {
-    // digits 255..0 in descending order, 4 per lane: lane L owns 255-4L .. 252-4L
-    uint32_t c[4], tot = 0;
+  if (before < (uint32_t)need && before + tot >= (uint32_t)need) {
+    uint32_t run = before;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = sh.hist[0][255 - 4 * lane - j];
-      tot += c[j];
-    }
-    // inclusive scan of lane totals (descending digit order)
-    uint32_t inc = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += v;
-    }
-    const uint32_t before = inc - tot;   // count of keys in higher digits
-    const int32_t need = sh.need;
-    // the lane whose range crosses `need`
-    if (before < (uint32_t)need && inc >= (uint32_t)need) {
-      uint32_t run = before;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (run + c[j] >= (uint32_t)need) {
-          const uint32_t digit = 255u - 4u * lane - j;
-          sh.prefix = prefix | (digit << shift);
-          sh.mask = mask | (255u << shift);
-          sh.need = need - (int32_t)run;
-          break;
-        }
-        run += c[j];
+    for (int j = 0; j < PER; ++j) {
+      if (run + c[j] >= (uint32_t)need) {
+        const uint32_t digit = NB - 1 - PER * threadIdx.x - j;
+        sh.prefix = prefix | (digit << shift);
+        sh.mask = mask | ((uint32_t)(NB - 1) << shift);
+        sh.need = need - (int32_t)run;
+        break;
       }
+      run += c[j];
     }
   }
   __syncthreads();
 }
 
-template <bool STAGED>
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float *__restrict__ logits,
-                                                                 int64_t ld,
-                                                                 const int32_t *__restrict__ row_len,
-                                                                 int k, int32_t *__restrict__ idx) {
-  extern __shared__ uint32_t staged[];
-  __shared__ TopkShared sh;
-  const int r = blockIdx.x;
-  const int n = row_len[r];
-  const float *row = logits + (int64_t)r * ld;
-  int32_t *out = idx + (int64_t)r * k;
+// Exact top-k of n keys given by acc (key(i), pos(i); items in ascending position
+// order), written to out[0..k) in ascending position order.  Requires n > k.
+// When first_digit >= 0 the caller already knows the 12-bit digit of T and that
+// `need_in_digit` keys with that digit belong to the result.
+template <int NT, class Acc>
+__device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__ out,
+                             BlockScratch<NT> &sh, int first_digit = -1, int need_in_digit = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (n <= k) {   // every position is selected
-    for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-  if (STAGED) {
-    for (int i = threadIdx.x; i < n; i += kTopkThreads) staged[i] = order_key(row[i]);
-  }
   if (threadIdx.x == 0) {
-    sh.prefix = 0;
-    sh.mask = 0;
-    sh.need = k;
+    if (first_digit >= 0) {
+      sh.prefix = (uint32_t)first_digit << (kD1Bits + kD2Bits);
+      sh.mask = (uint32_t)(kBins - 1) << (kD1Bits + kD2Bits);
+      sh.need = need_in_digit;
+    } else {
+      sh.prefix = 0;
+      sh.mask = 0;
+      sh.need = k;
+    }
   }
   __syncthreads();
-  for (int shift = 24; shift >= 0; shift -= 8) radix_pass<STAGED>(sh, staged, row, n, shift);
-  const uint32_t T = sh.prefix;      // key of the k-th largest score
-  const int32_t need_eq = sh.need;   // how many keys == T to take, lowest positions first
-
-  // Ordered write.  Wave w owns the contiguous span [w*span, (w+1)*span); pass A counts
-  // its keys > T and == T, a scan over waves gives each wave its starting ranks, pass B
-  // writes in position order with ballot prefix counts.
-  const int span = (((n + kTopkWaves - 1) / kTopkWaves) + 63) & ~63;
-  const int lo = wave * span;
-  const int hi = min(n, lo + span);
+  if (first_digit < 0) radix_digit<NT, kD0Bits>(acc, n, kD1Bits + kD2Bits, sh);
+  radix_digit<NT, kD1Bits>(acc, n, kD2Bits, sh);
+  radix_digit<NT, kD2Bits>(acc, n, 0, sh);
+  const uint32_t T = sh.prefix;
+  const int32_t need_eq = sh.need;
+  // ordered write: wave w owns a contiguous span; counts, wave offsets, then ballots
+  constexpr int NW = NT / kWave;
+  const int span = (((n + NW - 1) / NW) + 63) & ~63;
+  const int lo = wave * span, hi = min(n, lo + span);
   uint32_t gt_cnt = 0, eq_cnt = 0;
   for (int base = lo; base < hi; base += 64) {
     const int i = base + lane;
-    uint32_t u = 0;
-    if (i < hi) u = STAGED ? staged[i] : order_key(row[i]);
+    const uint32_t u = i < hi ? acc.key(i) : 0u;
     gt_cnt += __popcll(__ballot(i < hi && u > T));
     eq_cnt += __popcll(__ballot(i < hi && u == T));
   }
   if (lane == 0) {
-    sh.wave_cnt[0][wave] = gt_cnt;
-    sh.wave_cnt[1][wave] = eq_cnt;
+    sh.wcnt[0][wave] = gt_cnt;
+    sh.wcnt[1][wave] = eq_cnt;
   }
   __syncthreads();
   uint32_t eq_before = 0, sel_before = 0;
-  for (int w = 0; w < wave; ++w) eq_before += sh.wave_cnt[1][w];
   for (int w = 0; w < wave; ++w) {
-    uint32_t eb = 0;
-    for (int v = 0; v < w; ++v) eb += sh.wave_cnt[1][v];
-    const int32_t take = max(0, min((int32_t)sh.wave_cnt[1][w], need_eq - (int32_t)eb));
-    sel_before += sh.wave_cnt[0][w] + (uint32_t)take;
+    const int32_t take = max(0, min((int32_t)sh.wcnt[1][w], need_eq - (int32_t)eq_before));
+    sel_before += sh.wcnt[0][w] + (uint32_t)take;
+    eq_before += sh.wcnt[1][w];
   }
   const uint64_t lt = lanemask_lt();
   for (int base = lo; base < hi; base += 64) {
     const int i = base + lane;
-    uint32_t u = 0;
-    if (i < hi) u = STAGED ? staged[i] : order_key(row[i]);
+    const uint32_t u = i < hi ? acc.key(i) : 0u;
     const bool gt = i < hi && u > T;
     const bool eq = i < hi && u == T;
     const uint64_t eq_mask = __ballot(eq);
     const uint32_t eq_rank = eq_before + __popcll(eq_mask & lt);
     const bool sel = gt || (eq && eq_rank < (uint32_t)need_eq);
     const uint64_t sel_mask = __ballot(sel);
-    if (sel) out[sel_before + __popcll(sel_mask & lt)] = i;
+    if (sel) out[sel_before + __popcll(sel_mask & lt)] = acc.pos(i);
     eq_before += __popcll(eq_mask);
     sel_before += __popcll(sel_mask);
   }
 }
 
-size_t topk_workspace_bytes(int, int, int) { return 0; }
+struct RowAcc {            // keys computed on the fly from a score row in global memory
+  const float *row;
+  __device__ uint32_t key(int i) const { return order_key(row[i]); }
+  __device__ int32_t pos(int i) const { return i; }
+};
+struct StagedAcc {         // keys staged in LDS
+  const uint32_t *keys;
+  __device__ uint32_t key(int i) const { return keys[i]; }
+  __device__ int32_t pos(int i) const { return i; }
+};
+struct SurvivorAcc {       // (key, position) survivors staged in LDS
+  const uint32_t *keys;
+  const int32_t *posn;
+  __device__ uint32_t key(int i) const { return keys[i]; }
+  __device__ int32_t pos(int i) const { return posn[i]; }
+};
+
+__device__ __forceinline__ void write_all(int32_t *out, int n, int k) {
+  for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < n ? i : -1;
+}
+
+// ------------------------------------------------------------------------------------
+// many-row schedule: one workgroup per row
+// ------------------------------------------------------------------------------------
+template <bool STAGED>
+__global__ __launch_bounds__(kSmallThreads) void topk_row_kernel(const float *__restrict__ logits,
+                                                                 int64_t ld,
+                                                                 const int32_t *__restrict__ row_len,
+                                                                 int k, int32_t *__restrict__ idx) {
+  extern __shared__ uint32_t staged[];
+  __shared__ BlockScratch<kSmallThreads> sh;
+  const int r = blockIdx.x;
+  const int n = row_len[r];
+  const float *row = logits + (int64_t)r * ld;
+  int32_t *out = idx + (int64_t)r * k;
+  if (n <= k) {
+    write_all(out, n, k);
+    return;
+  }
+  if constexpr (STAGED) {
+    for (int i = threadIdx.x; i < n; i += kSmallThreads) staged[i] = order_key(row[i]);
+    __syncthreads();
+    select_block<kSmallThreads>(StagedAcc{staged}, n, k, out, sh);
+  } else {
+    select_block<kSmallThreads>(RowAcc{row}, n, k, out, sh);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// few-row schedule
+// ------------------------------------------------------------------------------------
+struct MbWs {
+  uint32_t *hcnt;     // [R][C]          nonzero bins per chunk histogram
+  uint32_t *hlist;    // [R][C][kBins]   (digit << 16 | count) of the nonzero bins
+  uint32_t *meta;     // [R][2]          b*, number of scores with digit > b*
+  uint32_t *scnt;     // [R][C]          survivors per chunk
+  uint2 *slist;       // [R][C][kChunk]  (key, position) survivors per chunk
+  int C;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline size_t mb_ws_bytes(int R, int C) {
+  return align256(sizeof(uint32_t) * (size_t)R * C) * 2 +
+         align256(sizeof(uint32_t) * (size_t)R * C * kBins) + align256(sizeof(uint32_t) * (size_t)R * 2) +
+         sizeof(uint2) * (size_t)R * C * kChunk;
+}
+
+__host__ __device__ inline MbWs carve_ws(void *ws, int R, int C) {
+  uint8_t *p = static_cast<uint8_t *>(ws);
+  MbWs w;
+  w.hcnt = reinterpret_cast<uint32_t *>(p);
+  p += align256(sizeof(uint32_t) * (size_t)R * C);
+  w.scnt = reinterpret_cast<uint32_t *>(p);
+  p += align256(sizeof(uint32_t) * (size_t)R * C);
+  w.hlist = reinterpret_cast<uint32_t *>(p);
+  p += align256(sizeof(uint32_t) * (size_t)R * C * kBins);
+  w.meta = reinterpret_cast<uint32_t *>(p);
+  p += align256(sizeof(uint32_t) * (size_t)R * 2);
+  w.slist = reinterpret_cast<uint2 *>(p);
+  w.C = C;
+  return w;
+}
+
+// (1) per-chunk histogram of the 12-bit digit, compressed to its nonzero bins
+__global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(const float *__restrict__ logits,
+                                                               int64_t ld,
+                                                               const int32_t *__restrict__ row_len,
+                                                               int k, MbWs ws) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t wtot[kMbThreads / kWave];
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int n = row_len[r];
+  const int base = c * kChunk;
+  if (n <= k || base >= n) return;
+  const float *row = logits + (int64_t)r * ld;
+  for (int i = threadIdx.x; i < kBins; i += kMbThreads) lh[i] = 0;
+  __syncthreads();
+  {
+    // all 16 loads of a thread are issued before any is used
+    constexpr int kPerThread = kChunk / kMbThreads;
+    float v[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = base + threadIdx.x + j * kMbThreads;
+      v[j] = i < n ? row[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = base + threadIdx.x + j * kMbThreads;
+      if (i < n) atomicAdd(&lh[order_key(v[j]) >> (32 - kD0Bits)], 1u);
+    }
+  }
+  __syncthreads();
+  // ordered compaction of the nonzero bins: thread t owns bins 16t .. 16t+15
+  constexpr int PER = kBins / kMbThreads;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t nz = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) nz += lh[PER * threadIdx.x + j] ? 1u : 0u;
+  uint32_t inc = nz;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  uint32_t off = inc - nz, total = 0;
+  for (int w = 0; w < kMbThreads / kWave; ++w) {
+    off += (w < wave) ? wtot[w] : 0u;
+    total += wtot[w];
+  }
+  uint32_t *dst = ws.hlist + ((size_t)r * ws.C + c) * kBins;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t b = PER * threadIdx.x + j, cnt = lh[b];
+    if (cnt) dst[off++] = (b << 16) | cnt;
+  }
+  if (threadIdx.x == 0) ws.hcnt[(size_t)r * ws.C + c] = total;
+}
+
+// (2) merge the row's histograms, find b*, keep this chunk's survivors in position order
+__global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__restrict__ logits,
+                                                                 int64_t ld,
+                                                                 const int32_t *__restrict__ row_len,
+                                                                 int k, int32_t *__restrict__ idx,
+                                                                 MbWs ws) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t wtot[kMbThreads / kWave];
+  __shared__ uint32_t wcnt[kMbThreads / kWave];
+  __shared__ uint32_t s_bstar, s_above;
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int n = row_len[r];
+  const int base = c * kChunk;
+  if (n <= k) {
+    if (c == 0) write_all(idx + (int64_t)r * k, n, k);
+    return;
+  }
+  if (base >= n) return;
+  const int nblk = (n + kChunk - 1) / kChunk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kBins; i += kMbThreads) lh[i] = 0;
+  // chunk j's entries go to a wave picked round-robin; every load is independent
+  __syncthreads();
+  for (int j = wave; j < nblk; j += kMbThreads / kWave) {
+    const uint32_t nzj = ws.hcnt[(size_t)r * ws.C + j];
+    const uint32_t *src = ws.hlist + ((size_t)r * ws.C + j) * kBins;
+    for (uint32_t t = lane; t < nzj; t += kWave) {
+      const uint32_t e = src[t];
+      atomicAdd(&lh[e >> 16], e & 0xFFFFu);
+    }
+  }
+  __syncthreads();
+  // digit b* holding the k-th largest: thread t owns bins 4095-16t-j (descending)
+  constexpr int PER = kBins / kMbThreads;
+  uint32_t cc[PER], tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    cc[j] = lh[kBins - 1 - PER * threadIdx.x - j];
+    tot += cc[j];
+  }
+  uint32_t inc = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  uint32_t before = inc - tot;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+  if (before < (uint32_t)k && before + tot >= (uint32_t)k) {
+    uint32_t run = before;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (run + cc[j] >= (uint32_t)k) {
+        s_bstar = kBins - 1 - PER * threadIdx.x - j;
+        s_above = run;
+        break;
+      }
+      run += cc[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t bstar = s_bstar;
+  if (c == 0 && threadIdx.x == 0) {
+    ws.meta[2 * r] = bstar;
+    ws.meta[2 * r + 1] = s_above;
+  }
+  // survivors of this chunk (digit >= b*), in position order
+  const float *row = logits + (int64_t)r * ld;
+  constexpr int kPerWave = kChunk / (kMbThreads / kWave);   // 1024 scores per wave
+  constexpr int kIter = kPerWave / 64;
+  uint32_t keys[kIter];
+  uint32_t wc = 0;
+  const int wlo = base + wave * kPerWave;
+#pragma unroll
+  for (int j = 0; j < kIter; ++j) {
+    const int i = wlo + 64 * j + lane;
+    keys[j] = i < n ? order_key(row[i]) : 0u;
+    wc += __popcll(__ballot(i < n && (keys[j] >> (32 - kD0Bits)) >= bstar));
+  }
+  if (lane == 0) wcnt[wave] = wc;
+  __syncthreads();
+  uint32_t off = 0, total = 0;
+  for (int w = 0; w < kMbThreads / kWave; ++w) {
+    off += (w < wave) ? wcnt[w] : 0u;
+    total += wcnt[w];
+  }
+  uint2 *lst = ws.slist + ((size_t)r * ws.C + c) * kChunk;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int j = 0; j < kIter; ++j) {
+    const int i = wlo + 64 * j + lane;
+    const bool keep = i < n && (keys[j] >> (32 - kD0Bits)) >= bstar;
+    const uint64_t m = __ballot(keep);
+    if (keep) lst[off + __popcll(m & lt)] = make_uint2(keys[j], (uint32_t)i);
+    off += __popcll(m);
+  }
+  if (threadIdx.x == 0) ws.scnt[(size_t)r * ws.C + c] = total;
+}
+
+// (3) one workgroup per row: exact select among the survivors
+__global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *__restrict__ logits,
+                                                                   int64_t ld,
+                                                                   const int32_t *__restrict__ row_len,
+                                                                   int k, int32_t *__restrict__ idx,
+                                                                   MbWs ws) {
+  __shared__ BlockScratch<kSmallThreads> sh;
+  __shared__ uint32_t skey[kSurvivorCap];
+  __shared__ int32_t spos[kSurvivorCap];
+  __shared__ uint32_t coff[kMaxChunks + 1];
+  const int r = blockIdx.x;
+  const int n = row_len[r];
+  if (n <= k) return;
+  int32_t *out = idx + (int64_t)r * k;
+  const int nblk = (n + kChunk - 1) / kChunk;
+  {
+    // exclusive prefix of the per-chunk survivor counts (nblk <= kMaxChunks <= kSmallThreads)
+    const uint32_t cnt = threadIdx.x < nblk ? ws.scnt[(size_t)r * ws.C + threadIdx.x] : 0u;
+    uint32_t total;
+    const uint32_t before = block_excl_scan<kSmallThreads>(cnt, total, sh);
+    if (threadIdx.x < nblk) coff[threadIdx.x] = before;
+    if (threadIdx.x == 0) coff[nblk] = total;
+  }
+  __syncthreads();
+  const int M = (int)coff[nblk];
+  const int bstar = (int)ws.meta[2 * r];
+  const int above = (int)ws.meta[2 * r + 1];
+  if (M <= kSurvivorCap) {
+    for (int j = threadIdx.x / kWave; j < nblk; j += kSmallThreads / kWave) {
+      const uint2 *src = ws.slist + ((size_t)r * ws.C + j) * kChunk;
+      const int cj = (int)(coff[j + 1] - coff[j]);
+      for (int t = threadIdx.x % kWave; t < cj; t += kWave) {
+        const uint2 v = src[t];
+        skey[coff[j] + t] = v.x;
+        spos[coff[j] + t] = (int32_t)v.y;
+      }
+    }
+    __syncthreads();
+    select_block<kSmallThreads>(SurvivorAcc{skey, spos}, M, k, out, sh, bstar, k - above);
+  } else {
+    // degenerate score distributions (huge ties around the threshold): whole row
+    select_block<kSmallThreads>(RowAcc{logits + (int64_t)r * ld}, n, k, out, sh, bstar, k - above);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// dispatch
+// ------------------------------------------------------------------------------------
+static bool few_rows(int num_rows, int max_row_len) {
+  // Long rows that cannot fill the GPU with one workgroup each go to the chunked schedule.
+  return max_row_len > 8192 && num_rows < 256 && max_row_len <= kMaxChunks * kChunk;
+}
+
+size_t topk_workspace_bytes(int num_rows, int max_row_len, int) {
+  if (!few_rows(num_rows, max_row_len)) return 0;
+  const int C = (max_row_len + kChunk - 1) / kChunk;
+  return mb_ws_bytes(num_rows, C);
+}
 
 hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,
-                       int max_row_len, int k, int32_t *idx, void *, hipStream_t stream) {
-  if (max_row_len <= kTopkLdsElems) {
+                       int max_row_len, int k, int32_t *idx, void *ws, hipStream_t stream) {
+  if (few_rows(num_rows, max_row_len)) {
+    const int C = (max_row_len + kChunk - 1) / kChunk;
+    const MbWs w = carve_ws(ws, num_rows, C);
+    dim3 grid(C, num_rows);
+    topk_hist_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, w);
+    topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+    topk_final_kernel<<<num_rows, kSmallThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+    return hipGetLastError();
+  }
+  if (max_row_len <= kStageElems) {
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_rows_kernel<true>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_row_kernel<true>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)(sizeof(uint32_t) * kTopkLdsElems));
+                                         (int)(sizeof(uint32_t) * kStageElems));
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    topk_rows_kernel<true><<<num_rows, kTopkThreads, sizeof(uint32_t) * max_row_len, stream>>>(
+    topk_row_kernel<true><<<num_rows, kSmallThreads, sizeof(uint32_t) * max_row_len, stream>>>(
         logits, ld, row_len, k, idx);
+  } else {
+    topk_row_kernel<false><<<num_rows, kSmallThreads, 0, stream>>>(logits, ld, row_len, k, idx);
   }
-  else
-    topk_rows_kernel<false><<<num_rows, kTopkThreads, 0, stream>>>(logits, ld, row_len, k, idx);
   return hipGetLastError();
 }
 

@@ -129,8 +129,8 @@ def test_mla_validation(lib):
 
 
 def test_workspace_queries_are_consistent():
-    # few rows: split partials (fp32 [R, splits, H, d_v + 1]); many rows: no split
+    # few rows: split partials (bf16 [R, splits, H, d_v] + fp32 [R, splits, H]); many rows: none
     few = dsa.sparse_mla_workspace_size(8, 128, 512, 2048)
-    assert few % (4 * 8 * 128 * 513) == 0
+    assert few % (8 * 128 * (2 * 512 + 4)) == 0
     assert dsa.sparse_mla_workspace_size(4096, 128, 512, 2048) == 0
     assert dsa.sparse_mla_workspace_size(0, 128, 512, 2048) == 0

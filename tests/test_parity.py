@@ -229,3 +229,49 @@ def test_prefill_and_decode_entry_points_agree():
     ref, _ = oracle_mla(wl, idx.cpu().numpy())
     assert oracle.max_abs_rel(a.float().cpu().numpy(), ref) <= TOL["bf16"]
     assert oracle.max_abs_rel(b.float().cpu().numpy(), ref) <= TOL["bf16"]
+
+
+def test_hip_graph_replays_match_eager():
+    """The whole decode step captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) equals the eager result bit for bit."""
+    wl = workloads.decode([3000, 20000, 9000, 2047], idx_dtype="fp8", seed=21, device=DEV,
+                          name="graph")
+    rows = dev_rows(wl)
+    R = wl.num_rows
+    logits = torch.zeros((R, wl.max_row_len), dtype=torch.float32, device=DEV)
+    idx = torch.empty((R, wl.topk), dtype=torch.int32, device=DEV)
+    out = torch.empty((R, wl.H, wl.D_v), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((R, wl.H), dtype=torch.float32, device=DEV)
+    tk_ws = torch.zeros(max(dsa.topk_workspace_size(R, wl.max_row_len, wl.topk), 1),
+                        dtype=torch.uint8, device=DEV)
+    ml_ws = torch.zeros(max(dsa.sparse_mla_workspace_size(R, wl.H, wl.D_v, wl.topk), 1),
+                        dtype=torch.uint8, device=DEV)
+
+    def step():
+        dsa.indexer_logits(rows, wl.q_idx, wl.w, wl.k_idx, logits, q_scale=wl.q_scale,
+                           k_scale=wl.k_scale)
+        dsa.topk(logits, wl.row_len, wl.topk, wl.max_row_len, idx=idx, ws=tk_ws)
+        dsa.sparse_mla_decode(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=lse, ws=ml_ws)
+
+    say("graph capture")
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (logits, idx, out, lse)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (logits, idx, out, lse):
+            t.fill_(7)                         # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        valid = torch.arange(wl.max_row_len, device=DEV)[None, :] < wl.row_len[:, None]
+        assert torch.equal(logits[valid], ref[0][valid]), rep   # only s < row_len is written
+        for a, b in zip((idx, out, lse), ref[1:]):
+            assert torch.equal(a, b), rep
