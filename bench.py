@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows in the oracle sample")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches only (default: the step is captured in a HIP graph)")
     return p.parse_args()
@@ -130,6 +132,15 @@ def main():
 
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read_per_launch": n, "bytes_written_per_launch": n}))
+        return
     wl = workloads.config(args.config, device=dev)
     rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, seq_start=wl.seq_start,
                     page_table=wl.page_table)

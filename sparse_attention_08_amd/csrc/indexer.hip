@@ -89,6 +89,18 @@ constexpr int kIdxDim = 128;
 // MFMA operand reads (8 keys at the same logical chunk per LDS cycle) hit 8 distinct
 // bank groups.  The swizzle is applied on the global side, by choosing which chunk
 // each lane fetches.
+#ifndef DSA_IDX_SWZ
+#define DSA_IDX_SWZ 1
+#endif
+// XOR applied to the 16-byte chunk index of key `key` (low 3 bits for 128-byte fp8 rows,
+// low 4 bits for 256-byte bf16 rows): 16 consecutive keys read at one logical chunk land
+// on 16 distinct 16-byte bank groups.
+template <bool FP8>
+__device__ __forceinline__ int key_swz(int key) {
+  if constexpr (DSA_IDX_SWZ == 0) return key & 7;
+  if constexpr (FP8) return ((key >> 1) & 7) ^ ((key & 1) << 2);
+  return key & 15;
+}
 #ifndef DSA_IDX_DEPTH
 #define DSA_IDX_DEPTH 4
 #endif
@@ -117,12 +129,32 @@ typedef void __attribute__((address_space(3))) *lds_void_ptr;
 // leaves the export and LDS/scalar counters unconstrained (gfx9 field layout).
 constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// Keys are streamed once: the loads carry the non-temporal cache hint (aux bit 1).
 __device__ __forceinline__ void dma16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 16, 0, 2);
 }
 __device__ __forceinline__ void dma4(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 4, 0, 0);
 }
+
+// Per-lane constant part of a group's DMA addresses: for key instruction j, the key of the
+// group this lane's 16 bytes belong to and the byte offset of its source chunk.
+template <bool FP8>
+struct DmaLane {
+  static constexpr int kJ = kGroupBytes / 1024;
+  int key[kJ];
+  int byte[kJ];
+  __device__ __forceinline__ void init(int lane) {
+    using C = IdxCfg<FP8>;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int pos = 1024 * j + 16 * lane;             // byte position inside the slot
+      key[j] = pos / C::kRowBytes;
+      const int chunk = (pos % C::kRowBytes) >> 4;      // physical chunk
+      byte[j] = key[j] * C::kRowBytes + 16 * (chunk ^ key_swz<FP8>(key[j]));
+    }
+  }
+};
 
 // Issues the loads of the group starting at key s0 into `slot` (clamped into the span,
 // so a look-ahead past its end re-reads keys that are already in cache).  base_row:
@@ -132,7 +164,7 @@ template <bool FP8, bool PAGED>
 __device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__restrict__ k,
                                             const float *__restrict__ k_scale, int64_t base_row,
                                             int page_lane, int64_t p0, int64_t s0, int64_t s_last,
-                                            int lane) {
+                                            const DmaLane<FP8> &dl, int lane) {
   using C = IdxCfg<FP8>;
   s0 = min<int64_t>(s0, s_last & ~(int64_t)(C::kKeys - 1));
   int64_t row0;
@@ -142,17 +174,19 @@ __device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__rest
   } else {
     row0 = base_row + s0;
   }
+  const uint8_t *gbase = k + row0 * C::kRowBytes;
   const int last = (int)(s_last - s0);   // last valid key offset inside the group
+  if (last >= C::kKeys - 1) {            // the whole group lies inside the span
 #pragma unroll
-  for (int j = 0; j < kGroupBytes / 1024; ++j) {
-    const int pos = 1024 * j + 16 * lane;             // byte position inside the slot
-    const int key = pos / C::kRowBytes;
-    const int chunk = (pos % C::kRowBytes) >> 4;      // physical chunk
-    const int src_chunk = chunk ^ (key & 7);          // logical chunk stored there
-    const int kk = min(key, last);
-    dma16(k + (row0 + kk) * C::kRowBytes + 16 * src_chunk, slot + 1024 * j);
+    for (int j = 0; j < DmaLane<FP8>::kJ; ++j) dma16(gbase + dl.byte[j], slot + 1024 * j);
+    if constexpr (FP8) dma4(k_scale + row0 + lane, slot + kGroupBytes);
+  } else {
+#pragma unroll
+    for (int j = 0; j < DmaLane<FP8>::kJ; ++j)
+      dma16(gbase + dl.byte[j] + (min(dl.key[j], last) - dl.key[j]) * C::kRowBytes,
+            slot + 1024 * j);
+    if constexpr (FP8) dma4(k_scale + row0 + min(lane, last), slot + kGroupBytes);
   }
-  if constexpr (FP8) dma4(k_scale + row0 + min(lane, last), slot + kGroupBytes);
 }
 
 // MFMA + fused epilogue for the group in `slot`; returns in lane (g, c) the score of key
@@ -170,7 +204,7 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
     i32x4 kf[C::kChunks];
 #pragma unroll
     for (int i = 0; i < C::kChunks; ++i) {
-      const int chunk = (g * C::kChunks + i) ^ (key & 7);
+      const int chunk = (g * C::kChunks + i) ^ key_swz<FP8>(key);
       kf[i] = *reinterpret_cast<const i32x4 *>(slot + key * C::kRowBytes + 16 * chunk);
     }
     f32x4 acc[4];
@@ -193,7 +227,7 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], fmaxf(acc[hb][i], 0.f), v);
+      for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], relu(acc[hb][i]), v);
     v = sum_xor32(sum_xor16(v));   // sum over the 4 lane rows: all 64 heads
     if (g == u) mine = v;
   }
@@ -213,7 +247,7 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   i32x4 *q_lds = reinterpret_cast<i32x4 *>(smem);
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r];
   const int64_t blk_begin = (int64_t)blockIdx.x * kIdxWaves * keys_per_wave;
@@ -227,6 +261,7 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   int64_t base_row = 0;
   int page_lane = 0;
   const int64_t p0 = s_begin >> 6;
+  DmaLane<FP8> dl;
   // loads per group: kGroupBytes/1024 key instructions (+1 scale instruction for fp8)
   constexpr int kLoads = kGroupBytes / 1024 + (FP8 ? 1 : 0);
   if (active) {
@@ -237,10 +272,11 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
       base_row = rows.seq_start[b];
     }
     // the first kDepth-1 key groups start streaming before the query block is loaded
+    dl.init(lane);
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d)
       issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, page_lane, p0,
-                              s_begin + (int64_t)d * C::kKeys, s_last, lane);
+                              s_begin + (int64_t)d * C::kKeys, s_last, dl, lane);
   }
   {
     const i32x4 *qg = reinterpret_cast<const i32x4 *>(q + (int64_t)r * kIdxHeads * C::kRowBytes);
@@ -270,7 +306,7 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   for (int i = 0; i < n_groups; ++i) {
     issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
                             base_row, page_lane, p0, s_begin + (int64_t)(i + kDepth - 1) * C::kKeys,
-                            s_last, lane);
+                            s_last, dl, lane);
     // group i is older than the kDepth-1 groups issued after it: loads complete in order
     __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
     const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);

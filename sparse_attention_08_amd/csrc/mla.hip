@@ -127,13 +127,12 @@ constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;          // 1152 B per cache entry
 constexpr int kTile = 32;                    // entries per LDS tile
 constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB = 36 DMA instructions of 1 KB
-constexpr int kMlaThreads = 256;             // 4 waves x 16 heads
-constexpr int kMlaWaves = kMlaThreads / kWave;
+constexpr int kMlaWaves = 8;                 // 4 head groups x 2 value halves
+constexpr int kMlaThreads = kMlaWaves * kWave;
 constexpr int kHeadsPerBlock = 64;
 constexpr int kRing = DSA_MLA_DEPTH;          // LDS tile slots (kRing - 1 tiles in flight)
 constexpr int kMaxSlotsPerSplit = 2048;
-constexpr int kDmaPerWave = kTileBytes / 1024 / kMlaWaves;   // 9
-static_assert(kTileBytes % (1024 * kMlaWaves) == 0, "tile DMA must split evenly over waves");
+static_assert(kTileBytes % 1024 == 0, "tile DMA is whole 1 KB instructions");
 
 // XOR swizzle of the 16-byte chunk index inside its aligned group of 8 chunks.
 __device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 3) & 1); }
@@ -148,24 +147,33 @@ constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0
 
 struct MlaShared {
   uint8_t tiles[kRing][kTileBytes];
-  uint32_t crow[kMaxSlotsPerSplit];      // cache row of each slot of the split
+  uint32_t crow[kMaxSlotsPerSplit];        // cache row of each slot of the split
   uint32_t valid[kMaxSlotsPerSplit / 32];  // one bit per slot
+  float xmax[4][2][16];                    // per head group, half: tile max of each head
+  uint2 xp[4][2][kWave];                   // per head group, half: 4 bf16 weights per lane
+  float xl[4][2][16];                      // final partial sums of the two halves
 };
 
-// This wave's share of the DMA of tile `t` into `dst`: LDS position P = 1024*j + 16*lane of
-// the tile holds entry P / 1152, physical chunk (P % 1152) / 16, i.e. logical chunk
-// physical ^ swz(entry) of that entry's cache row.
+// The 36 DMA instructions of a tile go to waves 0..7 in turn (waves 0-3 issue 5, 4-7
+// issue 4).  LDS position P = 1024*j + 16*lane of the tile holds entry P / 1152,
+// physical chunk (P % 1152) / 16, i.e. logical chunk physical ^ swz(entry).
+constexpr int kTileDma = kTileBytes / 1024;   // 36
+__device__ __forceinline__ int tile_dma_count(int wave) {
+  return kTileDma / kMlaWaves + (wave < kTileDma % kMlaWaves ? 1 : 0);
+}
 __device__ __forceinline__ void issue_tile(uint8_t *dst, const uint32_t *crow_tile,
                                           const uint8_t *__restrict__ kv, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int j = wave * kDmaPerWave + i;
-    const int pos = 1024 * j + 16 * lane;
-    const int e = pos / kRowBytes;
-    const int pch = (pos - e * kRowBytes) >> 4;
-    const int lch = pch ^ swz(e);
-    const uint8_t *src = kv + (int64_t)crow_tile[e] * kRowBytes + 16 * lch;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(dst + 1024 * j), 16, 0, 0);
+  for (int i = 0; i < (kTileDma + kMlaWaves - 1) / kMlaWaves; ++i) {
+    const int j = wave + kMlaWaves * i;
+    if (j < kTileDma) {
+      const int pos = 1024 * j + 16 * lane;
+      const int e = pos / kRowBytes;
+      const int pch = (pos - e * kRowBytes) >> 4;
+      const int lch = pch ^ swz(e);
+      const uint8_t *src = kv + (int64_t)crow_tile[e] * kRowBytes + 16 * lch;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(dst + 1024 * j), 16, 0, 0);
+    }
   }
 }
 
@@ -182,6 +190,11 @@ __device__ __forceinline__ bool mla_coord(int bid, int R, int HG, int S, MlaCoor
   return c.r < R;
 }
 
+// Wave (hg, half) owns heads h0..h0+15 (hg = wave % 4) and value dims [256*half, +256)
+// (half = wave / 4).  Per tile it scores entries 8g + 4*half + i (i < 4) of its lane
+// row g: one 16-row MFMA block of S^T = C . Q^T.  The pair of waves sharing hg trade
+// their per-head tile maxima and their bf16 weights through LDS, so each then holds the
+// weights of all 32 entries for O^T += V^T . P^T over its value half.
 template <bool PAGED>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     RowsDev rows, int R, int H, float scale_log2, const uint16_t *__restrict__ q,
@@ -194,9 +207,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   if (!mla_coord(blockIdx.x, R, H / kHeadsPerBlock, splits, co)) return;
   const int r = co.r, split = co.split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hg = wave & 3, half = wave >> 2;
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r], b = rows.row_seq[r];
-  const int h0 = co.hgrp * kHeadsPerBlock + wave * 16;
+  const int h0 = co.hgrp * kHeadsPerBlock + hg * 16;
   const int slot_begin = split * slots_per_split;
   const int slot_end = min(k, slot_begin + slots_per_split);
   const int n_slots = max(0, slot_end - slot_begin);
@@ -226,9 +240,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   }
   __syncthreads();
 
-  f32x4 oacc[32];
+  f32x4 oacc[16];
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 16; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   // prologue: tiles 0 .. kRing-2 in flight (past the end: re-read the last tile, harmless)
@@ -239,9 +253,19 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       issue_tile(sh.tiles[d], sh.crow + t * kTile, kv, wave, lane);
     }
   }
-  const int arow0 = 8 * (c >> 2) + (c & 3);
-  const int arow1 = arow0 + 4;
+  // rows of the score tile this lane feeds as the MFMA A operand: result rows 4g+i map
+  // to entries 8g + 4*half + i
+  const int arow = 8 * (c >> 2) + (c & 3) + 4 * half;
+  const int a_even = 16 * (g ^ swz(arow)), a_odd = 16 * ((4 + g) ^ swz(arow));
   const int tr_i = c >> 2, tr_q = c & 3;
+  const int swa = swz(8 * g + tr_i), swb = swz(8 * g + tr_i + 4);
+  int offa[4], offb[4];
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4) {
+    offa[m4] = 16 * ((2 * m4 + (tr_q >> 1)) ^ swa);
+    offb[m4] = 16 * ((2 * m4 + (tr_q >> 1)) ^ swb);
+  }
+  const int n_dma = tile_dma_count(wave);
 
   for (int it = 0; it < n_tiles; ++it) {
     // the slot of tile it-1 is free once every wave has passed the previous iteration
@@ -250,77 +274,66 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       const int t = min(it + kRing - 1, n_tiles - 1);
       issue_tile(sh.tiles[(it + kRing - 1) % kRing], sh.crow + t * kTile, kv, wave, lane);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kDmaPerWave * (kRing - 1)));
+    if (n_dma == 5) __builtin_amdgcn_s_waitcnt(vmcnt_only(5 * (kRing - 1)));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(4 * (kRing - 1)));
     __syncthreads();   // every wave's share of tile `it` has landed
     const uint32_t valid = sh.valid[it];
     if (valid == 0) continue;
     const uint8_t *tile = sh.tiles[it % kRing];
-    // ---- scores S^T (entries x heads), K = 576 in 18 steps of 32.  Chunk 4t + g of row
-    // arow sits at 128*(t/2) + 16*(((4*(t&1)) + g) ^ swz(arow)): two per-lane bases plus
-    // compile-time offsets.
-    const uint8_t *a0b = tile + arow0 * kRowBytes;
-    const uint8_t *a1b = tile + arow1 * kRowBytes;
-    const int a0e = 16 * (g ^ swz(arow0)), a0o = 16 * ((4 + g) ^ swz(arow0));
-    const int a1e = 16 * (g ^ swz(arow1)), a1o = 16 * ((4 + g) ^ swz(arow1));
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- scores of entries 8g + 4*half + i for head c, K = 576 in 18 steps of 32
+    const uint8_t *ab = tile + arow * kRowBytes;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};   // even / odd k-steps
 #pragma unroll
-    for (int t = 0; t < 18; ++t) {
-      const int hi = 128 * (t >> 1);
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(a0b + hi + ((t & 1) ? a0o : a0e));
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(a1b + hi + ((t & 1) ? a1o : a1e));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[t], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[t], s1, 0, 0, 0);
+    for (int t = 0; t < 18; t += 2) {
+      const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(ab + 128 * (t >> 1) + a_even);
+      const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(ab + 128 * (t >> 1) + a_odd);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[t], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[t + 1], s1, 0, 0, 0);
     }
-    // ---- online softmax for head c over entries 8g .. 8g+7 (log2 domain).  The reference
-    // maximum m_run is only moved when the tile maximum exceeds it by more than 8 (a factor
-    // 256): weights then stay <= 2^8, fp32 accumulation is unaffected, and the rescale of
-    // the 128 accumulator registers is rare instead of per tile.
-    float z[8];
+    float z[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = ((valid >> (8 * g + i)) & 1u) ? s0[i] * scale_log2 : -INFINITY;
-      z[4 + i] = ((valid >> (8 * g + 4 + i)) & 1u) ? s1[i] * scale_log2 : -INFINITY;
-    }
-    float mx = z[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
-    mx = max_xor32(max_xor16(mx));                  // finite: the tile has a valid entry
-    const bool first = m_run == -INFINITY;          // accumulators still zero
+    for (int i = 0; i < 4; ++i)
+      z[i] = ((valid >> (8 * g + 4 * half + i)) & 1u) ? (s0[i] + s1[i]) * scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mx = max_xor32(max_xor16(mx));   // this half's maximum for head c
+    if (g == 0) sh.xmax[hg][half][c] = mx;
+    __syncthreads();
+    mx = fmaxf(mx, sh.xmax[hg][half ^ 1][c]);   // finite: the tile has a valid entry
+    // ---- lazy online softmax (log2 domain): the reference maximum only moves when the
+    // tile maximum exceeds it by more than 8, so weights stay <= 2^8 and the rescale of
+    // the accumulators is rare.  Both waves of the pair take identical decisions.
+    const bool first = m_run == -INFINITY;
     const bool move = first || mx > m_run + 8.f;
     if (__ballot(move && !first)) {
       const float alpha = move ? exp2f(m_run - mx) : 1.f;
 #pragma unroll
-      for (int nb = 0; nb < 32; ++nb)
+      for (int nb = 0; nb < 16; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
       l_run *= alpha;
     }
     if (move) m_run = mx;
-    float p[8], ps = 0.f;
+    float p[4], ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(z[e] - m_run);
-      ps += p[e];
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2f(z[i] - m_run);
+      ps += p[i];
     }
-    l_run += sum_xor32(sum_xor16(ps));
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];
-    // ---- O^T += V^T . P^T: A = V^T (dv rows 16nb + c, entries 8g + e via two transposing
-    // LDS reads), B = P^T (entries 8g + e, head c); result rows dv 16nb + 4g + i, column
-    // head c.  Chunk 2nb + (tr_q >> 1) of row ra sits at 128*(nb/4) + one of 4 per-lane
-    // offsets (nb % 4).
-    const uint8_t *vab = tile + (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1);
+    l_run += sum_xor32(sum_xor16(ps));   // this half's entries only
+    const uint32_t plo = (uint32_t)f32_to_bf16_bits(p[0]) | ((uint32_t)f32_to_bf16_bits(p[1]) << 16);
+    const uint32_t phi = (uint32_t)f32_to_bf16_bits(p[2]) | ((uint32_t)f32_to_bf16_bits(p[3]) << 16);
+    sh.xp[hg][half][lane] = make_uint2(plo, phi);
+    __syncthreads();
+    const uint2 oth = sh.xp[hg][half ^ 1][lane];
+    // B operand P^T: entries 8g + e (e < 4 from half 0, e >= 4 from half 1), head c
+    const uint2 p_lo = half == 0 ? make_uint2(plo, phi) : oth;
+    const uint2 p_hi = half == 0 ? oth : make_uint2(plo, phi);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(p_lo.x, p_lo.y, p_hi.x, p_hi.y));
+    // ---- O^T += V^T . P^T over this wave's value half: dv rows 256*half + 16nb + c
+    const uint8_t *vab = tile + (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1) + 512 * half;
     const uint8_t *vbb = vab + 4 * kRowBytes;
-    const int swa = swz(8 * g + tr_i), swb = swz(8 * g + tr_i + 4);
-    int offa[4], offb[4];
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
-      offa[m4] = 16 * ((2 * m4 + (tr_q >> 1)) ^ swa);
-      offb[m4] = 16 * ((2 * m4 + (tr_q >> 1)) ^ swb);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 32; ++nb) {
+    for (int nb = 0; nb < 16; ++nb) {
       const int hi = 128 * (nb >> 2);
       const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (lds_bf16x4_ptr)(vab + hi + offa[nb & 3]));
@@ -331,18 +344,21 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     }
   }
 
-  // no LDS write may still be in flight when the workgroup's LDS is released
+  // no LDS write may still be in flight when the workgroup's LDS is reused or released
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-  // ---- epilogue.  Lane (g, c) holds head h0 + c, dims 16nb + 4g + i.  The wave stages
-  // its 16 x 512 bf16 block in LDS (the tile ring is free now) and writes it back with
-  // 16-byte stores, 1 KB (one head row) per instruction.
-  const float linv = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse2 = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
+  // the two halves' sums make the full softmax denominator
+  if (g == 0) sh.xl[hg][half][c] = l_run;
   __syncthreads();
-  constexpr int kStageRow = kDv * 2 + 16;   // bytes per staged head row (padded)
+  const float l_tot = sh.xl[hg][0][c] + sh.xl[hg][1][c];
+  const float linv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  // ---- epilogue.  Lane (g, c) holds head h0 + c, dims 256*half + 16nb + 4g + i.  The
+  // wave stages its 16 x 256 bf16 block in LDS (the tile ring is free now) and writes it
+  // back with 16-byte stores.
+  constexpr int kStageRow = 256 * 2 + 16;   // bytes per staged head row (padded)
   uint8_t *stage = sh.tiles[0] + wave * 16 * kStageRow;
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) {
+  for (int nb = 0; nb < 16; ++nb) {
     const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[nb][0] * linv) |
                         ((uint32_t)f32_to_bf16_bits(oacc[nb][1] * linv) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[nb][2] * linv) |
@@ -353,17 +369,19 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   __builtin_amdgcn_wave_barrier();
   uint16_t *dst;
   if (splits == 1) {
-    dst = out + ((int64_t)r * H + h0) * kDv;
-    if (lse && g == 0) lse[(int64_t)r * H + h0 + c] = lse2 * kLn2;
+    dst = out + ((int64_t)r * H + h0) * kDv + 256 * half;
+    if (lse && g == 0 && half == 0) lse[(int64_t)r * H + h0 + c] = lse2 * kLn2;
   } else {
     const int64_t ph0 = ((int64_t)r * splits + split) * H + h0;
-    dst = part_o + ph0 * kDv;
-    if (g == 0) part_lse[ph0 + c] = lse2;
+    dst = part_o + ph0 * kDv + 256 * half;
+    if (g == 0 && half == 0) part_lse[ph0 + c] = lse2;
   }
+  // row j of the staged block = head h0 + j: 512 bytes = 32 lanes x 16 B; two rows per store
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + j * kStageRow + lane * 16);
-    *reinterpret_cast<i32x4 *>(dst + (int64_t)j * kDv + lane * 8) = v;
+  for (int j = 0; j < 16; j += 2) {
+    const int row = j + (lane >> 5), col = lane & 31;
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * kStageRow + col * 16);
+    *reinterpret_cast<i32x4 *>(dst + (int64_t)row * kDv + col * 8) = v;
   }
 }
 
