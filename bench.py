@@ -53,6 +53,11 @@ def parse():
                    help="only copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches only (default: the step is captured in a HIP graph)")
+    p.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
+                   help="no GPU work: 'trace NAME STATS_CSV CMD' writes profiles/NAME.md from a "
+                        "rocprofv3 --kernel-trace --stats run; 'pmc KERNEL FETCH_CSV WRITE_CSV "
+                        "COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB CONFIG CMD...' writes "
+                        "profiles/KERNEL_pmc.{json,md} (HBM bytes per launch)")
     return p.parse_args()
 
 
@@ -73,20 +78,86 @@ def algorithmic_flops(wl, lens):
     return idx_f, mla_f
 
 
-def pmc_traffic(kernel: str, units: float):
-    """HBM bytes per launch from a committed counter summary, or None when it is missing or
-    was taken on a different version of the kernel source."""
+def pmc_traffic(kernel: str, config: int):
+    """HBM bytes per launch from a committed counter summary, or None when it is missing, was
+    taken on another workload or on a different version of the kernel source."""
     path = os.path.join(PROFILES, f"{kernel}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             d = json.load(f)
-        if d.get("source_sha") != source_hash(kernel):
+        if d.get("source_sha") != source_hash(kernel) or d.get("workload_config") != config:
             return None
         return float(d["hbm_bytes_per_launch"])
     except Exception:
         return None
+
+
+def _short_name(name: str) -> str:
+    name = name.replace("void ", "")
+    return name.split("(")[0] if name.startswith("dsa::") else name[:60]
+
+
+def summarize_trace(out_name: str, stats_csv: str, command: str):
+    """profiles/<out_name>.md: the dsa kernels of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "dsa::" in r["Name"]]
+    lines = [f"# {out_name}", "", "Command (from the repository root, on one MI355X):", "",
+             "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | share of dsa time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / total:.1%} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, out_name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_per_dispatch(csv_path: str, match: str, counter: str):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {match!r} in {csv_path}")
+    return statistics.median(vals), len(vals)
+
+
+def summarize_pmc(kernel, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib,
+                  config, command):
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for a plain copy of copy_mib MiB."""
+    copy_kib = float(copy_mib) * 1024.0
+    cf, _ = _counter_per_dispatch(copy_fetch_csv, "copy", "FETCH_SIZE")
+    cw, _ = _counter_per_dispatch(copy_write_csv, "copy", "WRITE_SIZE")
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    kf, nf = _counter_per_dispatch(fetch_csv, "dsa::" + kernel, "FETCH_SIZE")
+    kw, nw = _counter_per_dispatch(write_csv, "dsa::" + kernel, "WRITE_SIZE")
+    read_b, write_b = kf * f_scale * 1024.0, kw * w_scale * 1024.0
+    d = {"kernel": kernel, "workload_config": int(config), "source_sha": source_hash(kernel),
+         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+         "copy_probe_mib": float(copy_mib), "copy_fetch_kib": cf, "copy_write_kib": cw,
+         "fetch_scale": f_scale, "write_scale": w_scale,
+         "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+         "hbm_bytes_per_launch": read_b + write_b, "dispatches": [nf, nw], "command": command}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"{kernel}_pmc.json"), "w") as f:
+        json.dump(d, f, indent=1)
+    with open(os.path.join(PROFILES, f"{kernel}_pmc.md"), "w") as f:
+        f.write(f"# HBM traffic of {kernel} (workload config {config})\n\n"
+                f"Commands (from the repository root; `<C>` is FETCH_SIZE, then WRITE_SIZE):\n\n"
+                f"```\n{command}\n```\n\n"
+                f"| quantity | value |\n|---|---:|\n"
+                f"| FETCH_SIZE per dispatch (median of {nf}) | {kf:,.0f} KiB |\n"
+                f"| WRITE_SIZE per dispatch (median of {nw}) | {kw:,.0f} KiB |\n"
+                f"| copy of {copy_mib} MiB: FETCH_SIZE / WRITE_SIZE | {cf:,.0f} / {cw:,.0f} KiB |\n"
+                f"| scale applied (bytes per counted byte): read / write | {f_scale:.3f} / {w_scale:.3f} |\n"
+                f"| HBM read bytes per launch | {read_b / 1e6:,.2f} MB |\n"
+                f"| HBM write bytes per launch | {write_b / 1e6:,.2f} MB |\n"
+                f"| kernel source sha256[:16] | `{d['source_sha']}` |\n")
 
 
 def cpu_baseline(wl_host, n_rows: int):
@@ -121,6 +192,15 @@ def cpu_baseline(wl_host, n_rows: int):
 
 def main():
     args = parse()
+    if args.summarize:
+        a = args.summarize
+        if a[0] == "trace" and len(a) >= 4:
+            summarize_trace(a[1], a[2], " ".join(a[3:]))
+        elif a[0] == "pmc" and len(a) >= 9:
+            summarize_pmc(a[1], a[2], a[3], a[4], a[5], a[6], a[7], " ".join(a[8:]))
+        else:
+            raise SystemExit("--summarize trace NAME CSV CMD... | pmc KERNEL F W CF CW MIB CONFIG CMD...")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is a single-GPU "
               f"build and measures no multi-GPU configuration.", file=sys.stderr)
@@ -249,7 +329,7 @@ def main():
     else:
         achieved = idx_b / (idx_mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic("indexer_mfma_kernel", R),
+                "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic("indexer_mfma_kernel", args.config),
                 "kernel": "indexer_mfma_kernel",
                 "algorithmic_bytes_per_launch": idx_b}
     res = {

@@ -273,8 +273,8 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
     }
     // the first kDepth-1 key groups start streaming before the query block is loaded
     dl.init(lane);
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
+    const int n_pro = (int)min<int64_t>(kDepth - 1, (s_last - s_begin) / C::kKeys + 1);
+    for (int d = 0; d < n_pro; ++d)
       issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, page_lane, p0,
                               s_begin + (int64_t)d * C::kKeys, s_last, dl, lane);
   }
@@ -304,17 +304,20 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   float *out = logits + (int64_t)r * ld;
   const int n_groups = (int)((s_end - s_begin + C::kKeys - 1) / C::kKeys);
   for (int i = 0; i < n_groups; ++i) {
-    issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
-                            base_row, page_lane, p0, s_begin + (int64_t)(i + kDepth - 1) * C::kKeys,
-                            s_last, dl, lane);
-    // group i is older than the kDepth-1 groups issued after it: loads complete in order
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
+    if (i + kDepth - 1 < n_groups) {
+      issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
+                              base_row, page_lane, p0, s_begin + (int64_t)(i + kDepth - 1) * C::kKeys,
+                              s_last, dl, lane);
+      // group i is older than the kDepth-1 groups issued after it: loads complete in order
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
+    } else {
+      // tail: nothing is issued past the span, so wait for every load still in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    }
     const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);
     const int64_t s = s_begin + (int64_t)i * C::kKeys + lane;
     if (lane < C::kKeys && s < s_end) out[s] = v;
   }
-  // the look-ahead loads past the span must land before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 }
 
 size_t indexer_lds_bytes(bool fp8) {
