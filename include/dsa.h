@@ -140,8 +140,9 @@ int dsa_topk(const float *logits, int64_t ld_logits, const int32_t *row_len, int
  * q   [R, H, d_qk] in `dtype`;  kv contiguous [cache rows, d_qk] / paged [pages, 64, d_qk]
  * idx [R, k] int32 positions (e.g. from dsa_topk);  out [R, H, d_v] in `dtype`
  * lse [R, H] f32 natural-log sum-exp, or NULL.
+ * softmax_scale must be finite and positive (DSA_ERR_INVALID_ARG otherwise).
  * Supported: f32 with 1 <= H <= 128, d_v <= d_qk <= 256;
- *            bf16 with H = 64 or 128, d_qk = 576, d_v = 512.  1 <= k <= 2048.
+ *            bf16 with H = 128, d_qk = 576, d_v = 512.  1 <= k <= 2048.
  * The decode entry points split the selections over several workgroups for few-row
  * batches and need ws of dsa_sparse_mla_workspace_size(R, H, d_v, k) bytes;
  * dsa_sparse_mla_prefill never splits and takes ws = NULL, ws_bytes = 0. */

@@ -66,7 +66,7 @@ int mla_common(const dsa_rows *rows, bool paged, MlaMode mode, int dtype, int n_
   if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
   if (n_heads <= 0 || d_qk <= 0 || d_v <= 0 || d_v > d_qk) return DSA_ERR_INVALID_ARG;
   if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_INVALID_ARG;
-  if (!isfinite(softmax_scale)) return DSA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DSA_ERR_INVALID_ARG;
   if (rows->num_rows == 0) return DSA_OK;
   if (!q || !kv || !idx || !out) return DSA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -79,7 +79,7 @@ int mla_common(const dsa_rows *rows, bool paged, MlaMode mode, int dtype, int n_
                                          static_cast<float *>(out), lse, s));
   }
   if (dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
-  if ((n_heads != 64 && n_heads != 128) || d_qk != 576 || d_v != 512) return DSA_ERR_UNSUPPORTED;
+  if (n_heads != 128 || d_qk != 576 || d_v != 512) return DSA_ERR_UNSUPPORTED;
   int splits = 1;
   if (mode == MlaMode::kDecode) {
     splits = dsa::mla_num_splits(rows->num_rows, n_heads, k);

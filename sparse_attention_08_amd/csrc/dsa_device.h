@@ -46,6 +46,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two floats -> packed bf16 pair (a in the low half), round to nearest even in hardware.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
 // Order-preserving map of a finite float to uint32 (larger float -> larger key),
 // with -0 folded onto +0 so the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -56,6 +63,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 // max(x, 0) as a signed-integer max on the bits: negative floats (and -0) have the sign
 // bit set and compare below 0, so this is ReLU in one instruction (no NaN quieting).
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every vector
+// memory operation of the wave (vmcnt(0)), which would drain global->LDS loads that are
+// meant to stay in flight across the barrier; here only LDS operations (lgkmcnt) are
+// completed first.  The signal fences keep the compiler from moving memory accesses
+// across it.  Global->LDS loads a wave issued must be awaited with its own vmcnt wait.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }

@@ -120,24 +120,28 @@ hipError_t launch_mla_f32(const RowsHost &rh, bool paged, int H, int Dqk, int Dv
 // bf16 MFMA path, d_qk = 576 (512 latent + 64 RoPE), d_v = 512.
 // ------------------------------------------------------------------------------------
 #ifndef DSA_MLA_DEPTH
-#define DSA_MLA_DEPTH 4
+#define DSA_MLA_DEPTH 3
 #endif
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;          // 1152 B per cache entry
 constexpr int kTile = 32;                    // entries per LDS tile
 constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB = 36 DMA instructions of 1 KB
-constexpr int kMlaWaves = 8;                 // 4 head groups x 2 value halves
+constexpr int kMlaWaves = 8;                 // 4 head quarters x 2 halves
 constexpr int kMlaThreads = kMlaWaves * kWave;
-constexpr int kHeadsPerBlock = 64;
+constexpr int kHeadsPerBlock = 128;
 constexpr int kRing = DSA_MLA_DEPTH;          // LDS tile slots (kRing - 1 tiles in flight)
 constexpr int kMaxSlotsPerSplit = 2048;
+constexpr int kSlotRounds = kMaxSlotsPerSplit / kMlaThreads;   // 4
 static_assert(kTileBytes % 1024 == 0, "tile DMA is whole 1 KB instructions");
 
-// XOR swizzle of the 16-byte chunk index inside its aligned group of 8 chunks.
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 3) & 1); }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+// XOR swizzle of the 16-byte chunk index inside its aligned group of 8 chunks, from row
+// bits 4, 1 and 3.  The 16 rows 8a + b (a, b < 4) read together by one score-operand
+// load, and the 8 rows 8g + i (g of one lane pair, i < 4) of one transposing value load,
+// then hit disjoint LDS banks (rows are 288 dwords apart, so odd rows start half a bank
+// sweep later).  Bit 2 is unused: rows r and r + 4 share the swizzle.
+__device__ __forceinline__ int swz(int row) {
+  return ((row >> 4) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
 }
 
 typedef bf16x4 __attribute__((address_space(3))) *lds_bf16x4_ptr;
@@ -147,54 +151,104 @@ constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0
 
 struct MlaShared {
   uint8_t tiles[kRing][kTileBytes];
-  uint32_t crow[kMaxSlotsPerSplit];        // cache row of each slot of the split
-  uint32_t valid[kMaxSlotsPerSplit / 32];  // one bit per slot
-  float xmax[4][2][16];                    // per head group, half: tile max of each head
-  uint2 xp[4][2][kWave];                   // per head group, half: 4 bf16 weights per lane
-  float xl[4][2][16];                      // final partial sums of the two halves
+  uint32_t crow[kMaxSlotsPerSplit];        // cache rows of the split's valid slots, compacted
+  f32x4 xs[kMlaWaves][4][kWave];           // partial score tiles traded between wave pairs
+  uint32_t wcount[kMlaWaves];
 };
 
 // The 36 DMA instructions of a tile go to waves 0..7 in turn (waves 0-3 issue 5, 4-7
 // issue 4).  LDS position P = 1024*j + 16*lane of the tile holds entry P / 1152,
 // physical chunk (P % 1152) / 16, i.e. logical chunk physical ^ swz(entry).
 constexpr int kTileDma = kTileBytes / 1024;   // 36
+constexpr int kDmaMax = (kTileDma + kMlaWaves - 1) / kMlaWaves;   // 5
+// One 16-byte-per-lane global->LDS load (1 KB per wave at `lds`, lane l at lds + 16 l).
+// Written as a two-instruction asm statement rather than the builtin: the compiler treats
+// every LDS access it cannot disambiguate from a pending global->LDS load as aliasing it
+// and, before the transposing LDS reads of the value product, would wait for all such
+// loads, draining the tile ring each iteration.  The instruction writes no register, its
+// operands are consumed at issue, and the kernel waits for the data with explicit vmcnt
+// counts (loads complete in order) before any wave reads the tile.
+__device__ __forceinline__ void dma16(const void *src, const void *lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la)
+                   : "memory");
+}
+
 __device__ __forceinline__ int tile_dma_count(int wave) {
   return kTileDma / kMlaWaves + (wave < kTileDma % kMlaWaves ? 1 : 0);
 }
-__device__ __forceinline__ void issue_tile(uint8_t *dst, const uint32_t *crow_tile,
-                                          const uint8_t *__restrict__ kv, int wave, int lane) {
+// Per-lane constants of a wave's DMA instructions, two 16-bit fields per word: for
+// instruction i, (tile entry) | (byte offset of the source chunk inside the entry) << 5.
+struct TileDma {
+  uint32_t pk[(kDmaMax + 1) / 2];
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < (kTileDma + kMlaWaves - 1) / kMlaWaves; ++i) {
-    const int j = wave + kMlaWaves * i;
-    if (j < kTileDma) {
-      const int pos = 1024 * j + 16 * lane;
-      const int e = pos / kRowBytes;
-      const int pch = (pos - e * kRowBytes) >> 4;
-      const int lch = pch ^ swz(e);
-      const uint8_t *src = kv + (int64_t)crow_tile[e] * kRowBytes + 16 * lch;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(dst + 1024 * j), 16, 0, 0);
+    for (int w = 0; w < (kDmaMax + 1) / 2; ++w) pk[w] = 0;
+#pragma unroll
+    for (int i = 0; i < kDmaMax; ++i) {
+      const int pos = 1024 * (wave + kMlaWaves * i) + 16 * lane;
+      const int e = min(pos / kRowBytes, kTile - 1);   // instructions past the tile: unused
+      const int byte = 16 * (((pos - e * kRowBytes) >> 4) ^ swz(e)) & 2047;
+      pk[i >> 1] |= (uint32_t)(e | (byte << 5)) << (16 * (i & 1));
     }
+  }
+};
+__device__ __forceinline__ void issue_tile(uint8_t *dst, const uint32_t *crow_tile,
+                                          const uint8_t *__restrict__ kv, const TileDma &td,
+                                          int n_dma, int wave) {
+  // opaque copies: keeps the compiler from hoisting per-instruction 64-bit addresses out
+  // of the tile loop (they would not fit in registers)
+  uint32_t p[(kDmaMax + 1) / 2];
+#pragma unroll
+  for (int w = 0; w < (kDmaMax + 1) / 2; ++w) {
+    p[w] = td.pk[w];
+    __asm__ volatile("" : "+v"(p[w]));
+  }
+  uint32_t cr[kDmaMax], byte[kDmaMax];
+#pragma unroll
+  for (int i = 0; i < kDmaMax; ++i) {
+    const uint32_t f = (p[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    cr[i] = crow_tile[f & 31u];
+    byte[i] = f >> 5;
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaMax; ++i) {
+    if (i < kDmaMax - 1 || n_dma == kDmaMax)
+      dma16(kv + (uint64_t)cr[i] * kRowBytes + byte[i], dst + 1024 * (wave + kMlaWaves * i));
   }
 }
 
-// Workgroup -> (row, head group, split).  Workgroups are dealt to the 8 XCDs round-robin by
-// id, so all workgroups of a row (its splits and both head groups) land on one XCD: the
-// gathered entries are shared through that XCD's L2 and the partials stay in it.
-struct MlaCoord { int r, hgrp, split; };
-__device__ __forceinline__ bool mla_coord(int bid, int R, int HG, int S, MlaCoord &c) {
+// Waits until at most `younger` tiles of N loads each (issued after the awaited one) are
+// still in flight; vector-memory loads complete in issue order.
+static_assert(kRing >= 2 && kRing <= 4, "the ring keeps at most two tiles younger than the current");
+template <int N>
+__device__ __forceinline__ void wait_younger(int younger) {
+  if (kRing - 2 >= 2 && younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * N));
+  else if (kRing - 2 >= 1 && younger >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(N));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+}
+
+// Workgroup -> (row, split).  Workgroups are dealt to the 8 XCDs round-robin by id, so
+// all splits of a row land on one XCD: their query block and partials share its L2.
+struct MlaCoord { int r, split; };
+__device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
   const int x = bid & 7, j = bid >> 3;
-  c.r = (j / (HG * S)) * 8 + x;
-  const int rem = j % (HG * S);
-  c.hgrp = rem / S;
-  c.split = rem % S;
+  c.r = (j / S) * 8 + x;
+  c.split = j % S;
   return c.r < R;
 }
 
-// Wave (hg, half) owns heads h0..h0+15 (hg = wave % 4) and value dims [256*half, +256)
-// (half = wave / 4).  Per tile it scores entries 8g + 4*half + i (i < 4) of its lane
-// row g: one 16-row MFMA block of S^T = C . Q^T.  The pair of waves sharing hg trade
-// their per-head tile maxima and their bf16 weights through LDS, so each then holds the
-// weights of all 32 entries for O^T += V^T . P^T over its value half.
+// One workgroup: all 128 heads of query row r over one split of its top-k slots.
+// Wave (hq, vh) = (wave % 4, wave / 4) owns heads 32hq .. 32hq+31 and half vh of both
+// contractions: the even (vh = 0) or odd (vh = 1) 32-dim steps of the 576-dim scores,
+// and value dims [256 vh, 256 vh + 256).  Per tile of 32 entries it forms its partial
+// S^T = C . Q^T (entries as MFMA rows, 2 x 2 blocks of 16 entries x 16 heads, q in
+// registers), trades it with its partner wave (hq, 1 - vh) through LDS, so both hold the
+// full scores and take identical softmax decisions, then accumulates
+// O^T += V^T . P^T over its value half, V^T read from the same LDS tile with the
+// transposing LDS read.  Entry rows of the score blocks are permuted (block kb, row
+// 4g + i <-> entry 8g + 4kb + i) so that each lane's weights are exactly the B operand
+// of the value product: no exchange of weights is needed.
 template <bool PAGED>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     RowsDev rows, int R, int H, float scale_log2, const uint16_t *__restrict__ q,
@@ -204,184 +258,233 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared &sh = *reinterpret_cast<MlaShared *>(mla_smem);
   MlaCoord co;
-  if (!mla_coord(blockIdx.x, R, H / kHeadsPerBlock, splits, co)) return;
+  if (!mla_coord(blockIdx.x, R, splits, co)) return;
   const int r = co.r, split = co.split;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hg = wave & 3, half = wave >> 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hq = wave & 3, vh = wave >> 2;
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r], b = rows.row_seq[r];
-  const int h0 = co.hgrp * kHeadsPerBlock + hg * 16;
+  const int h0 = hq * 32;
   const int slot_begin = split * slots_per_split;
-  const int slot_end = min(k, slot_begin + slots_per_split);
-  const int n_slots = max(0, slot_end - slot_begin);
-  const int n_tiles = (n_slots + kTile - 1) / kTile;
-  const int32_t *idx_row = idx + (int64_t)r * k;
+  const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
+  const int32_t *idx_row = idx + (int64_t)r * k + slot_begin;
 
-  // q^T operand: head h0 + c, dims 32t + 8g .. +8 for t < 18 (in flight during the
+  // q^T operands: head h0 + 16hb + c, dims 64t + 32vh + 8g .. +8 (in flight during the
   // slot resolution below)
-  bf16x8 qf[18];
+  bf16x8 qf[2][9];
   {
-    const bf16x8 *qp =
-        reinterpret_cast<const bf16x8 *>(q + ((int64_t)r * H + h0 + c) * kDqk + 8 * g);
 #pragma unroll
-    for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
-  }
-  // cache rows and validity of every slot of the split (invalid slots read position 0)
-  const int64_t row_of_0 = cache_row<PAGED>(rows, b, 0);
-  for (int t0 = 0; t0 < n_tiles * kTile; t0 += kMlaThreads) {
-    const int t = t0 + threadIdx.x;
-    int s = -1;
-    if (t < n_slots) s = idx_row[slot_begin + t];
-    const bool ok = t < n_slots && s >= 0 && s < len;
-    const uint64_t vm = __ballot(ok);
-    if (t < n_tiles * kTile) sh.crow[t] = (uint32_t)(ok ? cache_row<PAGED>(rows, b, s) : row_of_0);
-    if (lane == 0 && t < n_tiles * kTile) sh.valid[t >> 5] = (uint32_t)vm;
-    if (lane == 32 && t < n_tiles * kTile) sh.valid[t >> 5] = (uint32_t)(vm >> 32);
-  }
-  __syncthreads();
-
-  f32x4 oacc[16];
+    for (int hb = 0; hb < 2; ++hb) {
+      const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+          q + ((int64_t)r * H + h0 + 16 * hb + c) * kDqk + 32 * vh + 8 * g);
 #pragma unroll
-  for (int nb = 0; nb < 16; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // prologue: tiles 0 .. kRing-2 in flight (past the end: re-read the last tile, harmless)
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int d = 0; d < kRing - 1; ++d) {
-      const int t = min(d, n_tiles - 1);
-      issue_tile(sh.tiles[d], sh.crow + t * kTile, kv, wave, lane);
+      for (int t = 0; t < 9; ++t) qf[hb][t] = qp[8 * t];
     }
   }
-  // rows of the score tile this lane feeds as the MFMA A operand: result rows 4g+i map
-  // to entries 8g + 4*half + i
-  const int arow = 8 * (c >> 2) + (c & 3) + 4 * half;
-  const int a_even = 16 * (g ^ swz(arow)), a_odd = 16 * ((4 + g) ^ swz(arow));
-  const int tr_i = c >> 2, tr_q = c & 3;
-  const int swa = swz(8 * g + tr_i), swb = swz(8 * g + tr_i + 4);
-  int offa[4], offb[4];
+  // cache rows of the valid slots, compacted in slot order
+  int n_valid = 0;
+  {
+    int sv[kSlotRounds];
 #pragma unroll
-  for (int m4 = 0; m4 < 4; ++m4) {
-    offa[m4] = 16 * ((2 * m4 + (tr_q >> 1)) ^ swa);
-    offb[m4] = 16 * ((2 * m4 + (tr_q >> 1)) ^ swb);
+    for (int j = 0; j < kSlotRounds; ++j) {
+      const int t = j * kMlaThreads + threadIdx.x;
+      sv[j] = t < n_slots ? idx_row[t] : -1;
+    }
+    int64_t crow_v[kSlotRounds];
+#pragma unroll
+    for (int j = 0; j < kSlotRounds; ++j)
+      crow_v[j] = (sv[j] >= 0 && sv[j] < len) ? cache_row<PAGED>(rows, b, sv[j]) : -1;
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int j = 0; j < kSlotRounds; ++j) {
+      if (j * kMlaThreads >= n_slots) break;
+      const bool ok = crow_v[j] >= 0;
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) sh.wcount[wave] = (uint32_t)__popcll(m);
+      lds_barrier();
+      int before = n_valid, total = 0;
+#pragma unroll
+      for (int w = 0; w < kMlaWaves; ++w) {
+        const int cw = (int)sh.wcount[w];
+        before += w < wave ? cw : 0;
+        total += cw;
+      }
+      if (ok) sh.crow[before + __popcll(m & lt)] = (uint32_t)crow_v[j];
+      n_valid += total;
+      lds_barrier();
+    }
   }
+  const int n_tiles = (n_valid + kTile - 1) / kTile;
+  // the tail of the last tile gathers a harmless valid row and is masked off
+  if (threadIdx.x < n_tiles * kTile - n_valid) sh.crow[n_valid + threadIdx.x] = sh.crow[0];
+  lds_barrier();
+
+  f32x4 oacc[2][16];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) oacc[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+
   const int n_dma = tile_dma_count(wave);
+  TileDma td;
+  td.init(wave, lane);
+  // prologue: tiles 0 .. kRing-2 in flight
+  for (int d = 0; d < kRing - 1 && d < n_tiles; ++d)
+    issue_tile(sh.tiles[d], sh.crow + d * kTile, kv, td, n_dma, wave);
 
+  // score operand rows: block kb, lane row c <-> entry 8(c>>2) + (c&3) + 4kb; both rows of a
+  // lane share one swizzle, and its dims 64t + 32vh + 8g are chunk 8t + 4vh + g
+  const int arow = 8 * (c >> 2) + (c & 3);
+  const int a_off = arow * kRowBytes + 16 * ((4 * vh + g) ^ swz(arow));
+  // value operand: transposing reads of entries 8g + tr_i (+4), dims 256vh + 16nb + 4tr_q
+  // (chunk 2m + (tr_q >> 1)) ^ swz = 2 (m ^ (swz >> 1)) + ((tr_q >> 1) ^ (swz & 1)); entries
+  // 8g + tr_i and 8g + tr_i + 4 share the swizzle, so the second is an immediate offset
+  const int tr_i = c >> 2, tr_q = c & 3;
+  const int swa = swz(8 * g + tr_i);
+  const int ua = swa >> 1;
+  const int v_off_a = (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1) + 512 * vh +
+                      16 * ((tr_q >> 1) ^ (swa & 1));
+  f32x4 *xs_mine = sh.xs[wave][0] + lane;
+  const f32x4 *xs_peer = sh.xs[wave ^ 4][0] + lane;
+
+  uint32_t slot_use = 0, slot_issue = (kRing - 1) * kTileBytes;   // byte offsets in the ring
   for (int it = 0; it < n_tiles; ++it) {
-    // the slot of tile it-1 is free once every wave has passed the previous iteration
-    __syncthreads();
-    {
-      const int t = min(it + kRing - 1, n_tiles - 1);
-      issue_tile(sh.tiles[(it + kRing - 1) % kRing], sh.crow + t * kTile, kv, wave, lane);
+    // tiles it+1 .. it+kRing-2 (those that exist) were issued after tile `it`
+    const int younger = min(kRing - 2, n_tiles - 1 - it);
+    if (n_dma == 5) wait_younger<5>(younger);
+    else wait_younger<4>(younger);
+    // every wave's share of tile `it` has landed, and every wave is done with tile it-1
+    lds_barrier();
+    if (it + kRing - 1 < n_tiles)
+      issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kRing - 1) * kTile, kv, td, n_dma, wave);
+    const uint8_t *tile = sh.tiles[0] + slot_use;
+    // ring slots advance by one tile and wrap (uniform, loop-carried: no division)
+    slot_use = slot_use + kTileBytes == kRing * kTileBytes ? 0u : slot_use + kTileBytes;
+    slot_issue = slot_issue + kTileBytes == kRing * kTileBytes ? 0u : slot_issue + kTileBytes;
+    // ---- partial scores over this wave's 9 dim steps
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) sc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 9; ++t) {
+      const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(tile + a_off + 128 * t);
+      const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(tile + a_off + 4 * kRowBytes + 128 * t);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        sc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[hb][t], sc[0][hb], 0, 0, 0);
+        sc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[hb][t], sc[1][hb], 0, 0, 0);
+      }
     }
-    if (n_dma == 5) __builtin_amdgcn_s_waitcnt(vmcnt_only(5 * (kRing - 1)));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_only(4 * (kRing - 1)));
-    __syncthreads();   // every wave's share of tile `it` has landed
-    const uint32_t valid = sh.valid[it];
-    if (valid == 0) continue;
-    const uint8_t *tile = sh.tiles[it % kRing];
-    // ---- scores of entries 8g + 4*half + i for head c, K = 576 in 18 steps of 32
-    const uint8_t *ab = tile + arow * kRowBytes;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};   // even / odd k-steps
+    // ---- trade partial scores with the partner wave; both then hold identical sums
 #pragma unroll
-    for (int t = 0; t < 18; t += 2) {
-      const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(ab + 128 * (t >> 1) + a_even);
-      const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(ab + 128 * (t >> 1) + a_odd);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[t], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[t + 1], s1, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) xs_mine[kWave * j] = sc[j >> 1][j & 1];
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j >> 1][j & 1] += xs_peer[kWave * j];
+    // only the last tile can hold padding entries: their scores become -inf
+    const int nv = n_valid - it * kTile;
+    if (nv < kTile) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (8 * g + 4 * kb + i >= nv) {
+            sc[kb][0][i] = -INFINITY;
+            sc[kb][1][i] = -INFINITY;
+          }
     }
-    float z[4];
+    bf16x8 pf[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      z[i] = ((valid >> (8 * g + 4 * half + i)) & 1u) ? (s0[i] + s1[i]) * scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mx = max_xor32(max_xor16(mx));   // this half's maximum for head c
-    if (g == 0) sh.xmax[hg][half][c] = mx;
-    __syncthreads();
-    mx = fmaxf(mx, sh.xmax[hg][half ^ 1][c]);   // finite: the tile has a valid entry
-    // ---- lazy online softmax (log2 domain): the reference maximum only moves when the
-    // tile maximum exceeds it by more than 8, so weights stay <= 2^8 and the rescale of
-    // the accumulators is rare.  Both waves of the pair take identical decisions.
-    const bool first = m_run == -INFINITY;
-    const bool move = first || mx > m_run + 8.f;
-    if (__ballot(move && !first)) {
-      const float alpha = move ? exp2f(m_run - mx) : 1.f;
+    for (int hb = 0; hb < 2; ++hb) {
+      // tile maximum of head h0 + 16hb + c in the scaled log2 domain (scale > 0, finite:
+      // the tile has a valid entry)
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][hb][0], sc[0][hb][1]), fmaxf(sc[0][hb][2], sc[0][hb][3])),
+                       fmaxf(fmaxf(sc[1][hb][0], sc[1][hb][1]), fmaxf(sc[1][hb][2], sc[1][hb][3])));
+      mx = max_xor32(max_xor16(mx)) * scale_log2;
+      // lazy online softmax (log2 domain): the reference maximum only moves when the tile
+      // maximum exceeds it by more than 8, so weights stay <= 2^8 and rescales are rare
+      const bool first = m_run[hb] == -INFINITY;
+      const bool move = first || mx > m_run[hb] + 8.f;
+      if (__ballot(move && !first)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run[hb] - mx) : 1.f;
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb)
+        for (int nb = 0; nb < 16; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
-      l_run *= alpha;
+          for (int i = 0; i < 4; ++i) oacc[hb][nb][i] *= alpha;
+        l_part[hb] *= alpha;
+      }
+      if (move) m_run[hb] = mx;
+      const float neg_m = -m_run[hb];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 2][hb][e & 3], scale_log2, neg_m));
+        l_part[hb] += p[e];
+      }
+      pf[hb] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
     }
-    if (move) m_run = mx;
-    float p[4], ps = 0.f;
+    // ---- O^T += V^T . P^T over this wave's value half: value rows 256vh + 16nb + c
+    const uint8_t *va[4];   // per-lane bases; the 128-byte group and the +4 entries are immediates
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = exp2f(z[i] - m_run);
-      ps += p[i];
-    }
-    l_run += sum_xor32(sum_xor16(ps));   // this half's entries only
-    const uint32_t plo = (uint32_t)f32_to_bf16_bits(p[0]) | ((uint32_t)f32_to_bf16_bits(p[1]) << 16);
-    const uint32_t phi = (uint32_t)f32_to_bf16_bits(p[2]) | ((uint32_t)f32_to_bf16_bits(p[3]) << 16);
-    sh.xp[hg][half][lane] = make_uint2(plo, phi);
-    __syncthreads();
-    const uint2 oth = sh.xp[hg][half ^ 1][lane];
-    // B operand P^T: entries 8g + e (e < 4 from half 0, e >= 4 from half 1), head c
-    const uint2 p_lo = half == 0 ? make_uint2(plo, phi) : oth;
-    const uint2 p_hi = half == 0 ? oth : make_uint2(plo, phi);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(p_lo.x, p_lo.y, p_hi.x, p_hi.y));
-    // ---- O^T += V^T . P^T over this wave's value half: dv rows 256*half + 16nb + c
-    const uint8_t *vab = tile + (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1) + 512 * half;
-    const uint8_t *vbb = vab + 4 * kRowBytes;
+    for (int m4 = 0; m4 < 4; ++m4) va[m4] = tile + v_off_a + 32 * (m4 ^ ua);
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) {
       const int hi = 128 * (nb >> 2);
-      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4_ptr)(vab + hi + offa[nb & 3]));
-      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4_ptr)(vbb + hi + offb[nb & 3]));
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(va[nb & 3] + hi));
+      const bf16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(va[nb & 3] + 4 * kRowBytes + hi));
       const bf16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pf, oacc[nb], 0, 0, 0);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        oacc[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pf[hb], oacc[hb][nb], 0, 0, 0);
     }
   }
+  // every wave is done with the ring before it is reused for staging (no load is in flight:
+  // the last iteration waited for all of them)
+  lds_barrier();
 
-  // no LDS write may still be in flight when the workgroup's LDS is reused or released
-  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-  // the two halves' sums make the full softmax denominator
-  if (g == 0) sh.xl[hg][half][c] = l_run;
-  __syncthreads();
-  const float l_tot = sh.xl[hg][0][c] + sh.xl[hg][1][c];
-  const float linv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-  // ---- epilogue.  Lane (g, c) holds head h0 + c, dims 256*half + 16nb + 4g + i.  The
-  // wave stages its 16 x 256 bf16 block in LDS (the tile ring is free now) and writes it
-  // back with 16-byte stores.
+  // ---- epilogue.  Lane (g, c) holds head h0 + 16hb + c, dims 256vh + 16nb + 4g + i.  Each
+  // head block is staged in LDS (16 heads x 256 dims per wave) and written with 16-byte
+  // stores.
   constexpr int kStageRow = 256 * 2 + 16;   // bytes per staged head row (padded)
   uint8_t *stage = sh.tiles[0] + wave * 16 * kStageRow;
 #pragma unroll
-  for (int nb = 0; nb < 16; ++nb) {
-    const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[nb][0] * linv) |
-                        ((uint32_t)f32_to_bf16_bits(oacc[nb][1] * linv) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[nb][2] * linv) |
-                        ((uint32_t)f32_to_bf16_bits(oacc[nb][3] * linv) << 16);
-    *reinterpret_cast<uint2 *>(stage + c * kStageRow + (16 * nb + 4 * g) * 2) = make_uint2(lo, hi);
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
-  __builtin_amdgcn_wave_barrier();
-  uint16_t *dst;
-  if (splits == 1) {
-    dst = out + ((int64_t)r * H + h0) * kDv + 256 * half;
-    if (lse && g == 0 && half == 0) lse[(int64_t)r * H + h0 + c] = lse2 * kLn2;
-  } else {
-    const int64_t ph0 = ((int64_t)r * splits + split) * H + h0;
-    dst = part_o + ph0 * kDv + 256 * half;
-    if (g == 0 && half == 0) part_lse[ph0 + c] = lse2;
-  }
-  // row j of the staged block = head h0 + j: 512 bytes = 32 lanes x 16 B; two rows per store
+  for (int hb = 0; hb < 2; ++hb) {
+    const float l_tot = sum_xor32(sum_xor16(l_part[hb]));
+    const float linv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_run[hb] + log2f(l_tot) : -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    const int row = j + (lane >> 5), col = lane & 31;
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * kStageRow + col * 16);
-    *reinterpret_cast<i32x4 *>(dst + (int64_t)row * kDv + col * 8) = v;
+    for (int nb = 0; nb < 16; ++nb) {
+      const uint32_t lo = pack_bf16x2(oacc[hb][nb][0] * linv, oacc[hb][nb][1] * linv);
+      const uint32_t hi = pack_bf16x2(oacc[hb][nb][2] * linv, oacc[hb][nb][3] * linv);
+      *reinterpret_cast<uint2 *>(stage + c * kStageRow + (16 * nb + 4 * g) * 2) = make_uint2(lo, hi);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int hh = h0 + 16 * hb;
+    uint16_t *dst;
+    if (splits == 1) {
+      dst = out + ((int64_t)r * H + hh) * kDv + 256 * vh;
+      if (lse && g == 0 && vh == 0) lse[(int64_t)r * H + hh + c] = lse2 * kLn2;
+    } else {
+      const int64_t ph0 = ((int64_t)r * splits + split) * H + hh;
+      dst = part_o + ph0 * kDv + 256 * vh;
+      if (g == 0 && vh == 0) part_lse[ph0 + c] = lse2;
+    }
+    // row j of the staged block = head hh + j: 512 bytes = 32 lanes x 16 B; two rows per store
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const int row = j + (lane >> 5), col = lane & 31;
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * kStageRow + col * 16);
+      *reinterpret_cast<i32x4 *>(dst + (int64_t)row * kDv + col * 8) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // staging reads done before the next block's writes
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -389,7 +492,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
 // A workgroup of 256 threads merges 4 heads of one row (thread: 8 dims of one head);
 // workgroups are dealt to XCDs like the split workgroups of their row.
 constexpr int kCombHeads = 4;
-constexpr int kMaxCombine = 16;   // largest split count
+constexpr int kMaxCombine = 32;   // largest split count
 __global__ __launch_bounds__(256) void mla_combine_kernel(int R, int H, int splits,
                                                           const uint16_t *__restrict__ part_o,
                                                           const float *__restrict__ part_lse,
@@ -437,17 +540,20 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int R, int H, int spli
   i32x4 o;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    o[e] = (int)((uint32_t)f32_to_bf16_bits(acc[2 * e] * inv) |
-                 ((uint32_t)f32_to_bf16_bits(acc[2 * e + 1] * inv) << 16));
+    o[e] = (int)pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
   *reinterpret_cast<i32x4 *>(out + ((int64_t)r * H + h) * kDv + d0) = o;
   if (lse && (threadIdx.x & 63) == 0)
     lse[(int64_t)r * H + h] = wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
+#ifndef DSA_MLA_MIN_TILES
+#define DSA_MLA_MIN_TILES 2
+#endif
 int mla_num_splits(int num_rows, int n_heads, int k) {
+  // about one workgroup per CU for few-row batches, at least DSA_MLA_MIN_TILES tiles each
   const int base = num_rows * (n_heads / kHeadsPerBlock > 0 ? n_heads / kHeadsPerBlock : 1);
   int splits = (256 + base - 1) / base;
-  const int max_splits = (k + 4 * kTile - 1) / (4 * kTile);   // at least 4 tiles per split
+  const int max_splits = (k + DSA_MLA_MIN_TILES * kTile - 1) / (DSA_MLA_MIN_TILES * kTile);
   if (splits > max_splits) splits = max_splits;
   if (splits > kMaxCombine) splits = kMaxCombine;
   if (splits < 1) splits = 1;
@@ -490,8 +596,8 @@ hipError_t launch_mla_bf16(const RowsHost &rh, bool paged, int H, float scale, c
     part_o = static_cast<uint16_t *>(ws);
     part_lse = reinterpret_cast<float *>(part_o + (size_t)rh.num_rows * splits * H * kDv);
   }
-  const int R = rh.num_rows, HG = H / kHeadsPerBlock;
-  const unsigned grid = 8u * (unsigned)((R + 7) / 8) * HG * splits;
+  const int R = rh.num_rows;
+  const unsigned grid = 8u * (unsigned)((R + 7) / 8) * splits;
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
   const uint8_t *kv8 = static_cast<const uint8_t *>(kv);
   uint16_t *o16 = static_cast<uint16_t *>(out);

@@ -113,8 +113,11 @@ def test_mla_validation(lib):
     assert _mla(lib, r8, Dv=600) == INVALID                         # d_v > d_qk
     assert _mla(lib, r8, scale=float("nan")) == INVALID
     assert _mla(lib, r8, scale=float("inf")) == INVALID
+    assert _mla(lib, r8, scale=0.0) == INVALID
+    assert _mla(lib, r8, scale=-0.07) == INVALID
     assert _mla(lib, r8, ptrs=False) == INVALID
     assert _mla(lib, r8, H=96) == UNSUPPORTED
+    assert _mla(lib, r8, H=64) == UNSUPPORTED
     assert _mla(lib, r8, Dqk=512) == UNSUPPORTED
     assert _mla(lib, r8, dtype=2) == UNSUPPORTED                    # no fp8 attention
     assert _mla(lib, r8, dtype=0, H=129, Dqk=80, Dv=64) == UNSUPPORTED
