@@ -119,15 +119,21 @@ hipError_t launch_mla_f32(const RowsHost &rh, bool paged, int H, int Dqk, int Dv
 // ------------------------------------------------------------------------------------
 // bf16 MFMA path, d_qk = 576 (512 latent + 64 RoPE), d_v = 512.
 // ------------------------------------------------------------------------------------
+#ifndef DSA_MLA_QK_PREFETCH
+#define DSA_MLA_QK_PREFETCH 2
+#endif
+#ifndef DSA_MLA_PV_PREFETCH
+#define DSA_MLA_PV_PREFETCH 3
+#endif
 #ifndef DSA_MLA_DEPTH
-#define DSA_MLA_DEPTH 3
+#define DSA_MLA_DEPTH 4
 #endif
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;          // 1152 B per cache entry
 constexpr int kTile = 32;                    // entries per LDS tile
 constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB = 36 DMA instructions of 1 KB
-constexpr int kMlaWaves = 8;                 // 4 head quarters x 2 halves
+constexpr int kMlaWaves = 8;                 // 16 heads each
 constexpr int kMlaThreads = kMlaWaves * kWave;
 constexpr int kHeadsPerBlock = 128;
 constexpr int kRing = DSA_MLA_DEPTH;          // LDS tile slots (kRing - 1 tiles in flight)
@@ -135,13 +141,14 @@ constexpr int kMaxSlotsPerSplit = 2048;
 constexpr int kSlotRounds = kMaxSlotsPerSplit / kMlaThreads;   // 4
 static_assert(kTileBytes % 1024 == 0, "tile DMA is whole 1 KB instructions");
 
-// XOR swizzle of the 16-byte chunk index inside its aligned group of 8 chunks, from row
-// bits 4, 1 and 3.  The 16 rows 8a + b (a, b < 4) read together by one score-operand
-// load, and the 8 rows 8g + i (g of one lane pair, i < 4) of one transposing value load,
-// then hit disjoint LDS banks (rows are 288 dwords apart, so odd rows start half a bank
-// sweep later).  Bit 2 is unused: rows r and r + 4 share the swizzle.
+// XOR swizzle of the 16-byte chunk index inside its aligned group of 8 chunks: bit 0 =
+// row bit 0 ^ row bit 3, bit 1 = row bit 1 ^ row bit 3, bit 2 = row bit 1.  Picked by
+// measuring LDS read throughput on gfx950 over all swizzles built from row bits {0,1,3,4}:
+// with it the score-operand loads (16 rows 8a + b, a 16-byte chunk each) run at the rate
+// of contiguous loads, and the transposing value loads at the best rate found.  Row bit 2
+// is unused: rows r and r + 4 share the swizzle.
 __device__ __forceinline__ int swz(int row) {
-  return ((row >> 4) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
+  return ((row ^ (row >> 3)) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1) | (((row >> 1) & 1) << 2);
 }
 
 typedef bf16x4 __attribute__((address_space(3))) *lds_bf16x4_ptr;
@@ -152,7 +159,6 @@ constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0
 struct MlaShared {
   uint8_t tiles[kRing][kTileBytes];
   uint32_t crow[kMaxSlotsPerSplit];        // cache rows of the split's valid slots, compacted
-  f32x4 xs[kMlaWaves][4][kWave];           // partial score tiles traded between wave pairs
   uint32_t wcount[kMlaWaves];
 };
 
@@ -193,29 +199,34 @@ struct TileDma {
     }
   }
 };
+// The DMA instructions of one tile, prepared ahead: source addresses resolved from the
+// tile's cache rows, issued one at a time where they do not stall the wave.
+// Instruction i of a wave's tile loads reads, in each lane, tile entry entry(i) starting at
+// byte offset byte(i) of the entry (both from the packed per-lane constants).
+__device__ __forceinline__ uint32_t dma_field(const TileDma &td, int i) {
+  // opaque copy: keeps the compiler from hoisting 64-bit addresses out of the tile loop
+  uint32_t p = td.pk[i >> 1];
+  __asm__ volatile("" : "+v"(p));
+  return (p >> (16 * (i & 1))) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t dma_row(const uint32_t *crow_tile, const TileDma &td, int i) {
+  return crow_tile[dma_field(td, i) & 31u];
+}
+__device__ __forceinline__ void dma_issue(int i, uint32_t cache_row, uint8_t *dst,
+                                          const uint8_t *__restrict__ kv, const TileDma &td,
+                                          int n_dma, int wave) {
+  if (i < kDmaMax - 1 || n_dma == kDmaMax)
+    dma16(kv + (uint64_t)cache_row * kRowBytes + (dma_field(td, i) >> 5),
+          dst + 1024 * (wave + kMlaWaves * i));
+}
 __device__ __forceinline__ void issue_tile(uint8_t *dst, const uint32_t *crow_tile,
                                           const uint8_t *__restrict__ kv, const TileDma &td,
                                           int n_dma, int wave) {
-  // opaque copies: keeps the compiler from hoisting per-instruction 64-bit addresses out
-  // of the tile loop (they would not fit in registers)
-  uint32_t p[(kDmaMax + 1) / 2];
+  uint32_t cr[kDmaMax];
 #pragma unroll
-  for (int w = 0; w < (kDmaMax + 1) / 2; ++w) {
-    p[w] = td.pk[w];
-    __asm__ volatile("" : "+v"(p[w]));
-  }
-  uint32_t cr[kDmaMax], byte[kDmaMax];
+  for (int i = 0; i < kDmaMax; ++i) cr[i] = dma_row(crow_tile, td, i);
 #pragma unroll
-  for (int i = 0; i < kDmaMax; ++i) {
-    const uint32_t f = (p[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    cr[i] = crow_tile[f & 31u];
-    byte[i] = f >> 5;
-  }
-#pragma unroll
-  for (int i = 0; i < kDmaMax; ++i) {
-    if (i < kDmaMax - 1 || n_dma == kDmaMax)
-      dma16(kv + (uint64_t)cr[i] * kRowBytes + byte[i], dst + 1024 * (wave + kMlaWaves * i));
-  }
+  for (int i = 0; i < kDmaMax; ++i) dma_issue(i, cr[i], dst, kv, td, n_dma, wave);
 }
 
 // Waits until at most `younger` tiles of N loads each (issued after the awaited one) are
@@ -239,16 +250,12 @@ __device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
 }
 
 // One workgroup: all 128 heads of query row r over one split of its top-k slots.
-// Wave (hq, vh) = (wave % 4, wave / 4) owns heads 32hq .. 32hq+31 and half vh of both
-// contractions: the even (vh = 0) or odd (vh = 1) 32-dim steps of the 576-dim scores,
-// and value dims [256 vh, 256 vh + 256).  Per tile of 32 entries it forms its partial
-// S^T = C . Q^T (entries as MFMA rows, 2 x 2 blocks of 16 entries x 16 heads, q in
-// registers), trades it with its partner wave (hq, 1 - vh) through LDS, so both hold the
-// full scores and take identical softmax decisions, then accumulates
-// O^T += V^T . P^T over its value half, V^T read from the same LDS tile with the
-// transposing LDS read.  Entry rows of the score blocks are permuted (block kb, row
-// 4g + i <-> entry 8g + 4kb + i) so that each lane's weights are exactly the B operand
-// of the value product: no exchange of weights is needed.
+// Wave w owns heads 16w .. 16w+15 over the full contractions.  Per tile of 32 entries it
+// forms S^T = C . Q^T (entries as MFMA rows, 2 blocks of 16 entries x its 16 heads, q in
+// registers), runs the online softmax, and accumulates O^T += V^T . P^T over all 512
+// value dims, V^T read from the same LDS tile with the transposing LDS read.  Entry rows
+// of the score blocks are permuted (block kb, row 4g + i <-> entry 8g + 4kb + i) so that
+// each lane's weights are exactly the B operand of the value product.
 template <bool PAGED>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     RowsDev rows, int R, int H, float scale_log2, const uint16_t *__restrict__ q,
@@ -262,25 +269,20 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int r = co.r, split = co.split;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hq = wave & 3, vh = wave >> 2;
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r], b = rows.row_seq[r];
-  const int h0 = hq * 32;
+  const int h0 = wave * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
   const int32_t *idx_row = idx + (int64_t)r * k + slot_begin;
 
-  // q^T operands: head h0 + 16hb + c, dims 64t + 32vh + 8g .. +8 (in flight during the
-  // slot resolution below)
-  bf16x8 qf[2][9];
+  // q^T operand: head h0 + c, dims 32t + 8g .. +8 (in flight during the slot resolution)
+  bf16x8 qf[18];
   {
+    const bf16x8 *qp =
+        reinterpret_cast<const bf16x8 *>(q + ((int64_t)r * H + h0 + c) * kDqk + 8 * g);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-          q + ((int64_t)r * H + h0 + 16 * hb + c) * kDqk + 32 * vh + 8 * g);
-#pragma unroll
-      for (int t = 0; t < 9; ++t) qf[hb][t] = qp[8 * t];
-    }
+    for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
   }
   // cache rows of the valid slots, compacted in slot order
   int n_valid = 0;
@@ -320,12 +322,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   if (threadIdx.x < n_tiles * kTile - n_valid) sh.crow[n_valid + threadIdx.x] = sh.crow[0];
   lds_barrier();
 
-  f32x4 oacc[2][16];
+  f32x4 oacc[32];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int nb = 0; nb < 16; ++nb) oacc[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  for (int nb = 0; nb < 32; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
 
   const int n_dma = tile_dma_count(wave);
   TileDma td;
@@ -334,20 +334,17 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   for (int d = 0; d < kRing - 1 && d < n_tiles; ++d)
     issue_tile(sh.tiles[d], sh.crow + d * kTile, kv, td, n_dma, wave);
 
-  // score operand rows: block kb, lane row c <-> entry 8(c>>2) + (c&3) + 4kb; both rows of a
-  // lane share one swizzle, and its dims 64t + 32vh + 8g are chunk 8t + 4vh + g
+  // score operand rows: block kb, lane row c <-> entry 8(c>>2) + (c&3) + 4kb (both share a
+  // swizzle); dims 32t + 8g are chunk 4t + g: group t/2, in-group 4(t&1) + g
   const int arow = 8 * (c >> 2) + (c & 3);
-  const int a_off = arow * kRowBytes + 16 * ((4 * vh + g) ^ swz(arow));
-  // value operand: transposing reads of entries 8g + tr_i (+4), dims 256vh + 16nb + 4tr_q
-  // (chunk 2m + (tr_q >> 1)) ^ swz = 2 (m ^ (swz >> 1)) + ((tr_q >> 1) ^ (swz & 1)); entries
-  // 8g + tr_i and 8g + tr_i + 4 share the swizzle, so the second is an immediate offset
+  const int a_even = arow * kRowBytes + 16 * (g ^ swz(arow));
+  const int a_odd = arow * kRowBytes + 16 * ((4 + g) ^ swz(arow));
+  // value operand: transposing reads of entries 8g + tr_i (+4), dims 16nb + 4tr_q;
+  // (chunk 2m + (tr_q >> 1)) ^ swz = 2 (m ^ (swz >> 1)) + ((tr_q >> 1) ^ (swz & 1))
   const int tr_i = c >> 2, tr_q = c & 3;
   const int swa = swz(8 * g + tr_i);
   const int ua = swa >> 1;
-  const int v_off_a = (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1) + 512 * vh +
-                      16 * ((tr_q >> 1) ^ (swa & 1));
-  f32x4 *xs_mine = sh.xs[wave][0] + lane;
-  const f32x4 *xs_peer = sh.xs[wave ^ 4][0] + lane;
+  const int v_off = (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1) + 16 * ((tr_q >> 1) ^ (swa & 1));
 
   uint32_t slot_use = 0, slot_issue = (kRing - 1) * kTileBytes;   // byte offsets in the ring
   for (int it = 0; it < n_tiles; ++it) {
@@ -363,128 +360,124 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     // ring slots advance by one tile and wrap (uniform, loop-carried: no division)
     slot_use = slot_use + kTileBytes == kRing * kTileBytes ? 0u : slot_use + kTileBytes;
     slot_issue = slot_issue + kTileBytes == kRing * kTileBytes ? 0u : slot_issue + kTileBytes;
-    // ---- partial scores over this wave's 9 dim steps
-    f32x4 sc[2][2];
+    // ---- scores: 18 steps of 32 dims, two independent 16-entry blocks; the operand loads
+    // run kPf steps ahead of the products that use them
+    f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kPf = DSA_MLA_QK_PREFETCH;
+    bf16x8 xr[kPf][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) sc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 9; ++t) {
-      const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(tile + a_off + 128 * t);
-      const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(tile + a_off + 4 * kRowBytes + 128 * t);
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        sc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[hb][t], sc[0][hb], 0, 0, 0);
-        sc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[hb][t], sc[1][hb], 0, 0, 0);
-      }
+    for (int t = 0; t < kPf; ++t) {
+      const uint8_t *ap = tile + ((t & 1) ? a_odd : a_even) + 128 * (t >> 1);
+      xr[t][0] = *reinterpret_cast<const bf16x8 *>(ap);
+      xr[t][1] = *reinterpret_cast<const bf16x8 *>(ap + 4 * kRowBytes);
     }
-    // ---- trade partial scores with the partner wave; both then hold identical sums
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xs_mine[kWave * j] = sc[j >> 1][j & 1];
-    lds_barrier();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j >> 1][j & 1] += xs_peer[kWave * j];
+    for (int t = 0; t < 18; ++t) {
+      const bf16x8 x0 = xr[t % kPf][0], x1 = xr[t % kPf][1];
+      if (t + kPf < 18) {
+        const int tn = t + kPf;
+        const uint8_t *ap = tile + ((tn & 1) ? a_odd : a_even) + 128 * (tn >> 1);
+        xr[t % kPf][0] = *reinterpret_cast<const bf16x8 *>(ap);
+        xr[t % kPf][1] = *reinterpret_cast<const bf16x8 *>(ap + 4 * kRowBytes);
+      }
+      // keep the scheduler from sinking the loads next to their use
+      __builtin_amdgcn_sched_barrier(0);
+      sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[t], sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[t], sc1, 0, 0, 0);
+    }
     // only the last tile can hold padding entries: their scores become -inf
     const int nv = n_valid - it * kTile;
     if (nv < kTile) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (8 * g + 4 * kb + i >= nv) {
-            sc[kb][0][i] = -INFINITY;
-            sc[kb][1][i] = -INFINITY;
-          }
-    }
-    bf16x8 pf[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      // tile maximum of head h0 + 16hb + c in the scaled log2 domain (scale > 0, finite:
-      // the tile has a valid entry)
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][hb][0], sc[0][hb][1]), fmaxf(sc[0][hb][2], sc[0][hb][3])),
-                       fmaxf(fmaxf(sc[1][hb][0], sc[1][hb][1]), fmaxf(sc[1][hb][2], sc[1][hb][3])));
-      mx = max_xor32(max_xor16(mx)) * scale_log2;
-      // lazy online softmax (log2 domain): the reference maximum only moves when the tile
-      // maximum exceeds it by more than 8, so weights stay <= 2^8 and rescales are rare
-      const bool first = m_run[hb] == -INFINITY;
-      const bool move = first || mx > m_run[hb] + 8.f;
-      if (__ballot(move && !first)) {
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_run[hb] - mx) : 1.f;
-#pragma unroll
-        for (int nb = 0; nb < 16; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[hb][nb][i] *= alpha;
-        l_part[hb] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        if (8 * g + i >= nv) sc0[i] = -INFINITY;
+        if (8 * g + 4 + i >= nv) sc1[i] = -INFINITY;
       }
-      if (move) m_run[hb] = mx;
-      const float neg_m = -m_run[hb];
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 2][hb][e & 3], scale_log2, neg_m));
-        l_part[hb] += p[e];
-      }
-      pf[hb] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
     }
-    // ---- O^T += V^T . P^T over this wave's value half: value rows 256vh + 16nb + c
+    // tile maximum of head h0 + c in the scaled log2 domain (scale > 0; finite: the tile
+    // has a valid entry)
+    float mx = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
+                     fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
+    mx = max_xor32(max_xor16(mx)) * scale_log2;
+    // lazy online softmax (log2 domain): the reference maximum only moves when the tile
+    // maximum exceeds it by more than 8, so weights stay <= 2^8 and rescales are rare
+    const bool first = m_run == -INFINITY;
+    const bool move = first || mx > m_run + 8.f;
+    if (__ballot(move && !first)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
+      l_part *= alpha;
+    }
+    if (move) m_run = mx;
+    const float neg_m = -m_run;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sc0[i], scale_log2, neg_m));
+      p[4 + i] = __builtin_amdgcn_exp2f(fmaf(sc1[i], scale_log2, neg_m));
+    }
+    l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+    // ---- O^T += V^T . P^T: value rows 16nb + c
     const uint8_t *va[4];   // per-lane bases; the 128-byte group and the +4 entries are immediates
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) va[m4] = tile + v_off_a + 32 * (m4 ^ ua);
-#pragma unroll
-    for (int nb = 0; nb < 16; ++nb) {
+    for (int m4 = 0; m4 < 4; ++m4) va[m4] = tile + v_off + 32 * (m4 ^ ua);
+    constexpr int kPv = DSA_MLA_PV_PREFETCH;
+    bf16x8 vr[kPv];
+    auto load_v = [&](int nb) {
       const int hi = 128 * (nb >> 2);
       const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(va[nb & 3] + hi));
       const bf16x4 v1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(va[nb & 3] + 4 * kRowBytes + hi));
-      const bf16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        oacc[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pf[hb], oacc[hb][nb], 0, 0, 0);
+    for (int nb = 0; nb < kPv; ++nb) vr[nb] = load_v(nb);
+#pragma unroll
+    for (int nb = 0; nb < 32; ++nb) {
+      const bf16x8 vb = vr[nb % kPv];
+      if (nb + kPv < 32) vr[nb % kPv] = load_v(nb + kPv);
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pf, oacc[nb], 0, 0, 0);
     }
   }
   // every wave is done with the ring before it is reused for staging (no load is in flight:
   // the last iteration waited for all of them)
   lds_barrier();
 
-  // ---- epilogue.  Lane (g, c) holds head h0 + 16hb + c, dims 256vh + 16nb + 4g + i.  Each
-  // head block is staged in LDS (16 heads x 256 dims per wave) and written with 16-byte
-  // stores.
-  constexpr int kStageRow = 256 * 2 + 16;   // bytes per staged head row (padded)
+  // ---- epilogue.  Lane (g, c) holds head h0 + c, dims 16nb + 4g + i.  The wave stages its
+  // 16 x 512 block in LDS (the ring is free now) and writes it with 16-byte stores.
+  constexpr int kStageRow = kDv * 2 + 16;   // bytes per staged head row (padded)
   uint8_t *stage = sh.tiles[0] + wave * 16 * kStageRow;
+  const float l_tot = sum_xor32(sum_xor16(l_part));
+  const float linv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const float l_tot = sum_xor32(sum_xor16(l_part[hb]));
-    const float linv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse2 = l_tot > 0.f ? m_run[hb] + log2f(l_tot) : -INFINITY;
+  for (int nb = 0; nb < 32; ++nb) {
+    const uint32_t lo = pack_bf16x2(oacc[nb][0] * linv, oacc[nb][1] * linv);
+    const uint32_t hi = pack_bf16x2(oacc[nb][2] * linv, oacc[nb][3] * linv);
+    *reinterpret_cast<uint2 *>(stage + c * kStageRow + (16 * nb + 4 * g) * 2) = make_uint2(lo, hi);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+  uint16_t *dst;
+  if (splits == 1) {
+    dst = out + ((int64_t)r * H + h0) * kDv;
+    if (lse && g == 0) lse[(int64_t)r * H + h0 + c] = lse2 * kLn2;
+  } else {
+    const int64_t ph0 = ((int64_t)r * splits + split) * H + h0;
+    dst = part_o + ph0 * kDv;
+    if (g == 0) part_lse[ph0 + c] = lse2;
+  }
+  // row j of the staged block = head h0 + j: 1024 bytes = 64 lanes x 16 B
 #pragma unroll
-    for (int nb = 0; nb < 16; ++nb) {
-      const uint32_t lo = pack_bf16x2(oacc[hb][nb][0] * linv, oacc[hb][nb][1] * linv);
-      const uint32_t hi = pack_bf16x2(oacc[hb][nb][2] * linv, oacc[hb][nb][3] * linv);
-      *reinterpret_cast<uint2 *>(stage + c * kStageRow + (16 * nb + 4 * g) * 2) = make_uint2(lo, hi);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    const int hh = h0 + 16 * hb;
-    uint16_t *dst;
-    if (splits == 1) {
-      dst = out + ((int64_t)r * H + hh) * kDv + 256 * vh;
-      if (lse && g == 0 && vh == 0) lse[(int64_t)r * H + hh + c] = lse2 * kLn2;
-    } else {
-      const int64_t ph0 = ((int64_t)r * splits + split) * H + hh;
-      dst = part_o + ph0 * kDv + 256 * vh;
-      if (g == 0 && vh == 0) part_lse[ph0 + c] = lse2;
-    }
-    // row j of the staged block = head hh + j: 512 bytes = 32 lanes x 16 B; two rows per store
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const int row = j + (lane >> 5), col = lane & 31;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + row * kStageRow + col * 16);
-      *reinterpret_cast<i32x4 *>(dst + (int64_t)row * kDv + col * 8) = v;
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // staging reads done before the next block's writes
-    __builtin_amdgcn_wave_barrier();
+  for (int j = 0; j < 16; ++j) {
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + j * kStageRow + lane * 16);
+    *reinterpret_cast<i32x4 *>(dst + (int64_t)j * kDv + lane * 8) = v;
   }
 }
 

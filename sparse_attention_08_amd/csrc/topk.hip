@@ -320,13 +320,28 @@ __global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(const float *__re
   if (threadIdx.x == 0) ws.hcnt[(size_t)r * ws.C + c] = total;
 }
 
-// (2) merge the row's histograms, find b*, keep this chunk's survivors in position order
+// Chunk j of the flattened list whose exclusive prefix offsets are off[0..nc] (off[nc] =
+// total): the last j with off[j] <= e.  Binary search over LDS.
+__device__ __forceinline__ int chunk_of(const uint32_t *off, int nc, uint32_t e) {
+  int lo = 0, hi = nc - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= e) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// (2) merge the row's histograms, find b*, keep this chunk's survivors in position order.
+// Every global load is independent of the others: the chunk's scores are requested first,
+// then all chunk counts, then all histogram entries of the row at once.
 __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__restrict__ logits,
                                                                  int64_t ld,
                                                                  const int32_t *__restrict__ row_len,
                                                                  int k, int32_t *__restrict__ idx,
                                                                  MbWs ws) {
   __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t off[kMaxChunks + 1];
   __shared__ uint32_t wtot[kMbThreads / kWave];
   __shared__ uint32_t wcnt[kMbThreads / kWave];
   __shared__ uint32_t s_bstar, s_above;
@@ -340,16 +355,54 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
   if (base >= n) return;
   const int nblk = (n + kChunk - 1) / kChunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // this chunk's scores (wave w owns 1024 consecutive positions)
+  const float *row = logits + (int64_t)r * ld;
+  constexpr int kPerWave = kChunk / (kMbThreads / kWave);   // 1024 scores per wave
+  constexpr int kIter = kPerWave / 64;
+  const int wlo = base + wave * kPerWave;
+  float sv[kIter];
+#pragma unroll
+  for (int j = 0; j < kIter; ++j) {
+    const int i = wlo + 64 * j + lane;
+    sv[j] = i < n ? row[i] : 0.f;
+  }
+  // counts of every chunk histogram of the row (nblk <= kMaxChunks = kMbThreads)
+  const uint32_t cnt = threadIdx.x < nblk ? ws.hcnt[(size_t)r * ws.C + threadIdx.x] : 0u;
   for (int i = threadIdx.x; i < kBins; i += kMbThreads) lh[i] = 0;
-  // chunk j's entries go to a wave picked round-robin; every load is independent
-  __syncthreads();
-  for (int j = wave; j < nblk; j += kMbThreads / kWave) {
-    const uint32_t nzj = ws.hcnt[(size_t)r * ws.C + j];
-    const uint32_t *src = ws.hlist + ((size_t)r * ws.C + j) * kBins;
-    for (uint32_t t = lane; t < nzj; t += kWave) {
-      const uint32_t e = src[t];
-      atomicAdd(&lh[e >> 16], e & 0xFFFFu);
+  {
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += u;
     }
+    if (lane == 63) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t before = inc - cnt, total = 0;
+    for (int w = 0; w < kMbThreads / kWave; ++w) {
+      before += (w < wave) ? wtot[w] : 0u;
+      total += wtot[w];
+    }
+    if (threadIdx.x < nblk) off[threadIdx.x] = before;
+    if (threadIdx.x == 0) off[nblk] = total;
+  }
+  __syncthreads();
+  // all histogram entries of the row, 8 independent loads per thread per round
+  const uint32_t E = off[nblk];
+  for (uint32_t e0 = 0; e0 < E; e0 += 8 * kMbThreads) {
+    uint32_t ent[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = e0 + j * kMbThreads + threadIdx.x;
+      ent[j] = 0;
+      if (e < E) {
+        const int ch = chunk_of(off, nblk, e);
+        ent[j] = ws.hlist[((size_t)r * ws.C + ch) * kBins + (e - off[ch])];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (ent[j]) atomicAdd(&lh[ent[j] >> 16], ent[j] & 0xFFFFu);
   }
   __syncthreads();
   // digit b* holding the k-th largest: thread t owns bins 4095-16t-j (descending)
@@ -366,6 +419,7 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     const uint32_t u = __shfl_up(inc, o, kWave);
     if (lane >= o) inc += u;
   }
+  __syncthreads();   // wtot reuse
   if (lane == 63) wtot[wave] = inc;
   __syncthreads();
   uint32_t before = inc - tot;
@@ -389,24 +443,20 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     ws.meta[2 * r + 1] = s_above;
   }
   // survivors of this chunk (digit >= b*), in position order
-  const float *row = logits + (int64_t)r * ld;
-  constexpr int kPerWave = kChunk / (kMbThreads / kWave);   // 1024 scores per wave
-  constexpr int kIter = kPerWave / 64;
   uint32_t keys[kIter];
   uint32_t wc = 0;
-  const int wlo = base + wave * kPerWave;
 #pragma unroll
   for (int j = 0; j < kIter; ++j) {
     const int i = wlo + 64 * j + lane;
-    keys[j] = i < n ? order_key(row[i]) : 0u;
+    keys[j] = order_key(sv[j]);
     wc += __popcll(__ballot(i < n && (keys[j] >> (32 - kD0Bits)) >= bstar));
   }
   if (lane == 0) wcnt[wave] = wc;
   __syncthreads();
-  uint32_t off = 0, total = 0;
+  uint32_t soff = 0, stotal = 0;
   for (int w = 0; w < kMbThreads / kWave; ++w) {
-    off += (w < wave) ? wcnt[w] : 0u;
-    total += wcnt[w];
+    soff += (w < wave) ? wcnt[w] : 0u;
+    stotal += wcnt[w];
   }
   uint2 *lst = ws.slist + ((size_t)r * ws.C + c) * kChunk;
   const uint64_t lt = lanemask_lt();
@@ -415,13 +465,14 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     const int i = wlo + 64 * j + lane;
     const bool keep = i < n && (keys[j] >> (32 - kD0Bits)) >= bstar;
     const uint64_t m = __ballot(keep);
-    if (keep) lst[off + __popcll(m & lt)] = make_uint2(keys[j], (uint32_t)i);
-    off += __popcll(m);
+    if (keep) lst[soff + __popcll(m & lt)] = make_uint2(keys[j], (uint32_t)i);
+    soff += __popcll(m);
   }
-  if (threadIdx.x == 0) ws.scnt[(size_t)r * ws.C + c] = total;
+  if (threadIdx.x == 0) ws.scnt[(size_t)r * ws.C + c] = stotal;
 }
 
-// (3) one workgroup per row: exact select among the survivors
+// (3) one workgroup per row: exact select among the survivors, gathered with independent
+// loads (chunk of each survivor found from the prefix of the per-chunk counts)
 __global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *__restrict__ logits,
                                                                    int64_t ld,
                                                                    const int32_t *__restrict__ row_len,
@@ -436,6 +487,8 @@ __global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *
   if (n <= k) return;
   int32_t *out = idx + (int64_t)r * k;
   const int nblk = (n + kChunk - 1) / kChunk;
+  const int bstar = (int)ws.meta[2 * r];
+  const int above = (int)ws.meta[2 * r + 1];
   {
     // exclusive prefix of the per-chunk survivor counts (nblk <= kMaxChunks <= kSmallThreads)
     const uint32_t cnt = threadIdx.x < nblk ? ws.scnt[(size_t)r * ws.C + threadIdx.x] : 0u;
@@ -446,16 +499,23 @@ __global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *
   }
   __syncthreads();
   const int M = (int)coff[nblk];
-  const int bstar = (int)ws.meta[2 * r];
-  const int above = (int)ws.meta[2 * r + 1];
   if (M <= kSurvivorCap) {
-    for (int j = threadIdx.x / kWave; j < nblk; j += kSmallThreads / kWave) {
-      const uint2 *src = ws.slist + ((size_t)r * ws.C + j) * kChunk;
-      const int cj = (int)(coff[j + 1] - coff[j]);
-      for (int t = threadIdx.x % kWave; t < cj; t += kWave) {
-        const uint2 v = src[t];
-        skey[coff[j] + t] = v.x;
-        spos[coff[j] + t] = (int32_t)v.y;
+    constexpr int kRounds = (kSurvivorCap + kSmallThreads - 1) / kSmallThreads;   // 10
+    uint2 v[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int e = j * kSmallThreads + threadIdx.x;
+      if (e < M) {
+        const int ch = chunk_of(coff, nblk, (uint32_t)e);
+        v[j] = ws.slist[((size_t)r * ws.C + ch) * kChunk + (e - (int)coff[ch])];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int e = j * kSmallThreads + threadIdx.x;
+      if (e < M) {
+        skey[e] = v[j].x;
+        spos[e] = (int32_t)v[j].y;
       }
     }
     __syncthreads();
