@@ -101,24 +101,29 @@ __device__ __forceinline__ int key_swz(int key) {
   if constexpr (FP8) return ((key >> 1) & 7) ^ ((key & 1) << 2);
   return key & 15;
 }
+// Launch shape (measured on MI355X): 8 waves of 4 KB key groups, 3-deep LDS rings, grid
+// sized for about 256 workgroups.
 #ifndef DSA_IDX_DEPTH
-#define DSA_IDX_DEPTH 4
+#define DSA_IDX_DEPTH 3
 #endif
 #ifndef DSA_IDX_WAVES
-#define DSA_IDX_WAVES 4
+#define DSA_IDX_WAVES 8
 #endif
 #ifndef DSA_IDX_BLOCKS
-#define DSA_IDX_BLOCKS 512
+#define DSA_IDX_BLOCKS 256
 #endif
-constexpr int kGroupBytes = 8192;
+#ifndef DSA_IDX_GROUP_BYTES
+#define DSA_IDX_GROUP_BYTES 4096
+#endif
+constexpr int kGroupBytes = DSA_IDX_GROUP_BYTES;   // keys streamed per wave per step
 constexpr int kDepth = DSA_IDX_DEPTH;       // LDS slots per wave (kDepth-1 groups in flight)
 constexpr int kIdxWaves = DSA_IDX_WAVES;
 
 template <bool FP8>
 struct IdxCfg {
   static constexpr int kRowBytes = kIdxDim * (FP8 ? 1 : 2);   // 128 / 256
-  static constexpr int kKeys = kGroupBytes / kRowBytes;        // 64 / 32 keys per group
-  static constexpr int kTiles = kKeys / 16;                    // 4 / 2 MFMA tiles
+  static constexpr int kKeys = kGroupBytes / kRowBytes;        // keys per group (fp8: 32 at 4 KB)
+  static constexpr int kTiles = kKeys / 16;                    // 16-key MFMA tiles per group
   static constexpr int kChunks = kRowBytes / 64;               // 16-byte chunks per lane per key
   static constexpr int kSlotBytes = kGroupBytes + (FP8 ? 256 : 0);   // keys (+ 64 scales)
 };
@@ -156,30 +161,23 @@ struct DmaLane {
   }
 };
 
-// Issues the loads of the group starting at key s0 into `slot` (clamped into the span,
-// so a look-ahead past its end re-reads keys that are already in cache).  base_row:
-// contiguous layout, cache row of position 0; paged layout: lane i of page_lane holds
-// the page of position 64*(p0 + i).  A group never crosses a 64-token page.
+// Issues the loads of the key group starting at position s0 (< row length) into `slot`.
+// base_row: contiguous layout, cache row of position 0; paged layout: page holds the cache
+// page of the group (a group never crosses a 64-token page).  Keys past s_last (the row's
+// last position) re-read s_last, which stays in cache.
 template <bool FP8, bool PAGED>
 __device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__restrict__ k,
                                             const float *__restrict__ k_scale, int64_t base_row,
-                                            int page_lane, int64_t p0, int64_t s0, int64_t s_last,
+                                            int page, int64_t s0, int64_t s_last,
                                             const DmaLane<FP8> &dl, int lane) {
   using C = IdxCfg<FP8>;
-  s0 = min<int64_t>(s0, s_last & ~(int64_t)(C::kKeys - 1));
-  int64_t row0;
-  if constexpr (PAGED) {
-    const int page = __builtin_amdgcn_readlane(page_lane, (int)((s0 >> 6) - p0));
-    row0 = (int64_t)page * kPage + (s0 & 63);
-  } else {
-    row0 = base_row + s0;
-  }
+  const int64_t row0 = PAGED ? (int64_t)page * kPage + (s0 & 63) : base_row + s0;
   const uint8_t *gbase = k + row0 * C::kRowBytes;
-  const int last = (int)(s_last - s0);   // last valid key offset inside the group
-  if (last >= C::kKeys - 1) {            // the whole group lies inside the span
+  const int last = (int)min<int64_t>(s_last - s0, C::kKeys - 1);   // last valid key offset
+  if (last == C::kKeys - 1) {            // the whole group lies inside the row
 #pragma unroll
     for (int j = 0; j < DmaLane<FP8>::kJ; ++j) dma16(gbase + dl.byte[j], slot + 1024 * j);
-    if constexpr (FP8) dma4(k_scale + row0 + lane, slot + kGroupBytes);
+    if constexpr (FP8) dma4(k_scale + row0 + min(lane, C::kKeys - 1), slot + kGroupBytes);
   } else {
 #pragma unroll
     for (int j = 0; j < DmaLane<FP8>::kJ; ++j)
@@ -239,7 +237,7 @@ template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
     RowsDev rows, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, const float *__restrict__ w,
-    float *__restrict__ logits, int64_t ld, int keys_per_wave) {
+    float *__restrict__ logits, int64_t ld) {
   using C = IdxCfg<FP8>;
   constexpr int kQChunks = kIdxHeads * C::kRowBytes / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t idx_smem[];
@@ -250,33 +248,39 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r];
-  const int64_t blk_begin = (int64_t)blockIdx.x * kIdxWaves * keys_per_wave;
-  if (blk_begin >= len) return;
-  const int64_t s_begin = blk_begin + (int64_t)wave * keys_per_wave;
-  const bool active = s_begin < len;
-  const int64_t s_end = min<int64_t>(s_begin + keys_per_wave, len);
-  const int64_t s_last = s_end - 1;
+  // The row's key groups are dealt to its waves round-robin (wave wr of WR takes groups wr,
+  // wr + WR, ...), so at any time the row's waves stream one contiguous window of it.
+  const int n_row_groups = (len + C::kKeys - 1) / C::kKeys;
+  const int waves_per_row = gridDim.x * kIdxWaves;
+  const int wr = blockIdx.x * kIdxWaves + wave;
+  if (blockIdx.x * kIdxWaves >= n_row_groups) return;
+  const bool active = wr < n_row_groups;
+  const int n_groups = active ? (n_row_groups - wr + waves_per_row - 1) / waves_per_row : 0;
+  const int64_t s_last = len - 1;
   const int b = rows.row_seq[r];
   uint8_t *ring = smem + kQChunks * 16 + wave * kDepth * C::kSlotBytes;
   int64_t base_row = 0;
-  int page_lane = 0;
-  const int64_t p0 = s_begin >> 6;
+  int page_lane = 0;   // paged layout: lane j holds the page of the wave's j-th group
   DmaLane<FP8> dl;
   // loads per group: kGroupBytes/1024 key instructions (+1 scale instruction for fp8)
   constexpr int kLoads = kGroupBytes / 1024 + (FP8 ? 1 : 0);
+  auto group_start = [&](int j) { return (int64_t)(wr + j * waves_per_row) * C::kKeys; };
+  auto group_page = [&](int j) {
+    return PAGED ? __builtin_amdgcn_readlane(page_lane, j) : 0;
+  };
   if (active) {
     if constexpr (PAGED) {
-      const int64_t np = ((s_last >> 6) - p0) + 1;   // pages this span touches (<= 64)
-      if (lane < np) page_lane = rows.page_table[(int64_t)b * rows.max_pages + p0 + lane];
+      if (lane < n_groups)
+        page_lane = rows.page_table[(int64_t)b * rows.max_pages + (group_start(lane) >> 6)];
     } else {
       base_row = rows.seq_start[b];
     }
     // the first kDepth-1 key groups start streaming before the query block is loaded
     dl.init(lane);
-    const int n_pro = (int)min<int64_t>(kDepth - 1, (s_last - s_begin) / C::kKeys + 1);
+    const int n_pro = min(kDepth - 1, n_groups);
     for (int d = 0; d < n_pro; ++d)
-      issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, page_lane, p0,
-                              s_begin + (int64_t)d * C::kKeys, s_last, dl, lane);
+      issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, group_page(d),
+                              group_start(d), s_last, dl, lane);
   }
   {
     const i32x4 *qg = reinterpret_cast<const i32x4 *>(q + (int64_t)r * kIdxHeads * C::kRowBytes);
@@ -302,21 +306,20 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
       wt[hb][i] = FP8 ? w[hj] * q_scale[hj] : w[hj];
     }
   float *out = logits + (int64_t)r * ld;
-  const int n_groups = (int)((s_end - s_begin + C::kKeys - 1) / C::kKeys);
   for (int i = 0; i < n_groups; ++i) {
     if (i + kDepth - 1 < n_groups) {
       issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
-                              base_row, page_lane, p0, s_begin + (int64_t)(i + kDepth - 1) * C::kKeys,
+                              base_row, group_page(i + kDepth - 1), group_start(i + kDepth - 1),
                               s_last, dl, lane);
       // group i is older than the kDepth-1 groups issued after it: loads complete in order
       __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
     } else {
-      // tail: nothing is issued past the span, so wait for every load still in flight
+      // tail: nothing is issued past the wave's groups, so wait for every load in flight
       __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     }
     const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);
-    const int64_t s = s_begin + (int64_t)i * C::kKeys + lane;
-    if (lane < C::kKeys && s < s_end) out[s] = v;
+    const int64_t s = group_start(i) + lane;
+    if (lane < C::kKeys && s < len) out[s] = v;
   }
 }
 
@@ -328,8 +331,7 @@ size_t indexer_lds_bytes(bool fp8) {
 template <bool FP8, bool PAGED>
 static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const RowsDev &rows,
                              const uint8_t *q8, const float *q_scale, const uint8_t *k8,
-                             const float *k_scale, const float *w, float *logits, int64_t ld,
-                             int kpw) {
+                             const float *k_scale, const float *w, float *logits, int64_t ld) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&indexer_mfma_kernel<FP8, PAGED>),
@@ -338,7 +340,7 @@ static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const Ro
     attr_set = true;
   }
   indexer_mfma_kernel<FP8, PAGED><<<grid, kIdxWaves * kWave, shm, stream>>>(
-      rows, q8, q_scale, k8, k_scale, w, logits, ld, kpw);
+      rows, q8, q_scale, k8, k_scale, w, logits, ld);
   return hipGetLastError();
 }
 
@@ -353,17 +355,19 @@ hipError_t launch_indexer_mfma(const RowsHost &rh, bool paged, bool fp8, const v
   int64_t kpw = (total + kIdxWaves * kBlocksTarget - 1) / (kIdxWaves * kBlocksTarget);
   kpw = ((kpw + 63) / 64) * 64;
   if (kpw < 64) kpw = 64;
-  if (kpw > 4096) kpw = 4096;   // a span touches at most 64 pages (one per lane)
+  // at most 64 groups per wave (one page id per lane)
+  const int64_t max_kpw = 64 * (fp8 ? IdxCfg<true>::kKeys : IdxCfg<false>::kKeys);
+  if (kpw > max_kpw) kpw = max_kpw;
   const int64_t per_block = kIdxWaves * kpw;
   dim3 grid((unsigned)((rh.max_row_len + per_block - 1) / per_block), rh.num_rows);
   const size_t shm = indexer_lds_bytes(fp8);
   const uint8_t *q8 = static_cast<const uint8_t *>(q);
   const uint8_t *k8 = static_cast<const uint8_t *>(k);
   if (fp8)
-    return paged ? launch_one<true, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw)
-                 : launch_one<true, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw);
-  return paged ? launch_one<false, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw)
-               : launch_one<false, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, (int)kpw);
+    return paged ? launch_one<true, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld)
+                 : launch_one<true, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld);
+  return paged ? launch_one<false, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld)
+               : launch_one<false, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld);
 }
 
 }  // namespace dsa
