@@ -271,32 +271,40 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int len = rows.row_len[r], b = rows.row_seq[r];
+  // contiguous layout: the sequence's first cache row, fetched before anything else (it is
+  // a second dependent load on the way to the first tile)
+  const int64_t seq_base = PAGED ? 0 : rows.seq_start[b];
   const int h0 = wave * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
   const int32_t *idx_row = idx + (int64_t)r * k + slot_begin;
 
-  // q^T operand: head h0 + c, dims 32t + 8g .. +8 (in flight during the slot resolution)
-  bf16x8 qf[18];
-  {
-    const bf16x8 *qp =
-        reinterpret_cast<const bf16x8 *>(q + ((int64_t)r * H + h0 + c) * kDqk + 8 * g);
-#pragma unroll
-    for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
-  }
   // cache rows of the valid slots, compacted in slot order
   int n_valid = 0;
+  bf16x8 qf[18];
   {
+    // the slot loads go out before the query loads: waits on vector memory are in issue
+    // order, so resolving the slots does not wait for the query block
     int sv[kSlotRounds];
 #pragma unroll
     for (int j = 0; j < kSlotRounds; ++j) {
       const int t = j * kMlaThreads + threadIdx.x;
       sv[j] = t < n_slots ? idx_row[t] : -1;
     }
+    // q^T operand: head h0 + c, dims 32t + 8g .. +8 (in flight during the slot resolution
+    // and the first tile loads)
+    {
+      const bf16x8 *qp =
+          reinterpret_cast<const bf16x8 *>(q + ((int64_t)r * H + h0 + c) * kDqk + 8 * g);
+#pragma unroll
+      for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
+    }
     int64_t crow_v[kSlotRounds];
 #pragma unroll
     for (int j = 0; j < kSlotRounds; ++j)
-      crow_v[j] = (sv[j] >= 0 && sv[j] < len) ? cache_row<PAGED>(rows, b, sv[j]) : -1;
+      crow_v[j] = (sv[j] >= 0 && sv[j] < len)
+                      ? (PAGED ? cache_row<PAGED>(rows, b, sv[j]) : seq_base + sv[j])
+                      : -1;
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int j = 0; j < kSlotRounds; ++j) {
@@ -540,7 +548,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int R, int H, int spli
 }
 
 #ifndef DSA_MLA_MIN_TILES
-#define DSA_MLA_MIN_TILES 2
+#define DSA_MLA_MIN_TILES 4
 #endif
 int mla_num_splits(int num_rows, int n_heads, int k) {
   // about one workgroup per CU for few-row batches, at least DSA_MLA_MIN_TILES tiles each
