@@ -7,9 +7,11 @@ scales, top-2048, bf16 latent cache 576/512, 128 heads.
 
 Timing: inputs are resident in HBM; before every timed step a 1 GiB read evicts L2 and
 the Infinity Cache (outside the timed region), then HIP events on the launch stream
-bracket the step.  The timed step is the three stages captured once in a HIP graph and
-replayed (--no-graph: eager launches); an eager pass with events between the stages
-gives the per-stage attribution.  value = rows (tokens) / mean step time.
+bracket the step.  The timed step is one fused indexer + top-k call and the sparse MLA
+call, captured once in a HIP graph and replayed (--no-graph: eager launches; --separate:
+the indexer and the top-k as two calls); an eager pass with events between separate stage
+calls gives the per-stage attribution and the indexer's roofline.  value = rows (tokens) /
+mean step time.
 
 Prints ONE JSON line.  --config selects another of the five workloads for diagnostics.
 """
@@ -53,6 +55,9 @@ def parse():
                    help="only copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches only (default: the step is captured in a HIP graph)")
+    p.add_argument("--separate", action="store_true",
+                   help="timed step calls the indexer and the top-k separately (default: one "
+                        "fused indexer + top-k call)")
     p.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
                    help="no GPU work: 'trace NAME STATS_CSV CMD' writes profiles/NAME.md from a "
                         "rocprofv3 --kernel-trace --stats run; 'pmc KERNEL FETCH_CSV WRITE_CSV "
@@ -239,6 +244,13 @@ def main():
     def stage_indexer():
         idx_fn(rows, wl.q_idx, wl.w, wl.k_idx, logits, q_scale=wl.q_scale, k_scale=wl.k_scale)
 
+    fused_ws_n = dsa.indexer_topk_workspace_size(R, wl.max_row_len, wl.q_idx.dtype, wl.topk)
+    fused_ws = torch.empty(max(fused_ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def stage_indexer_topk():
+        dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, idx=idx,
+                         q_scale=wl.q_scale, k_scale=wl.k_scale, ws=fused_ws)
+
     def stage_topk():
         dsa.topk(logits, wl.row_len, wl.topk, wl.max_row_len, idx=idx, ws=tk_ws)
 
@@ -256,12 +268,17 @@ def main():
     flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
         stage_indexer(); stage_topk(); stage_mla()
+        stage_indexer_topk(); stage_mla()
     torch.cuda.synchronize()
 
     def step():
-        stage_indexer(); stage_topk(); stage_mla()
+        if args.separate:
+            stage_indexer(); stage_topk()
+        else:
+            stage_indexer_topk()
+        stage_mla()
 
-    # eager launches, with per-stage attribution
+    # eager launches, with per-stage attribution (indexer, top-k and MLA as separate calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -354,6 +371,7 @@ def main():
                  "hbm_frac_of_step": (idx_b + mla_b) / (mean * 1e-3) / (HBM_PEAK_GBS * 1e9),
                  "algorithmic_flops_per_step": idx_f + mla_f,
                  "launch_mode": mode,
+                 "indexer_topk": "separate calls" if args.separate else "fused call",
                  "eager_ms_per_step": statistics.fmean(eager_ms),
                  "stage_ms": {"indexer": idx_mean, "topk": statistics.fmean(topk_ms),
                               "sparse_mla": statistics.fmean(mla_ms)},

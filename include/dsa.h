@@ -128,6 +128,28 @@ int dsa_topk(const float *logits, int64_t ld_logits, const int32_t *row_len, int
              int max_row_len, int k, int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Stages 1 and 2 in one call: exactly the logits of dsa_indexer_logits(_paged) and the
+ * indices of dsa_topk on them, for the same arguments.  For batches of few long rows (the
+ * decode shape) the indexer workgroups also count their scores by the leading radix digit
+ * of the selection as they produce them, so the selection starts from those counts instead
+ * of a separate pass over the scores.
+ * topk: k of dsa_topk;  idx [R, topk] int32 output as dsa_topk.
+ * ws / ws_bytes: device scratch of at least dsa_indexer_topk_workspace_size(R,
+ * max_row_len, dtype, topk) bytes (may be NULL when that is 0); needs no initialisation;
+ * calls that share one workspace must not run concurrently.
+ * Errors: those of dsa_indexer_logits and of dsa_topk. */
+size_t dsa_indexer_topk_workspace_size(int num_rows, int max_row_len, int dtype, int k);
+int dsa_indexer_topk(const dsa_rows *rows, int dtype, int n_heads, int head_dim,
+                     const void *q, const float *q_scale, const void *k, const float *k_scale,
+                     const float *w, float *logits, int64_t ld_logits, int topk, int32_t *idx,
+                     void *ws, size_t ws_bytes, void *stream);
+int dsa_indexer_topk_paged(const dsa_rows *rows, int dtype, int n_heads, int head_dim,
+                           const void *q, const float *q_scale, const void *k,
+                           const float *k_scale, const float *w, float *logits,
+                           int64_t ld_logits, int topk, int32_t *idx, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Stage 3: MLA in MQA mode over the selected entries ("DeepSeek-V3.2 技术报告摘要",
  * section 1, MLA-based implementation; "Model techniques map", "Multi-head latent
  * attention", "Learnable attention sink", "Gated attention output").

@@ -59,6 +59,12 @@ def load_library() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]
         f.restype = i32
+    for name in ("dsa_indexer_topk", "dsa_indexer_topk_paged"):
+        f = getattr(lib, name)
+        f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i32, vp, vp, sz, vp]
+        f.restype = i32
+    lib.dsa_indexer_topk_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dsa_indexer_topk_workspace_size.restype = sz
     lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
     lib.dsa_topk_workspace_size.restype = sz
     lib.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -202,6 +208,44 @@ def topk(logits, row_len, k: int, max_row_len: int, idx=None, ws=None):
     s = lib.dsa_topk(_ptr(logits), int(logits.shape[-1]), _ptr(row_len), R, int(max_row_len), int(k),
                      _ptr(idx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check(s, "dsa_topk")
+    return idx
+
+
+# --------------------------------------------------------------------------- stages 1 + 2
+
+def indexer_topk_workspace_size(num_rows: int, max_row_len: int, dtype, k: int) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(torch.empty(0, dtype=dtype))
+    return int(load_library().dsa_indexer_topk_workspace_size(int(num_rows), int(max_row_len), code,
+                                                              int(k)))
+
+
+def indexer_topk(rows: Rows, q, w, k, logits, topk_k: int, idx=None, q_scale=None, k_scale=None,
+                 ws=None):
+    """Indexer scores into ``logits`` and their top-k positions into ``idx`` in one call."""
+    lib = load_library()
+    _dev(q, "q")
+    _dev(k, "k")
+    _dev(w, "w", (torch.float32,))
+    _dev(logits, "logits", (torch.float32,))
+    if q_scale is not None:
+        _dev(q_scale, "q_scale", (torch.float32,))
+    if k_scale is not None:
+        _dev(k_scale, "k_scale", (torch.float32,))
+    if q.dim() != 3:
+        raise ValueError("q must be [R, H, D]")
+    R = rows.num_rows
+    if idx is None:
+        idx = torch.empty((R, topk_k), dtype=torch.int32, device=logits.device)
+    _dev(idx, "idx", (torch.int32,))
+    need = indexer_topk_workspace_size(R, rows.max_row_len, dtype_code(q), topk_k)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    st = rows.struct()
+    fn = lib.dsa_indexer_topk_paged if rows.paged else lib.dsa_indexer_topk
+    s = fn(ctypes.byref(st), dtype_code(q), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(q_scale),
+           _ptr(k), _ptr(k_scale), _ptr(w), _ptr(logits), int(logits.shape[-1]), int(topk_k), _ptr(idx),
+           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check(s, "dsa_indexer_topk_paged" if rows.paged else "dsa_indexer_topk")
     return idx
 
 

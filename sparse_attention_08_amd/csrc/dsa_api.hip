@@ -32,9 +32,10 @@ RowsHost to_host(const dsa_rows *rows) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
-int indexer_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
-                   const void *q, const float *q_scale, const void *k, const float *k_scale,
-                   const float *w, float *logits, int64_t ld_logits, void *stream) {
+// Host-side checks of an indexer call; DSA_OK means the call may proceed (or is empty).
+int indexer_check(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
+                  const void *q, const float *q_scale, const void *k, const float *k_scale,
+                  const float *w, float *logits, int64_t ld_logits) {
   if (!rows_ok(rows, paged)) return DSA_ERR_INVALID_ARG;
   if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
   if (n_heads <= 0 || head_dim <= 0) return DSA_ERR_INVALID_ARG;
@@ -43,18 +44,76 @@ int indexer_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int
   if (ld_logits < rows->max_row_len) return DSA_ERR_INVALID_ARG;
   const bool fp8 = dtype == DSA_FP8_E4M3;
   if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr)) return DSA_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const RowsHost rh = to_host(rows);
   if (dtype == DSA_F32) {
     if (n_heads > 64 || head_dim > 256) return DSA_ERR_UNSUPPORTED;
-    return status_of(dsa::launch_indexer_f32(rh, paged, n_heads, head_dim,
-                                             static_cast<const float *>(q),
-                                             static_cast<const float *>(k), w, logits, ld_logits,
-                                             s));
+  } else if (n_heads != 64 || head_dim != 128) {
+    return DSA_ERR_UNSUPPORTED;
   }
-  if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
-  return status_of(dsa::launch_indexer_mfma(rh, paged, fp8, q, q_scale, k, k_scale, w, logits,
-                                            ld_logits, s));
+  return DSA_OK;
+}
+
+hipError_t indexer_launch(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
+                          const void *q, const float *q_scale, const void *k, const float *k_scale,
+                          const float *w, float *logits, int64_t ld_logits, hipStream_t s) {
+  const RowsHost rh = to_host(rows);
+  if (dtype == DSA_F32)
+    return dsa::launch_indexer_f32(rh, paged, n_heads, head_dim, static_cast<const float *>(q),
+                                   static_cast<const float *>(k), w, logits, ld_logits, s);
+  return dsa::launch_indexer_mfma(rh, paged, dtype == DSA_FP8_E4M3, q, q_scale, k, k_scale, w,
+                                  logits, ld_logits, s);
+}
+
+int indexer_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
+                   const void *q, const float *q_scale, const void *k, const float *k_scale,
+                   const float *w, float *logits, int64_t ld_logits, void *stream) {
+  const int st = indexer_check(rows, paged, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
+                               logits, ld_logits);
+  if (st != DSA_OK || rows->num_rows == 0) return st;
+  return status_of(indexer_launch(rows, paged, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
+                                  logits, ld_logits, static_cast<hipStream_t>(stream)));
+}
+
+// Histogram lists per row when the indexer workgroups feed the top-k directly, or 0 when the
+// batch takes the separate path (f32 indexer, or the one-workgroup-per-row top-k schedule).
+int fused_hist_lists(int num_rows, int max_row_len, int dtype) {
+  if (dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return 0;
+  const int nh = dsa::indexer_blocks_per_row(num_rows, max_row_len, dtype == DSA_FP8_E4M3);
+  return dsa::topk_hist_fusable(num_rows, max_row_len, nh) ? nh : 0;
+}
+
+size_t indexer_topk_ws(int num_rows, int max_row_len, int dtype, int k) {
+  const int nh = fused_hist_lists(num_rows, max_row_len, dtype);
+  return nh ? dsa::topk_fused_workspace_bytes(num_rows, max_row_len, nh)
+            : dsa::topk_workspace_bytes(num_rows, max_row_len, k);
+}
+
+int indexer_topk_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
+                        const void *q, const float *q_scale, const void *k, const float *k_scale,
+                        const float *w, float *logits, int64_t ld_logits, int topk, int32_t *idx,
+                        void *ws, size_t ws_bytes, void *stream) {
+  const int st = indexer_check(rows, paged, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
+                               logits, ld_logits);
+  if (st != DSA_OK) return st;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_INVALID_ARG;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!idx) return DSA_ERR_INVALID_ARG;
+  const size_t need = indexer_topk_ws(rows->num_rows, rows->max_row_len, dtype, topk);
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int R = rows->num_rows, L = rows->max_row_len;
+  const int nh = fused_hist_lists(R, L, dtype);
+  if (nh) {
+    const dsa::TopkHistDest dest = dsa::topk_hist_dest(ws, R, L, nh);
+    hipError_t e = dsa::launch_indexer_mfma_hist(to_host(rows), paged, dtype == DSA_FP8_E4M3, q,
+                                                 q_scale, k, k_scale, w, logits, ld_logits, dest, s);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    return status_of(dsa::launch_topk_after_hist(logits, ld_logits, rows->row_len, R, L, topk, idx,
+                                                 ws, nh, s));
+  }
+  hipError_t e = indexer_launch(rows, paged, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
+                                logits, ld_logits, s);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  return status_of(dsa::launch_topk(logits, ld_logits, rows->row_len, R, L, topk, idx, ws, s));
 }
 
 enum class MlaMode { kDecode, kPrefill };
@@ -120,6 +179,28 @@ int dsa_indexer_logits_paged(const dsa_rows *rows, int dtype, int n_heads, int h
                              int64_t ld_logits, void *stream) {
   return indexer_common(rows, true, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w, logits,
                         ld_logits, stream);
+}
+
+size_t dsa_indexer_topk_workspace_size(int num_rows, int max_row_len, int dtype, int k) {
+  if (num_rows < 0 || max_row_len < 1 || k < 1 || k > DSA_MAX_TOPK) return 0;
+  if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return 0;
+  return indexer_topk_ws(num_rows, max_row_len, dtype, k);
+}
+
+int dsa_indexer_topk(const dsa_rows *rows, int dtype, int n_heads, int head_dim, const void *q,
+                     const float *q_scale, const void *k, const float *k_scale, const float *w,
+                     float *logits, int64_t ld_logits, int topk, int32_t *idx, void *ws,
+                     size_t ws_bytes, void *stream) {
+  return indexer_topk_common(rows, false, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
+                             logits, ld_logits, topk, idx, ws, ws_bytes, stream);
+}
+
+int dsa_indexer_topk_paged(const dsa_rows *rows, int dtype, int n_heads, int head_dim,
+                           const void *q, const float *q_scale, const void *k,
+                           const float *k_scale, const float *w, float *logits, int64_t ld_logits,
+                           int topk, int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
+  return indexer_topk_common(rows, true, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
+                             logits, ld_logits, topk, idx, ws, ws_bytes, stream);
 }
 
 size_t dsa_topk_workspace_size(int num_rows, int max_row_len, int k) {

@@ -53,6 +53,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// Leading radix digit of the top-k select: sign, exponent and 3 mantissa bits of the key.
+constexpr int kLeadDigitBits = 12;
+constexpr int kLeadBins = 1 << kLeadDigitBits;
+
 // Order-preserving map of a finite float to uint32 (larger float -> larger key),
 // with -0 folded onto +0 so the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -27,9 +27,33 @@ hipError_t launch_indexer_f32(const RowsHost &rows, bool paged, int H, int D, co
 hipError_t launch_indexer_mfma(const RowsHost &rows, bool paged, bool fp8, const void *q,
                                const float *q_scale, const void *k, const float *k_scale,
                                const float *w, float *logits, int64_t ld, hipStream_t stream);
+// Workgroups per row of the MFMA indexer grid for this batch shape.
+int indexer_blocks_per_row(int num_rows, int max_row_len, bool fp8);
+// Same, also depositing each workgroup's leading-digit histogram of its scores (the
+// first stage of the few-row top-k), indexer_blocks_per_row lists per row.
+struct TopkHistDest;
+hipError_t launch_indexer_mfma_hist(const RowsHost &rows, bool paged, bool fp8, const void *q,
+                                    const float *q_scale, const void *k, const float *k_scale,
+                                    const float *w, float *logits, int64_t ld,
+                                    const TopkHistDest &hist, hipStream_t stream);
 
 // ---- top-k ----
+// Where a producer of scores deposits per-workgroup compressed histograms of the 12-bit
+// leading digit of the order keys (list j of row r: count at hcnt[r*stride + j], entries
+// (digit << 16 | count) at hlist[(r*stride + j) * 4096 ...]).
+struct TopkHistDest {
+  uint32_t *hcnt;
+  uint32_t *hlist;
+  int stride;
+};
 size_t topk_workspace_bytes(int num_rows, int max_row_len, int k);
+// few long rows whose leading-digit histograms come from the score producer
+bool topk_hist_fusable(int num_rows, int max_row_len, int hist_lists);
+size_t topk_fused_workspace_bytes(int num_rows, int max_row_len, int hist_lists);
+TopkHistDest topk_hist_dest(void *ws, int num_rows, int max_row_len, int hist_lists);
+hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                  int num_rows, int max_row_len, int k, int32_t *idx, void *ws,
+                                  int hist_lists, hipStream_t stream);
 hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,
                        int max_row_len, int k, int32_t *idx, void *ws, hipStream_t stream);
 

@@ -134,12 +134,23 @@ typedef void __attribute__((address_space(3))) *lds_void_ptr;
 // leaves the export and LDS/scalar counters unconstrained (gfx9 field layout).
 constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// Keys are streamed once: the loads carry the non-temporal cache hint (aux bit 1).
+// Global->LDS loads of 16 (keys) and 4 (fp8 scales) bytes per lane: lane l lands at
+// lds + l * size.  Keys are streamed once, so the key loads carry the non-temporal hint.
+// Written as two-instruction asm statements rather than the builtin: the compiler treats
+// every LDS write it cannot disambiguate from a pending global->LDS load as aliasing it
+// and would wait for all of them first (draining the rings).  The instructions write no
+// register and consume their operands at issue; the kernel waits for the data with
+// explicit vmcnt counts (loads complete in order) before reading a slot.
+__device__ __forceinline__ uint32_t lds_addr(const void *lds) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+}
 __device__ __forceinline__ void dma16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 16, 0, 2);
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds_addr(lds))
+                   : "memory");
 }
 __device__ __forceinline__ void dma4(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 4, 0, 0);
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
+                   : "memory");
 }
 
 // Per-lane constant part of a group's DMA addresses: for key instruction j, the key of the
@@ -233,16 +244,23 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
   return mine;
 }
 
-template <bool FP8, bool PAGED>
+// HIST: also count the scores of the workgroup by the 12-bit leading digit of their order
+// keys (the first stage of the few-row top-k) and deposit the nonzero bins, compressed, as
+// list blockIdx.x of row r.
+template <bool FP8, bool PAGED, bool HIST>
 __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
     RowsDev rows, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, const float *__restrict__ w,
-    float *__restrict__ logits, int64_t ld) {
+    float *__restrict__ logits, int64_t ld, uint32_t *__restrict__ hcnt,
+    uint32_t *__restrict__ hlist, int hstride) {
   using C = IdxCfg<FP8>;
   constexpr int kQChunks = kIdxHeads * C::kRowBytes / 16;
+  constexpr int kThreads = kIdxWaves * kWave;
   extern __shared__ __attribute__((aligned(16))) uint8_t idx_smem[];
+  __shared__ uint32_t wtot[kIdxWaves];
   uint8_t *smem = idx_smem;
   i32x4 *q_lds = reinterpret_cast<i32x4 *>(smem);
+  uint32_t *hist = reinterpret_cast<uint32_t *>(smem + kQChunks * 16 + kIdxWaves * kDepth * C::kSlotBytes);
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -253,7 +271,10 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   const int n_row_groups = (len + C::kKeys - 1) / C::kKeys;
   const int waves_per_row = gridDim.x * kIdxWaves;
   const int wr = blockIdx.x * kIdxWaves + wave;
-  if (blockIdx.x * kIdxWaves >= n_row_groups) return;
+  if (blockIdx.x * kIdxWaves >= n_row_groups) {
+    if (HIST && threadIdx.x == 0) hcnt[(size_t)r * hstride + blockIdx.x] = 0;
+    return;
+  }
   const bool active = wr < n_row_groups;
   const int n_groups = active ? (n_row_groups - wr + waves_per_row - 1) / waves_per_row : 0;
   const int64_t s_last = len - 1;
@@ -282,92 +303,154 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
       issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, group_page(d),
                               group_start(d), s_last, dl, lane);
   }
+  if constexpr (HIST)
+    for (int i = threadIdx.x; i < kLeadBins; i += kThreads) hist[i] = 0;
   {
     const i32x4 *qg = reinterpret_cast<const i32x4 *>(q + (int64_t)r * kIdxHeads * C::kRowBytes);
-    for (int i = threadIdx.x; i < kQChunks; i += kIdxWaves * kWave) q_lds[i] = qg[i];
+    for (int i = threadIdx.x; i < kQChunks; i += kThreads) q_lds[i] = qg[i];
   }
   __syncthreads();
-  if (!active) return;
 
-  // q operand of head 16*hb + c, dims [32g, 32g+32) (fp8) / [64g, 64g+64) (bf16)
-  i32x4 qf[4][C::kChunks];
+  if (active) {
+    // q operand of head 16*hb + c, dims [32g, 32g+32) (fp8) / [64g, 64g+64) (bf16)
+    i32x4 qf[4][C::kChunks];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-    for (int i = 0; i < C::kChunks; ++i)
-      qf[hb][i] = q_lds[(hb * 16 + c) * (C::kRowBytes / 16) + g * C::kChunks + i];
-  // head weights of the result rows this lane holds: heads 16*hb + 4g + i
-  float wt[4][4];
+      for (int i = 0; i < C::kChunks; ++i)
+        qf[hb][i] = q_lds[(hb * 16 + c) * (C::kRowBytes / 16) + g * C::kChunks + i];
+    // head weights of the result rows this lane holds: heads 16*hb + 4g + i
+    float wt[4][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t hj = (int64_t)r * kIdxHeads + hb * 16 + 4 * g + i;
-      wt[hb][i] = FP8 ? w[hj] * q_scale[hj] : w[hj];
+      for (int i = 0; i < 4; ++i) {
+        const int64_t hj = (int64_t)r * kIdxHeads + hb * 16 + 4 * g + i;
+        wt[hb][i] = FP8 ? w[hj] * q_scale[hj] : w[hj];
+      }
+    float *out = logits + (int64_t)r * ld;
+    for (int i = 0; i < n_groups; ++i) {
+      if (i + kDepth - 1 < n_groups) {
+        issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
+                                base_row, group_page(i + kDepth - 1), group_start(i + kDepth - 1),
+                                s_last, dl, lane);
+        // group i is older than the kDepth-1 groups issued after it: loads complete in order
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
+      } else {
+        // tail: nothing is issued past the wave's groups, so wait for every load in flight
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      }
+      const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);
+      const int64_t s = group_start(i) + lane;
+      if (lane < C::kKeys && s < len) {
+        out[s] = v;
+        if constexpr (HIST) atomicAdd(&hist[order_key(v) >> (32 - kLeadDigitBits)], 1u);
+      }
     }
-  float *out = logits + (int64_t)r * ld;
-  for (int i = 0; i < n_groups; ++i) {
-    if (i + kDepth - 1 < n_groups) {
-      issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
-                              base_row, group_page(i + kDepth - 1), group_start(i + kDepth - 1),
-                              s_last, dl, lane);
-      // group i is older than the kDepth-1 groups issued after it: loads complete in order
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
-    } else {
-      // tail: nothing is issued past the wave's groups, so wait for every load in flight
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  }
+
+  if constexpr (HIST) {
+    __syncthreads();   // every wave's counts are in (waves without groups come straight here)
+    // ordered compaction of the nonzero bins: thread t owns bins PER*t .. PER*t+PER-1
+    constexpr int PER = kLeadBins / kThreads;
+    uint32_t nz = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) nz += hist[PER * threadIdx.x + j] ? 1u : 0u;
+    uint32_t inc = nz;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += u;
     }
-    const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);
-    const int64_t s = group_start(i) + lane;
-    if (lane < C::kKeys && s < len) out[s] = v;
+    if (lane == 63) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t off = inc - nz, total = 0;
+    for (int wv = 0; wv < kIdxWaves; ++wv) {
+      off += (wv < wave) ? wtot[wv] : 0u;
+      total += wtot[wv];
+    }
+    uint32_t *dst = hlist + ((size_t)r * hstride + blockIdx.x) * kLeadBins;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t bin = PER * threadIdx.x + j, cnt = hist[bin];
+      if (cnt) dst[off++] = (bin << 16) | cnt;
+    }
+    if (threadIdx.x == 0) hcnt[(size_t)r * hstride + blockIdx.x] = total;
   }
 }
 
-size_t indexer_lds_bytes(bool fp8) {
-  return fp8 ? (size_t)kIdxHeads * IdxCfg<true>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<true>::kSlotBytes
-             : (size_t)kIdxHeads * IdxCfg<false>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<false>::kSlotBytes;
+size_t indexer_lds_bytes(bool fp8, bool hist) {
+  const size_t base = fp8 ? (size_t)kIdxHeads * IdxCfg<true>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<true>::kSlotBytes
+                          : (size_t)kIdxHeads * IdxCfg<false>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<false>::kSlotBytes;
+  return base + (hist ? sizeof(uint32_t) * kLeadBins : 0);
 }
 
-template <bool FP8, bool PAGED>
+template <bool FP8, bool PAGED, bool HIST>
 static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const RowsDev &rows,
                              const uint8_t *q8, const float *q_scale, const uint8_t *k8,
-                             const float *k_scale, const float *w, float *logits, int64_t ld) {
+                             const float *k_scale, const float *w, float *logits, int64_t ld,
+                             uint32_t *hcnt, uint32_t *hlist, int hstride) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&indexer_mfma_kernel<FP8, PAGED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&indexer_mfma_kernel<FP8, PAGED, HIST>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  indexer_mfma_kernel<FP8, PAGED><<<grid, kIdxWaves * kWave, shm, stream>>>(
-      rows, q8, q_scale, k8, k_scale, w, logits, ld);
+  indexer_mfma_kernel<FP8, PAGED, HIST><<<grid, kIdxWaves * kWave, shm, stream>>>(
+      rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
   return hipGetLastError();
 }
 
-hipError_t launch_indexer_mfma(const RowsHost &rh, bool paged, bool fp8, const void *q,
-                               const float *q_scale, const void *k, const float *k_scale,
-                               const float *w, float *logits, int64_t ld, hipStream_t stream) {
-  RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
-  // One workgroup per CU at a time (the LDS rings fill most of the CU's 160 KB); size the
-  // spans for about two rounds of 256 workgroups; spans are whole 64-key multiples.
-  const int64_t total = (int64_t)rh.num_rows * rh.max_row_len;
+// One workgroup per CU at a time (the LDS rings fill most of the CU's 160 KB); the keys per
+// wave are sized for about DSA_IDX_BLOCKS workgroups in all, whole 64-key multiples.
+static int64_t keys_per_wave(int num_rows, int max_row_len, bool fp8) {
+  const int64_t total = (int64_t)num_rows * max_row_len;
   constexpr int64_t kBlocksTarget = DSA_IDX_BLOCKS;
   int64_t kpw = (total + kIdxWaves * kBlocksTarget - 1) / (kIdxWaves * kBlocksTarget);
   kpw = ((kpw + 63) / 64) * 64;
   if (kpw < 64) kpw = 64;
   // at most 64 groups per wave (one page id per lane)
   const int64_t max_kpw = 64 * (fp8 ? IdxCfg<true>::kKeys : IdxCfg<false>::kKeys);
-  if (kpw > max_kpw) kpw = max_kpw;
-  const int64_t per_block = kIdxWaves * kpw;
-  dim3 grid((unsigned)((rh.max_row_len + per_block - 1) / per_block), rh.num_rows);
-  const size_t shm = indexer_lds_bytes(fp8);
+  return kpw > max_kpw ? max_kpw : kpw;
+}
+
+int indexer_blocks_per_row(int num_rows, int max_row_len, bool fp8) {
+  const int64_t per_block = kIdxWaves * keys_per_wave(num_rows, max_row_len, fp8);
+  return (int)((max_row_len + per_block - 1) / per_block);
+}
+
+template <bool HIST>
+static hipError_t launch_indexer(const RowsHost &rh, bool paged, bool fp8, const void *q,
+                                 const float *q_scale, const void *k, const float *k_scale,
+                                 const float *w, float *logits, int64_t ld, uint32_t *hcnt,
+                                 uint32_t *hlist, int hstride, hipStream_t stream) {
+  RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
+  dim3 grid((unsigned)indexer_blocks_per_row(rh.num_rows, rh.max_row_len, fp8), rh.num_rows);
+  const size_t shm = indexer_lds_bytes(fp8, HIST);
   const uint8_t *q8 = static_cast<const uint8_t *>(q);
   const uint8_t *k8 = static_cast<const uint8_t *>(k);
   if (fp8)
-    return paged ? launch_one<true, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld)
-                 : launch_one<true, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld);
-  return paged ? launch_one<false, true>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld)
-               : launch_one<false, false>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld);
+    return paged ? launch_one<true, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride)
+                 : launch_one<true, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
+  return paged ? launch_one<false, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride)
+               : launch_one<false, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
+}
+
+hipError_t launch_indexer_mfma(const RowsHost &rh, bool paged, bool fp8, const void *q,
+                               const float *q_scale, const void *k, const float *k_scale,
+                               const float *w, float *logits, int64_t ld, hipStream_t stream) {
+  return launch_indexer<false>(rh, paged, fp8, q, q_scale, k, k_scale, w, logits, ld, nullptr,
+                               nullptr, 0, stream);
+}
+
+hipError_t launch_indexer_mfma_hist(const RowsHost &rh, bool paged, bool fp8, const void *q,
+                                    const float *q_scale, const void *k, const float *k_scale,
+                                    const float *w, float *logits, int64_t ld,
+                                    const TopkHistDest &hist, hipStream_t stream) {
+  return launch_indexer<true>(rh, paged, fp8, q, q_scale, k, k_scale, w, logits, ld, hist.hcnt,
+                              hist.hlist, hist.stride, stream);
 }
 
 }  // namespace dsa

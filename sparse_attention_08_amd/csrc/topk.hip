@@ -25,7 +25,7 @@
 
 namespace dsa {
 
-constexpr int kD0Bits = 12, kD1Bits = 10, kD2Bits = 10;
+constexpr int kD0Bits = kLeadDigitBits, kD1Bits = 10, kD2Bits = 10;
 constexpr int kBins = 1 << kD0Bits;        // 4096
 constexpr int kChunk = 4096;               // scores per workgroup in the few-row schedule
 constexpr int kSmallThreads = 1024;
@@ -235,7 +235,8 @@ struct MbWs {
   uint32_t *meta;     // [R][2]          b*, number of scores with digit > b*
   uint32_t *scnt;     // [R][C]          survivors per chunk
   uint2 *slist;       // [R][C][kChunk]  (key, position) survivors per chunk
-  int C;
+  int C;              // chunk stride of the arrays above
+  int nh;             // histogram lists per row; 0: one per 4096-score chunk of the row
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -259,6 +260,7 @@ __host__ __device__ inline MbWs carve_ws(void *ws, int R, int C) {
   p += align256(sizeof(uint32_t) * (size_t)R * 2);
   w.slist = reinterpret_cast<uint2 *>(p);
   w.C = C;
+  w.nh = 0;
   return w;
 }
 
@@ -366,8 +368,9 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     const int i = wlo + 64 * j + lane;
     sv[j] = i < n ? row[i] : 0.f;
   }
-  // counts of every chunk histogram of the row (nblk <= kMaxChunks = kMbThreads)
-  const uint32_t cnt = threadIdx.x < nblk ? ws.hcnt[(size_t)r * ws.C + threadIdx.x] : 0u;
+  // counts of every histogram list of the row (nh <= kMaxChunks = kMbThreads)
+  const int nh = ws.nh ? ws.nh : nblk;
+  const uint32_t cnt = threadIdx.x < nh ? ws.hcnt[(size_t)r * ws.C + threadIdx.x] : 0u;
   for (int i = threadIdx.x; i < kBins; i += kMbThreads) lh[i] = 0;
   {
     uint32_t inc = cnt;
@@ -383,12 +386,12 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
       before += (w < wave) ? wtot[w] : 0u;
       total += wtot[w];
     }
-    if (threadIdx.x < nblk) off[threadIdx.x] = before;
-    if (threadIdx.x == 0) off[nblk] = total;
+    if (threadIdx.x < nh) off[threadIdx.x] = before;
+    if (threadIdx.x == 0) off[nh] = total;
   }
   __syncthreads();
   // all histogram entries of the row, 8 independent loads per thread per round
-  const uint32_t E = off[nblk];
+  const uint32_t E = off[nh];
   for (uint32_t e0 = 0; e0 < E; e0 += 8 * kMbThreads) {
     uint32_t ent[8];
 #pragma unroll
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
       const uint32_t e = e0 + j * kMbThreads + threadIdx.x;
       ent[j] = 0;
       if (e < E) {
-        const int ch = chunk_of(off, nblk, e);
+        const int ch = chunk_of(off, nh, e);
         ent[j] = ws.hlist[((size_t)r * ws.C + ch) * kBins + (e - off[ch])];
       }
     }
@@ -538,6 +541,33 @@ size_t topk_workspace_bytes(int num_rows, int max_row_len, int) {
   if (!few_rows(num_rows, max_row_len)) return 0;
   const int C = (max_row_len + kChunk - 1) / kChunk;
   return mb_ws_bytes(num_rows, C);
+}
+
+bool topk_hist_fusable(int num_rows, int max_row_len, int hist_lists) {
+  return few_rows(num_rows, max_row_len) && hist_lists >= 1 && hist_lists <= kMaxChunks;
+}
+
+size_t topk_fused_workspace_bytes(int num_rows, int max_row_len, int hist_lists) {
+  const int C = (max_row_len + kChunk - 1) / kChunk;
+  return mb_ws_bytes(num_rows, C > hist_lists ? C : hist_lists);
+}
+
+TopkHistDest topk_hist_dest(void *ws, int num_rows, int max_row_len, int hist_lists) {
+  const int C = (max_row_len + kChunk - 1) / kChunk;
+  const MbWs w = carve_ws(ws, num_rows, C > hist_lists ? C : hist_lists);
+  return TopkHistDest{w.hcnt, w.hlist, w.C};
+}
+
+hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                  int num_rows, int max_row_len, int k, int32_t *idx, void *ws,
+                                  int hist_lists, hipStream_t stream) {
+  const int C = (max_row_len + kChunk - 1) / kChunk;
+  MbWs w = carve_ws(ws, num_rows, C > hist_lists ? C : hist_lists);
+  w.nh = hist_lists;
+  dim3 grid(C, num_rows);
+  topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  topk_final_kernel<<<num_rows, kSmallThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,

@@ -33,6 +33,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert "dsa_indexer_logits" in names and "dsa_sparse_mla_decode_paged" in names
+    assert "dsa_indexer_topk" in names and "dsa_indexer_topk_workspace_size" in names
     for n in names:
         assert hasattr(lib, n), f"libdsa.so does not export {n}"
 
@@ -97,6 +98,29 @@ def test_topk_validation(lib):
     assert f(FAKE, 100, FAKE, 0, 100, 16, FAKE, None, 0, None) == OK           # empty batch
     assert f(FAKE, 100, FAKE, 4, 0, 16, FAKE, None, 0, None) == INVALID
     assert dsa.topk_workspace_size(4, 100, 0) == 0
+
+
+def test_indexer_topk_validation(lib):
+    def call(rows, dtype=1, ld=100, topk=16, idx=True, ws=None, ws_bytes=0, qs=None, ks=None,
+             name="dsa_indexer_topk"):
+        return getattr(lib, name)(ctypes.byref(rows), dtype, 64, 128, FAKE, qs, FAKE, ks, FAKE, FAKE,
+                                  ld, topk, FAKE if idx else None, ws, ws_bytes, None)
+    r = _rows()
+    assert call(r, topk=0) == INVALID
+    assert call(r, topk=2049) == INVALID
+    assert call(r, idx=False) == INVALID
+    assert call(r, ld=99) == INVALID
+    assert call(r, dtype=2) == INVALID                                 # fp8 without scales
+    assert call(_rows(num_rows=0)) == OK
+    assert call(r, name="dsa_indexer_topk_paged") == INVALID           # layout mismatch
+    # few long rows: the leading-digit histograms live in the workspace
+    big = _rows(num_rows=8, num_seqs=8, max_row_len=131072)
+    need = lib.dsa_indexer_topk_workspace_size(8, 131072, 2, 2048)
+    assert need >= dsa.topk_workspace_size(8, 131072, 2048) > 0
+    assert call(big, dtype=2, ld=131072, topk=2048, qs=FAKE, ks=FAKE) == WORKSPACE
+    assert call(big, dtype=2, ld=131072, topk=2048, qs=FAKE, ks=FAKE, ws=FAKE,
+                ws_bytes=need - 1) == WORKSPACE
+    assert lib.dsa_indexer_topk_workspace_size(8, 131072, 7, 2048) == 0   # bad dtype
 
 
 def _mla(lib, rows, name="dsa_sparse_mla_decode", dtype=1, H=128, Dqk=576, Dv=512, scale=0.07,

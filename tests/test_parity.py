@@ -130,6 +130,57 @@ def test_paged_physical_permutation_is_bit_identical():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+# ------------------------------------------------------------------------ fused indexer + top-k
+
+# few rows with a long maximum length: the indexer workgroups feed the selection directly
+FUSED_LENS = [1, 17, 2047, 2048, 2049, 9000, 20000, 40961]
+
+
+def _fused_vs_separate(wl):
+    rows = dev_rows(wl)
+    g = gpu_indexer(wl)
+    idx_sep = dsa.topk(g, wl.row_len, wl.topk, wl.max_row_len)
+    logits = torch.full_like(g, float("nan"))
+    idx_f = dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, q_scale=wl.q_scale,
+                             k_scale=wl.k_scale)
+    assert torch.equal(torch.nan_to_num(g, nan=-1.0), torch.nan_to_num(logits, nan=-1.0))
+    assert torch.equal(idx_sep, idx_f)
+    return g, idx_f
+
+
+@pytest.mark.parametrize("idx_dtype,paged", [("bf16", False), ("fp8", False), ("bf16", True),
+                                             ("fp8", True)])
+def test_fused_indexer_topk_matches_separate_calls(idx_dtype, paged):
+    wl = workloads.decode(FUSED_LENS, idx_dtype=idx_dtype, paged=paged, seed=91, device=DEV,
+                          name=f"fused_{idx_dtype}_{'paged' if paged else 'contig'}")
+    say(f"fused indexer+topk {wl.name}")
+    g, idx = _fused_vs_separate(wl)
+    lens = wl.row_len.cpu().numpy()
+    exp = oracle.topk(np.nan_to_num(g.cpu().numpy(), nan=0.0).astype(np.float32), lens, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), exp)
+    # a second call on the same workspace (left as the first call left it) agrees
+    ws = torch.empty(dsa.indexer_topk_workspace_size(wl.num_rows, wl.max_row_len, wl.q_idx.dtype,
+                                                     wl.topk), dtype=torch.uint8, device=DEV)
+    logits = torch.empty_like(g)
+    rows = dev_rows(wl)
+    a = dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, q_scale=wl.q_scale,
+                         k_scale=wl.k_scale, ws=ws).clone()
+    b = dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, q_scale=wl.q_scale,
+                         k_scale=wl.k_scale, ws=ws)
+    assert torch.equal(a, idx) and torch.equal(b, idx)
+
+
+def test_fused_indexer_topk_other_schedules_and_full_size():
+    # short rows take the one-workgroup-per-row selection: the call runs the stages in turn
+    wl = workloads.decode(RAGGED, idx_dtype="bf16", seed=92, device=DEV, name="fused_short")
+    say("fused indexer+topk short rows")
+    _fused_vs_separate(wl)
+    # the 128K-context decode batch at full size
+    wl = workloads.config(4, device=DEV)
+    say("fused indexer+topk config 4")
+    _fused_vs_separate(wl)
+
+
 # ------------------------------------------------------------------------ full-size configs
 
 @pytest.mark.parametrize("cfg,which", [(2, [0, 17, 63]), (4, [0, 5]), (5, [0, 1, 9, 31])])
