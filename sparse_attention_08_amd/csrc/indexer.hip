@@ -101,13 +101,20 @@ __device__ __forceinline__ int key_swz(int key) {
   if constexpr (FP8) return ((key >> 1) & 7) ^ ((key & 1) << 2);
   return key & 15;
 }
-// Launch shape (measured on MI355X): 8 waves of 4 KB key groups, 3-deep LDS rings, grid
-// sized for about 256 workgroups.
-#ifndef DSA_IDX_DEPTH
-#define DSA_IDX_DEPTH 3
+// Launch shape (measured on MI355X): 4 KB key groups; fp8 keys with 16 waves per workgroup
+// and 2-slot rings, bf16 keys (more registers per wave) with 8 waves and 3-slot rings; the
+// grid is sized for about 256 workgroups.
+#ifndef DSA_IDX_WAVES_FP8
+#define DSA_IDX_WAVES_FP8 16
 #endif
-#ifndef DSA_IDX_WAVES
-#define DSA_IDX_WAVES 8
+#ifndef DSA_IDX_DEPTH_FP8
+#define DSA_IDX_DEPTH_FP8 2
+#endif
+#ifndef DSA_IDX_WAVES_BF16
+#define DSA_IDX_WAVES_BF16 8
+#endif
+#ifndef DSA_IDX_DEPTH_BF16
+#define DSA_IDX_DEPTH_BF16 3
 #endif
 #ifndef DSA_IDX_BLOCKS
 #define DSA_IDX_BLOCKS 256
@@ -116,8 +123,6 @@ __device__ __forceinline__ int key_swz(int key) {
 #define DSA_IDX_GROUP_BYTES 4096
 #endif
 constexpr int kGroupBytes = DSA_IDX_GROUP_BYTES;   // keys streamed per wave per step
-constexpr int kDepth = DSA_IDX_DEPTH;       // LDS slots per wave (kDepth-1 groups in flight)
-constexpr int kIdxWaves = DSA_IDX_WAVES;
 
 template <bool FP8>
 struct IdxCfg {
@@ -126,6 +131,9 @@ struct IdxCfg {
   static constexpr int kTiles = kKeys / 16;                    // 16-key MFMA tiles per group
   static constexpr int kChunks = kRowBytes / 64;               // 16-byte chunks per lane per key
   static constexpr int kSlotBytes = kGroupBytes + (FP8 ? 256 : 0);   // keys (+ 64 scales)
+  static constexpr int kWaves = FP8 ? DSA_IDX_WAVES_FP8 : DSA_IDX_WAVES_BF16;   // per workgroup
+  static constexpr int kDepth = FP8 ? DSA_IDX_DEPTH_FP8 : DSA_IDX_DEPTH_BF16;   // ring slots per wave
+  static_assert(kKeys % 16 == 0 && kKeys >= 16 && kKeys <= 64, "a group is 1 to 4 MFMA tiles");
 };
 
 typedef void __attribute__((address_space(3))) *lds_void_ptr;
@@ -248,19 +256,18 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
 // keys (the first stage of the few-row top-k) and deposit the nonzero bins, compressed, as
 // list blockIdx.x of row r.
 template <bool FP8, bool PAGED, bool HIST>
-__global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
+__global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kernel(
     RowsDev rows, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, const float *__restrict__ w,
     float *__restrict__ logits, int64_t ld, uint32_t *__restrict__ hcnt,
     uint32_t *__restrict__ hlist, int hstride) {
   using C = IdxCfg<FP8>;
   constexpr int kQChunks = kIdxHeads * C::kRowBytes / 16;
-  constexpr int kThreads = kIdxWaves * kWave;
+  constexpr int kThreads = C::kWaves * kWave;
   extern __shared__ __attribute__((aligned(16))) uint8_t idx_smem[];
-  __shared__ uint32_t wtot[kIdxWaves];
   uint8_t *smem = idx_smem;
   i32x4 *q_lds = reinterpret_cast<i32x4 *>(smem);
-  uint32_t *hist = reinterpret_cast<uint32_t *>(smem + kQChunks * 16 + kIdxWaves * kDepth * C::kSlotBytes);
+  uint32_t *hist = reinterpret_cast<uint32_t *>(smem + kQChunks * 16 + C::kWaves * C::kDepth * C::kSlotBytes);
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -269,9 +276,9 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   // The row's key groups are dealt to its waves round-robin (wave wr of WR takes groups wr,
   // wr + WR, ...), so at any time the row's waves stream one contiguous window of it.
   const int n_row_groups = (len + C::kKeys - 1) / C::kKeys;
-  const int waves_per_row = gridDim.x * kIdxWaves;
-  const int wr = blockIdx.x * kIdxWaves + wave;
-  if (blockIdx.x * kIdxWaves >= n_row_groups) {
+  const int waves_per_row = gridDim.x * C::kWaves;
+  const int wr = blockIdx.x * C::kWaves + wave;
+  if (blockIdx.x * C::kWaves >= n_row_groups) {
     if (HIST && threadIdx.x == 0) hcnt[(size_t)r * hstride + blockIdx.x] = 0;
     return;
   }
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
   const int n_groups = active ? (n_row_groups - wr + waves_per_row - 1) / waves_per_row : 0;
   const int64_t s_last = len - 1;
   const int b = rows.row_seq[r];
-  uint8_t *ring = smem + kQChunks * 16 + wave * kDepth * C::kSlotBytes;
+  uint8_t *ring = smem + kQChunks * 16 + wave * C::kDepth * C::kSlotBytes;
   int64_t base_row = 0;
   int page_lane = 0;   // paged layout: lane j holds the page of the wave's j-th group
   DmaLane<FP8> dl;
@@ -296,9 +303,9 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
     } else {
       base_row = rows.seq_start[b];
     }
-    // the first kDepth-1 key groups start streaming before the query block is loaded
+    // the first C::kDepth-1 key groups start streaming before the query block is loaded
     dl.init(lane);
-    const int n_pro = min(kDepth - 1, n_groups);
+    const int n_pro = min(C::kDepth - 1, n_groups);
     for (int d = 0; d < n_pro; ++d)
       issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, group_page(d),
                               group_start(d), s_last, dl, lane);
@@ -330,17 +337,17 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
       }
     float *out = logits + (int64_t)r * ld;
     for (int i = 0; i < n_groups; ++i) {
-      if (i + kDepth - 1 < n_groups) {
-        issue_group<FP8, PAGED>(ring + ((i + kDepth - 1) % kDepth) * C::kSlotBytes, k, k_scale,
-                                base_row, group_page(i + kDepth - 1), group_start(i + kDepth - 1),
+      if (i + C::kDepth - 1 < n_groups) {
+        issue_group<FP8, PAGED>(ring + ((i + C::kDepth - 1) % C::kDepth) * C::kSlotBytes, k, k_scale,
+                                base_row, group_page(i + C::kDepth - 1), group_start(i + C::kDepth - 1),
                                 s_last, dl, lane);
-        // group i is older than the kDepth-1 groups issued after it: loads complete in order
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (kDepth - 1)));
+        // group i is older than the C::kDepth-1 groups issued after it: loads complete in order
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (C::kDepth - 1)));
       } else {
         // tail: nothing is issued past the wave's groups, so wait for every load in flight
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
       }
-      const float v = consume_group<FP8>(ring + (i % kDepth) * C::kSlotBytes, qf, wt, lane);
+      const float v = consume_group<FP8>(ring + (i % C::kDepth) * C::kSlotBytes, qf, wt, lane);
       const int64_t s = group_start(i) + lane;
       if (lane < C::kKeys && s < len) {
         out[s] = v;
@@ -362,10 +369,12 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
       const uint32_t u = __shfl_up(inc, o, kWave);
       if (lane >= o) inc += u;
     }
+    // wave totals go to the query block area: every wave holds its q operands in registers
+    uint32_t *wtot = reinterpret_cast<uint32_t *>(q_lds);
     if (lane == 63) wtot[wave] = inc;
     __syncthreads();
     uint32_t off = inc - nz, total = 0;
-    for (int wv = 0; wv < kIdxWaves; ++wv) {
+    for (int wv = 0; wv < C::kWaves; ++wv) {
       off += (wv < wave) ? wtot[wv] : 0u;
       total += wtot[wv];
     }
@@ -380,8 +389,10 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void indexer_mfma_kernel(
 }
 
 size_t indexer_lds_bytes(bool fp8, bool hist) {
-  const size_t base = fp8 ? (size_t)kIdxHeads * IdxCfg<true>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<true>::kSlotBytes
-                          : (size_t)kIdxHeads * IdxCfg<false>::kRowBytes + (size_t)kIdxWaves * kDepth * IdxCfg<false>::kSlotBytes;
+  using F = IdxCfg<true>;
+  using B = IdxCfg<false>;
+  const size_t base = fp8 ? (size_t)kIdxHeads * F::kRowBytes + (size_t)F::kWaves * F::kDepth * F::kSlotBytes
+                          : (size_t)kIdxHeads * B::kRowBytes + (size_t)B::kWaves * B::kDepth * B::kSlotBytes;
   return base + (hist ? sizeof(uint32_t) * kLeadBins : 0);
 }
 
@@ -398,7 +409,7 @@ static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const Ro
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  indexer_mfma_kernel<FP8, PAGED, HIST><<<grid, kIdxWaves * kWave, shm, stream>>>(
+  indexer_mfma_kernel<FP8, PAGED, HIST><<<grid, IdxCfg<FP8>::kWaves * kWave, shm, stream>>>(
       rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
   return hipGetLastError();
 }
@@ -408,7 +419,8 @@ static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const Ro
 static int64_t keys_per_wave(int num_rows, int max_row_len, bool fp8) {
   const int64_t total = (int64_t)num_rows * max_row_len;
   constexpr int64_t kBlocksTarget = DSA_IDX_BLOCKS;
-  int64_t kpw = (total + kIdxWaves * kBlocksTarget - 1) / (kIdxWaves * kBlocksTarget);
+  const int64_t waves = fp8 ? IdxCfg<true>::kWaves : IdxCfg<false>::kWaves;
+  int64_t kpw = (total + waves * kBlocksTarget - 1) / (waves * kBlocksTarget);
   kpw = ((kpw + 63) / 64) * 64;
   if (kpw < 64) kpw = 64;
   // at most 64 groups per wave (one page id per lane)
@@ -417,7 +429,8 @@ static int64_t keys_per_wave(int num_rows, int max_row_len, bool fp8) {
 }
 
 int indexer_blocks_per_row(int num_rows, int max_row_len, bool fp8) {
-  const int64_t per_block = kIdxWaves * keys_per_wave(num_rows, max_row_len, fp8);
+  const int64_t per_block = (fp8 ? IdxCfg<true>::kWaves : IdxCfg<false>::kWaves) *
+                            keys_per_wave(num_rows, max_row_len, fp8);
   return (int)((max_row_len + per_block - 1) / per_block);
 }
 

@@ -29,6 +29,11 @@ constexpr int kD0Bits = kLeadDigitBits, kD1Bits = 10, kD2Bits = 10;
 constexpr int kBins = 1 << kD0Bits;        // 4096
 constexpr int kChunk = 4096;               // scores per workgroup in the few-row schedule
 constexpr int kSmallThreads = 1024;
+#ifndef DSA_TOPK_FINAL_THREADS
+#define DSA_TOPK_FINAL_THREADS 1024
+#endif
+constexpr int kFinalThreads = DSA_TOPK_FINAL_THREADS;   // >= kMaxChunks
+static_assert(kFinalThreads >= 256 && (1 << 10) % kFinalThreads == 0, "final select shape");
 constexpr int kMbThreads = 256;
 constexpr int kStageElems = 28672;         // single-row schedule: up to 112 KB of staged keys
 constexpr int kSurvivorCap = 10240;        // survivors selected in LDS (80 KB)
@@ -476,12 +481,13 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
 
 // (3) one workgroup per row: exact select among the survivors, gathered with independent
 // loads (chunk of each survivor found from the prefix of the per-chunk counts)
-__global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *__restrict__ logits,
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_final_kernel(const float *__restrict__ logits,
                                                                    int64_t ld,
                                                                    const int32_t *__restrict__ row_len,
                                                                    int k, int32_t *__restrict__ idx,
                                                                    MbWs ws) {
-  __shared__ BlockScratch<kSmallThreads> sh;
+  __shared__ BlockScratch<NT> sh;
   __shared__ uint32_t skey[kSurvivorCap];
   __shared__ int32_t spos[kSurvivorCap];
   __shared__ uint32_t coff[kMaxChunks + 1];
@@ -493,21 +499,21 @@ __global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *
   const int bstar = (int)ws.meta[2 * r];
   const int above = (int)ws.meta[2 * r + 1];
   {
-    // exclusive prefix of the per-chunk survivor counts (nblk <= kMaxChunks <= kSmallThreads)
+    // exclusive prefix of the per-chunk survivor counts (nblk <= kMaxChunks <= NT)
     const uint32_t cnt = threadIdx.x < nblk ? ws.scnt[(size_t)r * ws.C + threadIdx.x] : 0u;
     uint32_t total;
-    const uint32_t before = block_excl_scan<kSmallThreads>(cnt, total, sh);
+    const uint32_t before = block_excl_scan<NT>(cnt, total, sh);
     if (threadIdx.x < nblk) coff[threadIdx.x] = before;
     if (threadIdx.x == 0) coff[nblk] = total;
   }
   __syncthreads();
   const int M = (int)coff[nblk];
   if (M <= kSurvivorCap) {
-    constexpr int kRounds = (kSurvivorCap + kSmallThreads - 1) / kSmallThreads;   // 10
+    constexpr int kRounds = (kSurvivorCap + NT - 1) / NT;   // 10
     uint2 v[kRounds];
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
-      const int e = j * kSmallThreads + threadIdx.x;
+      const int e = j * NT + threadIdx.x;
       if (e < M) {
         const int ch = chunk_of(coff, nblk, (uint32_t)e);
         v[j] = ws.slist[((size_t)r * ws.C + ch) * kChunk + (e - (int)coff[ch])];
@@ -515,17 +521,17 @@ __global__ __launch_bounds__(kSmallThreads) void topk_final_kernel(const float *
     }
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
-      const int e = j * kSmallThreads + threadIdx.x;
+      const int e = j * NT + threadIdx.x;
       if (e < M) {
         skey[e] = v[j].x;
         spos[e] = (int32_t)v[j].y;
       }
     }
     __syncthreads();
-    select_block<kSmallThreads>(SurvivorAcc{skey, spos}, M, k, out, sh, bstar, k - above);
+    select_block<NT>(SurvivorAcc{skey, spos}, M, k, out, sh, bstar, k - above);
   } else {
     // degenerate score distributions (huge ties around the threshold): whole row
-    select_block<kSmallThreads>(RowAcc{logits + (int64_t)r * ld}, n, k, out, sh, bstar, k - above);
+    select_block<NT>(RowAcc{logits + (int64_t)r * ld}, n, k, out, sh, bstar, k - above);
   }
 }
 
@@ -566,7 +572,7 @@ hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t
   w.nh = hist_lists;
   dim3 grid(C, num_rows);
   topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
-  topk_final_kernel<<<num_rows, kSmallThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  topk_final_kernel<kFinalThreads><<<num_rows, kFinalThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
   return hipGetLastError();
 }
 
@@ -578,7 +584,7 @@ hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, 
     dim3 grid(C, num_rows);
     topk_hist_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, w);
     topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
-    topk_final_kernel<<<num_rows, kSmallThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+    topk_final_kernel<kFinalThreads><<<num_rows, kFinalThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
     return hipGetLastError();
   }
   if (max_row_len <= kStageElems) {
