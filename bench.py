@@ -139,10 +139,13 @@ def summarize_pmc(kernel, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     cf, _ = _counter_per_dispatch(copy_fetch_csv, "copy", "FETCH_SIZE")
     cw, _ = _counter_per_dispatch(copy_write_csv, "copy", "WRITE_SIZE")
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
-    kf, nf = _counter_per_dispatch(fetch_csv, "dsa::" + kernel, "FETCH_SIZE")
-    kw, nw = _counter_per_dispatch(write_csv, "dsa::" + kernel, "WRITE_SIZE")
+    match = "dsa::" + kernel            # may name one instantiation, e.g. "k<true, false>"
+    kernel = kernel.split("<")[0]
+    kf, nf = _counter_per_dispatch(fetch_csv, match, "FETCH_SIZE")
+    kw, nw = _counter_per_dispatch(write_csv, match, "WRITE_SIZE")
     read_b, write_b = kf * f_scale * 1024.0, kw * w_scale * 1024.0
-    d = {"kernel": kernel, "workload_config": int(config), "source_sha": source_hash(kernel),
+    d = {"kernel": kernel, "instantiation": match, "workload_config": int(config),
+         "source_sha": source_hash(kernel),
          "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
          "copy_probe_mib": float(copy_mib), "copy_fetch_kib": cf, "copy_write_kib": cw,
          "fetch_scale": f_scale, "write_scale": w_scale,
@@ -152,7 +155,7 @@ def summarize_pmc(kernel, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     with open(os.path.join(PROFILES, f"{kernel}_pmc.json"), "w") as f:
         json.dump(d, f, indent=1)
     with open(os.path.join(PROFILES, f"{kernel}_pmc.md"), "w") as f:
-        f.write(f"# HBM traffic of {kernel} (workload config {config})\n\n"
+        f.write(f"# HBM traffic of `{match}` (workload config {config})\n\n"
                 f"Commands (from the repository root; `<C>` is FETCH_SIZE, then WRITE_SIZE):\n\n"
                 f"```\n{command}\n```\n\n"
                 f"| quantity | value |\n|---|---:|\n"
