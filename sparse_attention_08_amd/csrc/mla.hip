@@ -8,19 +8,17 @@
 // with a plain softmax (no sink, no output gate: same page, "Learnable attention sink",
 // "Gated attention output").
 //
-// bf16 kernel design.  A workgroup owns one query row, 64 heads (4 waves x 16 heads)
-// and a range of top-k slots.  The cache rows of all its slots are resolved up front;
-// selected entries are then gathered 32 at a time from HBM straight into a ring of LDS
-// tiles with direct global->LDS loads (several tiles in flight, no staging registers),
-// the XOR swizzle applied through the choice of source chunk.  Each wave computes the transposed
-// score tile S^T = C . Q^T (keys as MFMA rows, its 16 heads as columns, q resident in
-// registers), runs the online softmax in fp32 in the log2 domain, and accumulates
-// O += P . V with V read from the same LDS tile through the gfx950 transposing LDS
-// read (ds_read_b64_tr_b16), so the tile is stored once, row-major, for both products.
-// The LDS tile uses an XOR swizzle of 16-byte chunks so that both the row reads of the
-// score product and the transposed reads of the value product are conflict-free.
-// Few-row (decode) batches split the slots over several workgroups; each writes a
-// normalised bf16 partial and its log-sum-exp, and a combine kernel merges them.
+// bf16 kernel design.  A workgroup owns one query row, all 128 heads (8 waves x 16 heads)
+// and a range of its top-k slots.  The cache rows of the valid slots are resolved and
+// compacted up front; the selected entries are then gathered 32 at a time straight into a
+// ring of LDS tiles with global->LDS loads (several tiles in flight, no staging registers),
+// a swizzle of the 16-byte chunks applied through the choice of source chunk.  Each wave
+// computes the transposed score tile S^T = C . Q^T (entries as MFMA rows, its 16 heads as
+// columns, q resident in registers), runs the online softmax in fp32 in the log2 domain, and
+// accumulates O^T += V^T . P^T with V read from the same LDS tile through the gfx950
+// transposing LDS read (ds_read_b64_tr_b16), so the tile is stored once, row-major, for
+// both products.  Few-row (decode) batches split the slots over several workgroups; each
+// writes a normalised bf16 partial and its log-sum-exp, and a combine kernel merges them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -231,11 +229,11 @@ __device__ __forceinline__ void issue_tile(uint8_t *dst, const uint32_t *crow_ti
 
 // Waits until at most `younger` tiles of N loads each (issued after the awaited one) are
 // still in flight; vector-memory loads complete in issue order.
-static_assert(kRing >= 2 && kRing <= 4, "the ring keeps at most two tiles younger than the current");
+static_assert(kRing >= 3 && kRing <= 4, "at most two tiles in flight behind the current one");
 template <int N>
 __device__ __forceinline__ void wait_younger(int younger) {
-  if (kRing - 2 >= 2 && younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * N));
-  else if (kRing - 2 >= 1 && younger >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(N));
+  if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * N));
+  else if (younger >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(N));
   else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 }
 
@@ -338,8 +336,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int n_dma = tile_dma_count(wave);
   TileDma td;
   td.init(wave, lane);
-  // prologue: tiles 0 .. kRing-2 in flight
-  for (int d = 0; d < kRing - 1 && d < n_tiles; ++d)
+  // tile loads run kAhead tiles ahead of the tile being scored
+  constexpr int kAhead = kRing - 1;
+  for (int d = 0; d < kAhead && d < n_tiles; ++d)
     issue_tile(sh.tiles[d], sh.crow + d * kTile, kv, td, n_dma, wave);
 
   // score operand rows: block kb, lane row c <-> entry 8(c>>2) + (c&3) + 4kb (both share a
@@ -354,23 +353,11 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int ua = swa >> 1;
   const int v_off = (8 * g + tr_i) * kRowBytes + 8 * (tr_q & 1) + 16 * ((tr_q >> 1) ^ (swa & 1));
 
-  uint32_t slot_use = 0, slot_issue = (kRing - 1) * kTileBytes;   // byte offsets in the ring
-  for (int it = 0; it < n_tiles; ++it) {
-    // tiles it+1 .. it+kRing-2 (those that exist) were issued after tile `it`
-    const int younger = min(kRing - 2, n_tiles - 1 - it);
-    if (n_dma == 5) wait_younger<5>(younger);
-    else wait_younger<4>(younger);
-    // every wave's share of tile `it` has landed, and every wave is done with tile it-1
-    lds_barrier();
-    if (it + kRing - 1 < n_tiles)
-      issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kRing - 1) * kTile, kv, td, n_dma, wave);
-    const uint8_t *tile = sh.tiles[0] + slot_use;
-    // ring slots advance by one tile and wrap (uniform, loop-carried: no division)
-    slot_use = slot_use + kTileBytes == kRing * kTileBytes ? 0u : slot_use + kTileBytes;
-    slot_issue = slot_issue + kTileBytes == kRing * kTileBytes ? 0u : slot_issue + kTileBytes;
-    // ---- scores: 18 steps of 32 dims, two independent 16-entry blocks; the operand loads
-    // run kPf steps ahead of the products that use them
-    f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+  // ---- scores of a tile: 18 steps of 32 dims, two independent 16-entry blocks; the operand
+  // loads run kPf steps ahead of the products that use them
+  auto scores = [&](const uint8_t *tile, f32x4 &sc0, f32x4 &sc1) {
+    sc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    sc1 = f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int kPf = DSA_MLA_QK_PREFETCH;
     bf16x8 xr[kPf][2];
 #pragma unroll
@@ -393,6 +380,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[t], sc0, 0, 0, 0);
       sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[t], sc1, 0, 0, 0);
     }
+  };
+  // ---- online softmax of tile `it`: returns the bf16 weights (B operand of the value
+  // product) and rescales the accumulators when the running maximum moves
+  auto weights = [&](f32x4 sc0, f32x4 sc1, int it) {
     // only the last tile can hold padding entries: their scores become -inf
     const int nv = n_valid - it * kTile;
     if (nv < kTile) {
@@ -428,9 +419,11 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       p[4 + i] = __builtin_amdgcn_exp2f(fmaf(sc1[i], scale_log2, neg_m));
     }
     l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
-    // ---- O^T += V^T . P^T: value rows 16nb + c
+    return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+  };
+  // ---- O^T += V^T . P^T over a tile: value rows 16nb + c
+  auto accumulate = [&](const uint8_t *tile, bf16x8 pf) {
     const uint8_t *va[4];   // per-lane bases; the 128-byte group and the +4 entries are immediates
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4) va[m4] = tile + v_off + 32 * (m4 ^ ua);
@@ -452,6 +445,26 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
       oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pf, oacc[nb], 0, 0, 0);
     }
+  };
+
+  uint32_t slot_use = 0, slot_issue = kAhead * kTileBytes;   // byte offsets in the ring
+  for (int it = 0; it < n_tiles; ++it) {
+    // tiles it+1 .. it+kAhead-1 (those that exist) were issued after tile `it`
+    const int younger = min(kAhead - 1, n_tiles - 1 - it);
+    if (n_dma == 5) wait_younger<5>(younger);
+    else wait_younger<4>(younger);
+    // every wave's share of tile `it` has landed, and every wave is done with tile it-1
+    // (whose slot the next load overwrites)
+    lds_barrier();
+    if (it + kAhead < n_tiles)
+      issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kAhead) * kTile, kv, td, n_dma, wave);
+    const uint8_t *tile = sh.tiles[0] + slot_use;
+    f32x4 sc0, sc1;
+    scores(tile, sc0, sc1);
+    accumulate(tile, weights(sc0, sc1, it));
+    // ring slots advance by one tile and wrap (uniform, loop-carried: no division)
+    slot_use = slot_use + kTileBytes == kRing * kTileBytes ? 0u : slot_use + kTileBytes;
+    slot_issue = slot_issue + kTileBytes == kRing * kTileBytes ? 0u : slot_issue + kTileBytes;
   }
   // every wave is done with the ring before it is reused for staging (no load is in flight:
   // the last iteration waited for all of them)
