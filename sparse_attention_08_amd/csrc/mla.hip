@@ -456,11 +456,13 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     // every wave's share of tile `it` has landed, and every wave is done with tile it-1
     // (whose slot the next load overwrites)
     lds_barrier();
-    if (it + kAhead < n_tiles)
-      issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kAhead) * kTile, kv, td, n_dma, wave);
     const uint8_t *tile = sh.tiles[0] + slot_use;
     f32x4 sc0, sc1;
     scores(tile, sc0, sc1);
+    // the next tile's loads go out after the score product (measured faster than before it:
+    // the score loads of every wave start right at the barrier)
+    if (it + kAhead < n_tiles)
+      issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kAhead) * kTile, kv, td, n_dma, wave);
     accumulate(tile, weights(sc0, sc1, it));
     // ring slots advance by one tile and wrap (uniform, loop-carried: no division)
     slot_use = slot_use + kTileBytes == kRing * kTileBytes ? 0u : slot_use + kTileBytes;
