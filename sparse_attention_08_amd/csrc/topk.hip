@@ -38,6 +38,8 @@ constexpr int kMbThreads = 256;
 constexpr int kStageElems = 28672;         // single-row schedule: up to 112 KB of staged keys
 constexpr int kSurvivorCap = 10240;        // survivors selected in LDS (80 KB)
 constexpr int kMaxChunks = 256;            // chunked schedule handles rows up to 1M scores
+constexpr int kListHead = 8;               // histogram entries per thread loaded with the counts
+constexpr int kSurvHead = 4;               // survivors per thread loaded with the chunk counts
 
 // ------------------------------------------------------------------------------------
 // block-wide helpers
@@ -340,15 +342,15 @@ __device__ __forceinline__ int chunk_of(const uint32_t *off, int nc, uint32_t e)
 }
 
 // (2) merge the row's histograms, find b*, keep this chunk's survivors in position order.
-// Every global load is independent of the others: the chunk's scores are requested first,
-// then all chunk counts, then all histogram entries of the row at once.
+// One round of independent loads: the chunk's scores, then every histogram list's count
+// together with its first entries (a list is read by several threads); only lists longer
+// than that need a second round.
 __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__restrict__ logits,
                                                                  int64_t ld,
                                                                  const int32_t *__restrict__ row_len,
                                                                  int k, int32_t *__restrict__ idx,
                                                                  MbWs ws) {
   __shared__ uint32_t lh[kBins];
-  __shared__ uint32_t off[kMaxChunks + 1];
   __shared__ uint32_t wtot[kMbThreads / kWave];
   __shared__ uint32_t wcnt[kMbThreads / kWave];
   __shared__ uint32_t s_bstar, s_above;
@@ -373,44 +375,28 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     const int i = wlo + 64 * j + lane;
     sv[j] = i < n ? row[i] : 0.f;
   }
-  // counts of every histogram list of the row (nh <= kMaxChunks = kMbThreads)
+  // every histogram list of the row: tpl threads per list (nh <= kMaxChunks = kMbThreads)
   const int nh = ws.nh ? ws.nh : nblk;
-  const uint32_t cnt = threadIdx.x < nh ? ws.hcnt[(size_t)r * ws.C + threadIdx.x] : 0u;
-  for (int i = threadIdx.x; i < kBins; i += kMbThreads) lh[i] = 0;
-  {
-    uint32_t inc = cnt;
+  int tpl = kMbThreads;
+  while (tpl > 1 && tpl * nh > kMbThreads) tpl >>= 1;
+  const int l = threadIdx.x / tpl, sub = threadIdx.x % tpl;
+  const uint32_t *hl = ws.hlist + ((size_t)r * ws.C + l) * kBins;
+  uint32_t cnt = 0, ent[kListHead];
+  if (l < nh) {
+    cnt = ws.hcnt[(size_t)r * ws.C + l];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += u;
-    }
-    if (lane == 63) wtot[wave] = inc;
-    __syncthreads();
-    uint32_t before = inc - cnt, total = 0;
-    for (int w = 0; w < kMbThreads / kWave; ++w) {
-      before += (w < wave) ? wtot[w] : 0u;
-      total += wtot[w];
-    }
-    if (threadIdx.x < nh) off[threadIdx.x] = before;
-    if (threadIdx.x == 0) off[nh] = total;
+    for (int j = 0; j < kListHead; ++j) ent[j] = hl[sub + tpl * j];   // within the list's bins
   }
+  for (int i = threadIdx.x; i < kBins; i += kMbThreads) lh[i] = 0;
   __syncthreads();
-  // all histogram entries of the row, 8 independent loads per thread per round
-  const uint32_t E = off[nh];
-  for (uint32_t e0 = 0; e0 < E; e0 += 8 * kMbThreads) {
-    uint32_t ent[8];
+  if (l < nh) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = e0 + j * kMbThreads + threadIdx.x;
-      ent[j] = 0;
-      if (e < E) {
-        const int ch = chunk_of(off, nh, e);
-        ent[j] = ws.hlist[((size_t)r * ws.C + ch) * kBins + (e - off[ch])];
-      }
+    for (int j = 0; j < kListHead; ++j)
+      if ((uint32_t)(sub + tpl * j) < cnt) atomicAdd(&lh[ent[j] >> 16], ent[j] & 0xFFFFu);
+    for (uint32_t e = tpl * kListHead + sub; e < cnt; e += tpl) {
+      const uint32_t v = hl[e];
+      atomicAdd(&lh[v >> 16], v & 0xFFFFu);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (ent[j]) atomicAdd(&lh[ent[j] >> 16], ent[j] & 0xFFFFu);
   }
   __syncthreads();
   // digit b* holding the k-th largest: thread t owns bins 4095-16t-j (descending)
@@ -427,7 +413,6 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     const uint32_t u = __shfl_up(inc, o, kWave);
     if (lane >= o) inc += u;
   }
-  __syncthreads();   // wtot reuse
   if (lane == 63) wtot[wave] = inc;
   __syncthreads();
   uint32_t before = inc - tot;
@@ -498,33 +483,42 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(const float *__restrict_
   const int nblk = (n + kChunk - 1) / kChunk;
   const int bstar = (int)ws.meta[2 * r];
   const int above = (int)ws.meta[2 * r + 1];
+  // survivor counts of the chunks and each chunk's first survivors in one round of loads:
+  // tpc threads per chunk (nblk <= kMaxChunks <= NT), kSurvHead survivors each
+  int tpc = NT;
+  while (tpc > 1 && tpc * nblk > NT) tpc >>= 1;
+  const int ch = threadIdx.x / tpc, sub = threadIdx.x % tpc;
+  const uint2 *cl = ws.slist + ((size_t)r * ws.C + ch) * kChunk;
+  uint32_t cnt = 0;
+  uint2 head[kSurvHead];
+  if (ch < nblk) {
+    cnt = ws.scnt[(size_t)r * ws.C + ch];
+#pragma unroll
+    for (int j = 0; j < kSurvHead; ++j) head[j] = cl[sub + tpc * j];   // within the chunk's list
+  }
   {
-    // exclusive prefix of the per-chunk survivor counts (nblk <= kMaxChunks <= NT)
-    const uint32_t cnt = threadIdx.x < nblk ? ws.scnt[(size_t)r * ws.C + threadIdx.x] : 0u;
     uint32_t total;
-    const uint32_t before = block_excl_scan<NT>(cnt, total, sh);
-    if (threadIdx.x < nblk) coff[threadIdx.x] = before;
+    const uint32_t before = block_excl_scan<NT>(sub == 0 ? cnt : 0u, total, sh);
+    if (sub == 0 && ch < nblk) coff[ch] = before;
     if (threadIdx.x == 0) coff[nblk] = total;
   }
   __syncthreads();
   const int M = (int)coff[nblk];
   if (M <= kSurvivorCap) {
-    constexpr int kRounds = (kSurvivorCap + NT - 1) / NT;   // 10
-    uint2 v[kRounds];
+    if (ch < nblk) {
+      const int dst = (int)coff[ch];
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const int e = j * NT + threadIdx.x;
-      if (e < M) {
-        const int ch = chunk_of(coff, nblk, (uint32_t)e);
-        v[j] = ws.slist[((size_t)r * ws.C + ch) * kChunk + (e - (int)coff[ch])];
+      for (int j = 0; j < kSurvHead; ++j) {
+        const uint32_t e = sub + tpc * j;
+        if (e < cnt) {
+          skey[dst + e] = head[j].x;
+          spos[dst + e] = (int32_t)head[j].y;
+        }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const int e = j * NT + threadIdx.x;
-      if (e < M) {
-        skey[e] = v[j].x;
-        spos[e] = (int32_t)v[j].y;
+      for (uint32_t e = tpc * kSurvHead + sub; e < cnt; e += tpc) {
+        const uint2 v = cl[e];
+        skey[dst + e] = v.x;
+        spos[dst + e] = (int32_t)v.y;
       }
     }
     __syncthreads();

@@ -248,6 +248,15 @@ def test_topk_edge_cases():
         rows[5] = rng.standard_normal(n)
         _topk_case(rows, [n, n, n, 5000, 30000, 1], k)
         _topk_case(rows[:, :3000], [3000, 2048, 2049, 1, 17, 3000], k)
+    # rows up to 2^18 scores are selected by one workgroup each; longer ones take the chunked
+    # filter and a final workgroup
+    n = 300000
+    rows = np.zeros((3, n), dtype=np.float32)
+    rows[0] = rng.standard_normal(n)
+    rows[1] = rng.integers(-40, 41, size=n) / 8.0          # ties at the threshold
+    rows[2] = np.where(rng.random(n) < 0.5, 0.0, rng.standard_normal(n))
+    _topk_case(rows[:, :262144], [262144, 200001, 5], 2048)
+    _topk_case(rows, [300000, 262145, 40000], 2048)
 
 
 def test_mla_skips_invalid_and_empty_selections():
