@@ -2,7 +2,9 @@
 
 Every source under csrc/ is compiled with hipcc for gfx950 only, in parallel, then linked
 into sparse_attention_08_amd/libdsa.so next to this file.  Packed-fp32 instruction
-selection is switched off for all device code.
+selection is switched off for all device code; the leading scalar and pointer arguments of
+every kernel are preloaded into SGPRs at launch (no kernel-argument load before the first
+dependent memory access).
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # leading scalar/pointer kernel arguments arrive preloaded in SGPRs
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-I", INCLUDE, "-I", CSRC]
 
 

@@ -158,6 +158,7 @@ struct MlaShared {
   uint8_t tiles[kRing][kTileBytes];
   uint32_t crow[kMaxSlotsPerSplit];        // cache rows of the split's valid slots, compacted
   uint32_t wcount[kMlaWaves];
+  uint32_t wbad[kMlaWaves];                // invalid slots seen by each wave
 };
 
 // The 36 DMA instructions of a tile go to waves 0..7 in turn (waves 0-3 issue 5, 4-7
@@ -254,12 +255,17 @@ __device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
 // value dims, V^T read from the same LDS tile with the transposing LDS read.  Entry rows
 // of the score blocks are permuted (block kb, row 4g + i <-> entry 8g + 4kb + i) so that
 // each lane's weights are exactly the B operand of the value product.
+// The leading arguments are the ones the prologue needs first (scalars and pointers, so
+// the launch can preload them into registers).
 template <bool PAGED>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
-    RowsDev rows, int R, int H, float scale_log2, const uint16_t *__restrict__ q,
-    const uint8_t *__restrict__ kv, const int32_t *__restrict__ idx, int k, int slots_per_split,
-    int splits, uint16_t *__restrict__ out, float *__restrict__ lse, uint16_t *__restrict__ part_o,
-    float *__restrict__ part_lse) {
+    int R, int splits, int k, int slots_per_split, const int32_t *__restrict__ idx,
+    const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq,
+    const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
+    const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
+    const uint8_t *__restrict__ kv, uint16_t *__restrict__ out, float *__restrict__ lse,
+    uint16_t *__restrict__ part_o, float *__restrict__ part_lse) {
+  constexpr int H = kHeadsPerBlock;
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared &sh = *reinterpret_cast<MlaShared *>(mla_smem);
   MlaCoord co;
@@ -268,10 +274,6 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int len = rows.row_len[r], b = rows.row_seq[r];
-  // contiguous layout: the sequence's first cache row, fetched before anything else (it is
-  // a second dependent load on the way to the first tile)
-  const int64_t seq_base = PAGED ? 0 : rows.seq_start[b];
   const int h0 = wave * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
@@ -281,14 +283,16 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   int n_valid = 0;
   bf16x8 qf[18];
   {
-    // the slot loads go out before the query loads: waits on vector memory are in issue
-    // order, so resolving the slots does not wait for the query block
+    // the slot loads go out first (they need only the launch arguments), then the row's
+    // descriptor loads and the query block: waits on vector memory are in issue order, so
+    // resolving the slots does not wait for the query block
     int sv[kSlotRounds];
 #pragma unroll
     for (int j = 0; j < kSlotRounds; ++j) {
       const int t = j * kMlaThreads + threadIdx.x;
       sv[j] = t < n_slots ? idx_row[t] : -1;
     }
+    __builtin_amdgcn_sched_barrier(0);
     // q^T operand: head h0 + c, dims 32t + 8g .. +8 (in flight during the slot resolution
     // and the first tile loads)
     {
@@ -297,16 +301,42 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const RowsDev rows{row_seq, row_len, seq_start, page_table, max_pages};
+    const int len = row_len[r], b = row_seq[r];
+    const int64_t seq_base = PAGED ? 0 : seq_start[b];
     int64_t crow_v[kSlotRounds];
+    uint32_t bad = 0;
 #pragma unroll
-    for (int j = 0; j < kSlotRounds; ++j)
+    for (int j = 0; j < kSlotRounds; ++j) {
+      const int t = j * kMlaThreads + threadIdx.x;
       crow_v[j] = (sv[j] >= 0 && sv[j] < len)
                       ? (PAGED ? cache_row<PAGED>(rows, b, sv[j]) : seq_base + sv[j])
                       : -1;
+      bad += (t < n_slots && crow_v[j] < 0) ? 1u : 0u;
+    }
+    // common case, every slot valid: the slots are their own compaction.  Each thread files
+    // its slots' rows, wave 0 pads the last tile with slot 0's row, and one barrier settles
+    // whether that stands.
+#pragma unroll
+    for (int j = 0; j < kSlotRounds; ++j) {
+      const int t = j * kMlaThreads + threadIdx.x;
+      if (t < n_slots) sh.crow[t] = (uint32_t)crow_v[j];
+    }
+    const int pad = ((n_slots + kTile - 1) / kTile) * kTile - n_slots;   // < kTile <= 64
+    const uint32_t row0 = (uint32_t)__shfl((int)crow_v[0], 0, kWave);
+    if (wave == 0 && lane < pad) sh.crow[n_slots + lane] = row0;
+    const uint32_t wbad = (uint32_t)__popcll(__ballot(bad != 0));
+    if (lane == 0) sh.wbad[wave] = wbad;
+    lds_barrier();
+    uint32_t any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < kMlaWaves; ++w) any_bad |= sh.wbad[w];
+    if (any_bad == 0) n_valid = n_slots;
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int j = 0; j < kSlotRounds; ++j) {
-      if (j * kMlaThreads >= n_slots) break;
+      if (any_bad == 0 || j * kMlaThreads >= n_slots) break;
       const bool ok = crow_v[j] >= 0;
       const uint64_t m = __ballot(ok);
       if (lane == 0) sh.wcount[wave] = (uint32_t)__popcll(m);
@@ -324,9 +354,11 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     }
   }
   const int n_tiles = (n_valid + kTile - 1) / kTile;
-  // the tail of the last tile gathers a harmless valid row and is masked off
-  if (threadIdx.x < n_tiles * kTile - n_valid) sh.crow[n_valid + threadIdx.x] = sh.crow[0];
-  lds_barrier();
+  if (n_valid != n_slots) {
+    // the tail of the last tile gathers a harmless valid row and is masked off
+    if (threadIdx.x < n_tiles * kTile - n_valid) sh.crow[n_valid + threadIdx.x] = sh.crow[0];
+    lds_barrier();
+  }
 
   f32x4 oacc[32];
 #pragma unroll
@@ -488,13 +520,17 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
   __builtin_amdgcn_wave_barrier();
   uint16_t *dst;
+  // the lane's head, recomputed here: reusing the query-address index from the prologue
+  // would keep a 64-bit register live across the whole loop
+  int hc = c;
+  __asm__ volatile("" : "+v"(hc));
   if (splits == 1) {
     dst = out + ((int64_t)r * H + h0) * kDv;
-    if (lse && g == 0) lse[(int64_t)r * H + h0 + c] = lse2 * kLn2;
+    if (lse && g == 0) lse[(int64_t)r * H + h0 + hc] = lse2 * kLn2;
   } else {
     const int64_t ph0 = ((int64_t)r * splits + split) * H + h0;
     dst = part_o + ph0 * kDv;
-    if (g == 0) part_lse[ph0 + c] = lse2;
+    if (g == 0) part_lse[ph0 + hc] = lse2;
   }
   // row j of the staged block = head h0 + j: 1024 bytes = 64 lanes x 16 B
 #pragma unroll
@@ -597,7 +633,8 @@ static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const Row
     attr_set = true;
   }
   mla_bf16_kernel<PAGED><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
-      rows, R, H, sl2, q16, kv8, idx, k, per, splits, o16, lse, part_o, part_lse);
+      R, splits, k, per, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
+      rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse);
   return hipGetLastError();
 }
 
