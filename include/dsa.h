@@ -182,6 +182,39 @@ int dsa_sparse_mla_prefill(const dsa_rows *rows, int dtype, int n_heads, int d_q
                            const int32_t *idx, int k, void *out, float *lse,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Stages 1-3 of a decode batch in one call ("DeepSeek-V3.2 技术报告摘要", section 1: the
+ * indexer, the fine-grained selection and MLA in MQA mode over the selected entries):
+ * exactly the logits and idx of dsa_indexer_topk(_paged) with (idx_dtype, idx_heads, idx_dim,
+ * q_idx, q_idx_scale, k_idx, k_idx_scale, w, topk), and the out / lse of
+ * dsa_sparse_mla_decode(_paged) with (dtype, n_heads, d_qk, d_v, softmax_scale, q, kv) on
+ * those idx, bit for bit.  For batches of few long rows with the bf16 attention the last step
+ * of the selection runs inside the attention workgroups (each split of a row selects the row's
+ * positions from the survivors of the chunked selection, keeps its own slots and writes them
+ * to idx), so the attention does not wait for a separate selection launch.
+ * Arguments, layouts and their limits are those of the two calls; topk is also the attention's k.
+ * ws / ws_bytes: device scratch of at least dsa_sparse_attention_decode_workspace_size(R,
+ * max_row_len, idx_dtype, topk, n_heads, d_v) bytes (may be NULL when that is 0); needs no
+ * initialisation; calls that share one workspace must not run concurrently.
+ * Errors: those of the two calls (DSA_ERR_UNSUPPORTED for an fp8 attention). */
+size_t dsa_sparse_attention_decode_workspace_size(int num_rows, int max_row_len, int idx_dtype,
+                                                  int topk, int n_heads, int d_v);
+int dsa_sparse_attention_decode(const dsa_rows *rows, int idx_dtype, int idx_heads, int idx_dim,
+                                const void *q_idx, const float *q_idx_scale, const void *k_idx,
+                                const float *k_idx_scale, const float *w, float *logits,
+                                int64_t ld_logits, int topk, int32_t *idx, int dtype, int n_heads,
+                                int d_qk, int d_v, float softmax_scale, const void *q,
+                                const void *kv, void *out, float *lse, void *ws, size_t ws_bytes,
+                                void *stream);
+int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int idx_heads,
+                                      int idx_dim, const void *q_idx, const float *q_idx_scale,
+                                      const void *k_idx, const float *k_idx_scale, const float *w,
+                                      float *logits, int64_t ld_logits, int topk, int32_t *idx,
+                                      int dtype, int n_heads, int d_qk, int d_v,
+                                      float softmax_scale, const void *q, const void *kv,
+                                      void *out, float *lse, void *ws, size_t ws_bytes,
+                                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

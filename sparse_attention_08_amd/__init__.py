@@ -75,6 +75,13 @@ def load_library() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [rows_p, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         f.restype = i32
+    lib.dsa_sparse_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.dsa_sparse_attention_decode_workspace_size.restype = sz
+    for name in ("dsa_sparse_attention_decode", "dsa_sparse_attention_decode_paged"):
+        f = getattr(lib, name)
+        f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i32, vp,
+                      i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = i32
     _lib = lib
     return lib
 
@@ -298,3 +305,55 @@ def sparse_mla_decode_paged(rows: Rows, q, kv, idx, scale: float, d_v: int, out=
 def sparse_mla_prefill(rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None):
     """Sparse MLA (MQA mode) for many query rows (prefill), contiguous latent cache."""
     return _mla("dsa_sparse_mla_prefill", rows, q, kv, idx, scale, d_v, out, lse, None)
+
+
+# --------------------------------------------------------------------------- stages 1 + 2 + 3
+
+def sparse_attention_decode_workspace_size(num_rows: int, max_row_len: int, idx_dtype, topk: int,
+                                           n_heads: int, d_v: int) -> int:
+    code = idx_dtype if isinstance(idx_dtype, int) else dtype_code(torch.empty(0, dtype=idx_dtype))
+    return int(load_library().dsa_sparse_attention_decode_workspace_size(
+        int(num_rows), int(max_row_len), code, int(topk), int(n_heads), int(d_v)))
+
+
+def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, kv, scale: float,
+                            d_v: int, idx=None, out=None, lse=None, q_scale=None, k_scale=None,
+                            ws=None):
+    """Indexer scores, their top-k and the sparse MLA over it, in one call (decode).
+
+    Fills ``logits`` and ``idx`` as :func:`indexer_topk` and returns ``out`` as
+    :func:`sparse_mla_decode` (``_paged`` for a paged ``rows``) would on that ``idx``.
+    """
+    lib = load_library()
+    for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (kv, "kv")):
+        _dev(t, n)
+    _dev(w, "w", (torch.float32,))
+    _dev(logits, "logits", (torch.float32,))
+    _dev(q, "q", (torch.float32, torch.bfloat16))
+    if q_scale is not None:
+        _dev(q_scale, "q_scale", (torch.float32,))
+    if k_scale is not None:
+        _dev(k_scale, "k_scale", (torch.float32,))
+    if q_idx.dim() != 3 or q.dim() != 3:
+        raise ValueError("q_idx must be [R, H_I, D_I] and q [R, H, d_qk]")
+    R, H, Dqk = (int(x) for x in q.shape)
+    if idx is None:
+        idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    _dev(idx, "idx", (torch.int32,))
+    if out is None:
+        out = torch.empty((R, H, d_v), dtype=q.dtype, device=q.device)
+    _dev(out, "out", (q.dtype,))
+    if lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    need = sparse_attention_decode_workspace_size(R, rows.max_row_len, dtype_code(q_idx), topk, H, d_v)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = rows.struct()
+    name = "dsa_sparse_attention_decode_paged" if rows.paged else "dsa_sparse_attention_decode"
+    s = getattr(lib, name)(
+        ctypes.byref(st), dtype_code(q_idx), int(q_idx.shape[1]), int(q_idx.shape[2]), _ptr(q_idx),
+        _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), _ptr(logits), int(logits.shape[-1]),
+        int(topk), _ptr(idx), dtype_code(q), H, Dqk, int(d_v), float(scale), _ptr(q), _ptr(kv),
+        _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check(s, name)
+    return out

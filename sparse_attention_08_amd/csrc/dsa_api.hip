@@ -149,6 +149,75 @@ int mla_common(const dsa_rows *rows, bool paged, MlaMode mode, int dtype, int n_
                                         splits, ws, s));
 }
 
+// Stages 1-3 of a decode batch.  Up to kSelectInAttentionRows long rows (batches whose
+// indexer feeds the top-k histograms) with the bf16 attention finish the selection inside
+// the attention workgroups; every other batch runs the two calls in turn.  Each split of a
+// row repeats the row's selection, which pays while the saved launch outweighs the longer
+// attention prologue (measured: 8 rows of 128K gain, 32 rows of up to 64K lose).
+constexpr int kSelectInAttentionRows = 16;
+bool decode_fusable(int num_rows, int max_row_len, int idx_dtype, int dtype) {
+  return dtype == DSA_BF16 && num_rows <= kSelectInAttentionRows &&
+         fused_hist_lists(num_rows, max_row_len, idx_dtype) > 0;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_ws(int num_rows, int max_row_len, int idx_dtype, int topk, int n_heads, int d_v) {
+  return align256(indexer_topk_ws(num_rows, max_row_len, idx_dtype, topk)) +
+         dsa::mla_workspace_bytes(num_rows, n_heads, d_v, topk);
+}
+
+int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int idx_heads,
+                            int idx_dim, const void *q_idx, const float *q_idx_scale,
+                            const void *k_idx, const float *k_idx_scale, const float *w,
+                            float *logits, int64_t ld_logits, int topk, int32_t *idx, int dtype,
+                            int n_heads, int d_qk, int d_v, float softmax_scale, const void *q,
+                            const void *kv, void *out, float *lse, void *ws, size_t ws_bytes,
+                            void *stream) {
+  int st = indexer_check(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
+                         k_idx_scale, w, logits, ld_logits);
+  if (st != DSA_OK) return st;
+  if (topk < 1 || topk > DSA_MAX_TOPK) return DSA_ERR_INVALID_ARG;
+  if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
+  if (n_heads <= 0 || d_qk <= 0 || d_v <= 0 || d_v > d_qk) return DSA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DSA_ERR_INVALID_ARG;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!idx || !q || !kv || !out) return DSA_ERR_INVALID_ARG;
+  if (dtype == DSA_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (dtype == DSA_F32 && (n_heads > 128 || d_qk > 256 || d_v > 256)) return DSA_ERR_UNSUPPORTED;
+  if (dtype == DSA_BF16 && (n_heads != 128 || d_qk != 576 || d_v != 512))
+    return DSA_ERR_UNSUPPORTED;
+  const int R = rows->num_rows, L = rows->max_row_len;
+  const size_t tk_bytes = align256(indexer_topk_ws(R, L, idx_dtype, topk));
+  const size_t need = decode_ws(R, L, idx_dtype, topk, n_heads, d_v);
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  void *tk_ws = tk_bytes ? wsb : nullptr;
+  void *ml_ws = need > tk_bytes ? wsb + tk_bytes : nullptr;
+  const size_t ml_bytes = need - tk_bytes;
+  if (!decode_fusable(R, L, idx_dtype, dtype)) {
+    st = indexer_topk_common(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
+                             k_idx_scale, w, logits, ld_logits, topk, idx, tk_ws, tk_bytes, stream);
+    if (st != DSA_OK) return st;
+    return mla_common(rows, paged, MlaMode::kDecode, dtype, n_heads, d_qk, d_v, softmax_scale, q,
+                      kv, idx, topk, out, lse, ml_ws, ml_bytes, stream);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nh = fused_hist_lists(R, L, idx_dtype);
+  const dsa::TopkHistDest dest = dsa::topk_hist_dest(tk_ws, R, L, nh);
+  hipError_t e = dsa::launch_indexer_mfma_hist(to_host(rows), paged, idx_dtype == DSA_FP8_E4M3,
+                                               q_idx, q_idx_scale, k_idx, k_idx_scale, w, logits,
+                                               ld_logits, dest, s);
+  if (e == hipSuccess)
+    e = dsa::launch_topk_filter_after_hist(logits, ld_logits, rows->row_len, R, L, topk, idx,
+                                           tk_ws, nh, s);
+  if (e == hipSuccess)
+    e = dsa::launch_mla_bf16_select(to_host(rows), paged, n_heads, softmax_scale, q, kv, idx, topk,
+                                    out, lse, dsa::mla_num_splits(R, n_heads, topk), ml_ws,
+                                    logits, ld_logits, tk_ws, nh, s);
+  return status_of(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +306,41 @@ int dsa_sparse_mla_decode_paged(const dsa_rows *rows, int dtype, int n_heads, in
                                 size_t ws_bytes, void *stream) {
   return mla_common(rows, true, MlaMode::kDecode, dtype, n_heads, d_qk, d_v, softmax_scale, q, kv,
                     idx, k, out, lse, ws, ws_bytes, stream);
+}
+
+size_t dsa_sparse_attention_decode_workspace_size(int num_rows, int max_row_len, int idx_dtype,
+                                                  int topk, int n_heads, int d_v) {
+  if (num_rows < 1 || max_row_len < 1 || topk < 1 || topk > DSA_MAX_TOPK || n_heads < 1 || d_v < 1)
+    return 0;
+  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3) return 0;
+  return decode_ws(num_rows, max_row_len, idx_dtype, topk, n_heads, d_v);
+}
+
+int dsa_sparse_attention_decode(const dsa_rows *rows, int idx_dtype, int idx_heads, int idx_dim,
+                                const void *q_idx, const float *q_idx_scale, const void *k_idx,
+                                const float *k_idx_scale, const float *w, float *logits,
+                                int64_t ld_logits, int topk, int32_t *idx, int dtype, int n_heads,
+                                int d_qk, int d_v, float softmax_scale, const void *q,
+                                const void *kv, void *out, float *lse, void *ws, size_t ws_bytes,
+                                void *stream) {
+  return attention_decode_common(rows, false, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale,
+                                 k_idx, k_idx_scale, w, logits, ld_logits, topk, idx, dtype,
+                                 n_heads, d_qk, d_v, softmax_scale, q, kv, out, lse, ws, ws_bytes,
+                                 stream);
+}
+
+int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int idx_heads,
+                                      int idx_dim, const void *q_idx, const float *q_idx_scale,
+                                      const void *k_idx, const float *k_idx_scale, const float *w,
+                                      float *logits, int64_t ld_logits, int topk, int32_t *idx,
+                                      int dtype, int n_heads, int d_qk, int d_v,
+                                      float softmax_scale, const void *q, const void *kv,
+                                      void *out, float *lse, void *ws, size_t ws_bytes,
+                                      void *stream) {
+  return attention_decode_common(rows, true, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale,
+                                 k_idx, k_idx_scale, w, logits, ld_logits, topk, idx, dtype,
+                                 n_heads, d_qk, d_v, softmax_scale, q, kv, out, lse, ws, ws_bytes,
+                                 stream);
 }
 
 int dsa_sparse_mla_prefill(const dsa_rows *rows, int dtype, int n_heads, int d_qk, int d_v,

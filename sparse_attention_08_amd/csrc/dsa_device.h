@@ -116,6 +116,20 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4 and 8
+// lanes inside each row of 16 (lanes shifted in from outside the row add 0), then row 0's
+// total is added to row 1 and row 2's to row 3 (broadcast of lane 15 of each row), then
+// the running total at lane 31 is added to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2, 3
+  return v;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
   return lane ? (~0ull >> (64 - lane)) : 0ull;

@@ -54,6 +54,11 @@ TopkHistDest topk_hist_dest(void *ws, int num_rows, int max_row_len, int hist_li
 hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
                                   int num_rows, int max_row_len, int k, int32_t *idx, void *ws,
                                   int hist_lists, hipStream_t stream);
+// Only the chunk filter of the above: its survivors are left in ws for the attention kernel
+// that finishes the selection (launch_mla_bf16_select); rows with row_len <= k are written.
+hipError_t launch_topk_filter_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                         int num_rows, int max_row_len, int k, int32_t *idx,
+                                         void *ws, int hist_lists, hipStream_t stream);
 hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,
                        int max_row_len, int k, int32_t *idx, void *ws, hipStream_t stream);
 
@@ -67,5 +72,11 @@ hipError_t launch_mla_f32(const RowsHost &rows, bool paged, int H, int Dqk, int 
 hipError_t launch_mla_bf16(const RowsHost &rows, bool paged, int H, float scale, const void *q,
                            const void *kv, const int32_t *idx, int k, void *out, float *lse,
                            int splits, void *ws, hipStream_t stream);
+// Same, finishing each row's top-k from the survivors that launch_topk_filter_after_hist left
+// in topk_ws (hist_lists as given to it) and writing it to idx.
+hipError_t launch_mla_bf16_select(const RowsHost &rows, bool paged, int H, float scale,
+                                  const void *q, const void *kv, int32_t *idx, int k, void *out,
+                                  float *lse, int splits, void *ws, const float *logits,
+                                  int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream);
 
 }  // namespace dsa

@@ -21,6 +21,7 @@
 // writes a normalised bf16 partial and its log-sum-exp, and a combine kernel merges them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "topk_select.h"
 
 namespace dsa {
 
@@ -248,6 +249,22 @@ __device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
   return c.r < R;
 }
 
+// Finishing the row's top-k inside the attention workgroups (see mla_bf16_kernel).
+struct MlaSel {
+  const float *logits;   // the score rows (fallback of degenerate rows)
+  int64_t ld;
+  MbWs ws;               // the chunked filter's survivors
+  int chunks;            // 4096-score chunks of the longest row
+};
+constexpr size_t kSelScratchBytes = (sizeof(BlockScratch<kMlaThreads>) + 15) & ~(size_t)15;
+constexpr size_t kSelKeyOff = kSelScratchBytes;
+constexpr size_t kSelPosOff = kSelKeyOff + sizeof(uint32_t) * kSurvivorCap;
+constexpr size_t kSelCoffOff = kSelPosOff + sizeof(int32_t) * kSurvivorCap;
+constexpr size_t kSelListOff =
+    (kSelCoffOff + sizeof(uint32_t) * (kMaxChunks + 1) + 15) & ~(size_t)15;
+static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing * kTileBytes,
+              "selection scratch fits the tile ring");
+
 // One workgroup: all 128 heads of query row r over one split of its top-k slots.
 // Wave w owns heads 16w .. 16w+15 over the full contractions.  Per tile of 32 entries it
 // forms S^T = C . Q^T (entries as MFMA rows, 2 blocks of 16 entries x its 16 heads, q in
@@ -255,16 +272,20 @@ __device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
 // value dims, V^T read from the same LDS tile with the transposing LDS read.  Entry rows
 // of the score blocks are permuted (block kb, row 4g + i <-> entry 8g + 4kb + i) so that
 // each lane's weights are exactly the B operand of the value product.
+// SEL: the row's top-k is not given but finished here, from the survivors of the chunked
+// top-k filter (every split of the row selects the row's k positions in its tile ring, which
+// is free until the first tile load, keeps its own slots and writes them to idx as well).
+//
 // The leading arguments are the ones the prologue needs first (scalars and pointers, so
 // the launch can preload them into registers).
-template <bool PAGED>
+template <bool PAGED, bool SEL>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
-    int R, int splits, int k, int slots_per_split, const int32_t *__restrict__ idx,
+    int R, int splits, int k, int slots_per_split, int32_t *__restrict__ idx,
     const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
     const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
     const uint8_t *__restrict__ kv, uint16_t *__restrict__ out, float *__restrict__ lse,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_lse) {
+    uint16_t *__restrict__ part_o, float *__restrict__ part_lse, MlaSel sel) {
   constexpr int H = kHeadsPerBlock;
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared &sh = *reinterpret_cast<MlaShared *>(mla_smem);
@@ -277,29 +298,55 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int h0 = wave * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
-  const int32_t *idx_row = idx + (int64_t)r * k + slot_begin;
+  int32_t *idx_row = idx + (int64_t)r * k + slot_begin;   // read, or written when SEL
 
   // cache rows of the valid slots, compacted in slot order
   int n_valid = 0;
   bf16x8 qf[18];
   {
-    // the slot loads go out first (they need only the launch arguments), then the row's
-    // descriptor loads and the query block: waits on vector memory are in issue order, so
-    // resolving the slots does not wait for the query block
     int sv[kSlotRounds];
-#pragma unroll
-    for (int j = 0; j < kSlotRounds; ++j) {
-      const int t = j * kMlaThreads + threadIdx.x;
-      sv[j] = t < n_slots ? idx_row[t] : -1;
-    }
-    __builtin_amdgcn_sched_barrier(0);
     // q^T operand: head h0 + c, dims 32t + 8g .. +8 (in flight during the slot resolution
     // and the first tile loads)
-    {
+    auto load_q = [&]() {
       const bf16x8 *qp =
           reinterpret_cast<const bf16x8 *>(q + ((int64_t)r * H + h0 + c) * kDqk + 8 * g);
 #pragma unroll
       for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
+    };
+    if constexpr (SEL) {
+      // the row's k positions, ascending, into the tile ring; slot j of the row is the j-th.
+      // The query loads go out after the selection, whose loads they would hold up.
+      const SurvivorLoads<kMlaThreads> sl = issue_survivor_loads<kMlaThreads>(sel.ws, r, sel.chunks);
+      const int n = row_len[r];
+      int32_t *lst = reinterpret_cast<int32_t *>(sh.tiles[0] + kSelListOff);
+      if (n > k) {
+        select_from_survivors<kMlaThreads>(
+            sl, sel.logits, sel.ld, sel.ws, r, n, k, lst,
+            *reinterpret_cast<BlockScratch<kMlaThreads> *>(sh.tiles[0]),
+            reinterpret_cast<uint32_t *>(sh.tiles[0] + kSelKeyOff),
+            reinterpret_cast<int32_t *>(sh.tiles[0] + kSelPosOff),
+            reinterpret_cast<uint32_t *>(sh.tiles[0] + kSelCoffOff));
+        __syncthreads();
+      }
+      load_q();
+#pragma unroll
+      for (int j = 0; j < kSlotRounds; ++j) {
+        const int t = j * kMlaThreads + threadIdx.x;
+        const int slot = slot_begin + t;
+        sv[j] = t < n_slots ? (n > k ? lst[slot] : (slot < n ? slot : -1)) : -1;
+        if (t < n_slots) idx_row[t] = sv[j];
+      }
+    } else {
+      // the slot loads go out first (they need only the launch arguments), then the query
+      // block, then the row's descriptor loads: waits on vector memory are in issue order,
+      // so resolving the slots does not wait for the query block
+#pragma unroll
+      for (int j = 0; j < kSlotRounds; ++j) {
+        const int t = j * kMlaThreads + threadIdx.x;
+        sv[j] = t < n_slots ? idx_row[t] : -1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_q();
     }
     __builtin_amdgcn_sched_barrier(0);
     const RowsDev rows{row_seq, row_len, seq_start, page_table, max_pages};
@@ -505,7 +552,12 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   lds_barrier();
 
   // ---- epilogue.  Lane (g, c) holds head h0 + c, dims 16nb + 4g + i.  The wave stages its
-  // 16 x 512 block in LDS (the ring is free now) and writes it with 16-byte stores.
+  // 16 x 512 block in LDS (the ring is free now) and writes it with 16-byte stores.  The
+  // lane-derived addresses are recomputed from an opaque copy of the lane id: values kept
+  // from the prologue would otherwise stay live across the whole loop.
+  int le = threadIdx.x & 63;
+  __asm__ volatile("" : "+v"(le));
+  const int ce = le & 15, ge = le >> 4;
   constexpr int kStageRow = kDv * 2 + 16;   // bytes per staged head row (padded)
   uint8_t *stage = sh.tiles[0] + wave * 16 * kStageRow;
   const float l_tot = sum_xor32(sum_xor16(l_part));
@@ -515,28 +567,24 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   for (int nb = 0; nb < 32; ++nb) {
     const uint32_t lo = pack_bf16x2(oacc[nb][0] * linv, oacc[nb][1] * linv);
     const uint32_t hi = pack_bf16x2(oacc[nb][2] * linv, oacc[nb][3] * linv);
-    *reinterpret_cast<uint2 *>(stage + c * kStageRow + (16 * nb + 4 * g) * 2) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2 *>(stage + ce * kStageRow + (16 * nb + 4 * ge) * 2) = make_uint2(lo, hi);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
   __builtin_amdgcn_wave_barrier();
   uint16_t *dst;
-  // the lane's head, recomputed here: reusing the query-address index from the prologue
-  // would keep a 64-bit register live across the whole loop
-  int hc = c;
-  __asm__ volatile("" : "+v"(hc));
   if (splits == 1) {
     dst = out + ((int64_t)r * H + h0) * kDv;
-    if (lse && g == 0) lse[(int64_t)r * H + h0 + hc] = lse2 * kLn2;
+    if (lse && ge == 0) lse[(int64_t)r * H + h0 + ce] = lse2 * kLn2;
   } else {
     const int64_t ph0 = ((int64_t)r * splits + split) * H + h0;
     dst = part_o + ph0 * kDv;
-    if (g == 0) part_lse[ph0 + hc] = lse2;
+    if (ge == 0) part_lse[ph0 + ce] = lse2;
   }
   // row j of the staged block = head h0 + j: 1024 bytes = 64 lanes x 16 B
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + j * kStageRow + lane * 16);
-    *reinterpret_cast<i32x4 *>(dst + (int64_t)j * kDv + lane * 8) = v;
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + j * kStageRow + le * 16);
+    *reinterpret_cast<i32x4 *>(dst + (int64_t)j * kDv + le * 8) = v;
   }
 }
 
@@ -619,28 +667,31 @@ size_t mla_workspace_bytes(int num_rows, int n_heads, int d_v, int k) {
   return (size_t)num_rows * splits * n_heads * (sizeof(uint16_t) * (size_t)d_v + sizeof(float));
 }
 
-template <bool PAGED>
+template <bool PAGED, bool SEL>
 static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const RowsDev &rows, int R,
-                                    int H, float sl2, const uint16_t *q16, const uint8_t *kv8,
-                                    const int32_t *idx, int k, int per, int splits, uint16_t *o16,
-                                    float *lse, uint16_t *part_o, float *part_lse) {
+                                    float sl2, const uint16_t *q16, const uint8_t *kv8,
+                                    int32_t *idx, int k, int per, int splits, uint16_t *o16,
+                                    float *lse, uint16_t *part_o, float *part_lse,
+                                    const MlaSel &sel) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mla_bf16_kernel<PAGED>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mla_bf16_kernel<PAGED, SEL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(MlaShared));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  mla_bf16_kernel<PAGED><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
+  mla_bf16_kernel<PAGED, SEL><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
       R, splits, k, per, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
-      rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse);
+      rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse, sel);
   return hipGetLastError();
 }
 
-hipError_t launch_mla_bf16(const RowsHost &rh, bool paged, int H, float scale, const void *q,
-                           const void *kv, const int32_t *idx, int k, void *out, float *lse,
-                           int splits, void *ws, hipStream_t stream) {
+// idx is read (sel == nullptr) or written: with sel the kernel finishes the row's top-k from
+// the chunked filter's survivors.
+static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale, const void *q,
+                              const void *kv, int32_t *idx, int k, void *out, float *lse,
+                              int splits, void *ws, const MlaSel *sel, hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
   const int per = (((k + splits - 1) / splits) + kTile - 1) / kTile * kTile;
   uint16_t *part_o = nullptr;
@@ -655,14 +706,41 @@ hipError_t launch_mla_bf16(const RowsHost &rh, bool paged, int H, float scale, c
   const uint8_t *kv8 = static_cast<const uint8_t *>(kv);
   uint16_t *o16 = static_cast<uint16_t *>(out);
   const float sl2 = scale * kLog2e;
-  hipError_t e = paged ? launch_mla_kernel<true>(grid, stream, rows, R, H, sl2, q16, kv8, idx, k,
-                                                 per, splits, o16, lse, part_o, part_lse)
-                       : launch_mla_kernel<false>(grid, stream, rows, R, H, sl2, q16, kv8, idx, k,
-                                                  per, splits, o16, lse, part_o, part_lse);
+  const MlaSel none{};
+  hipError_t e;
+  if (sel)
+    e = paged ? launch_mla_kernel<true, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
+                                              splits, o16, lse, part_o, part_lse, *sel)
+              : launch_mla_kernel<false, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
+                                               splits, o16, lse, part_o, part_lse, *sel);
+  else
+    e = paged ? launch_mla_kernel<true, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
+                                               splits, o16, lse, part_o, part_lse, none)
+              : launch_mla_kernel<false, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
+                                                splits, o16, lse, part_o, part_lse, none);
   if (e != hipSuccess || splits == 1) return e;
   mla_combine_kernel<<<8u * (unsigned)((R + 7) / 8) * (H / kCombHeads), 256, 0, stream>>>(
       R, H, splits, part_o, part_lse, o16, lse);
   return hipGetLastError();
+}
+
+hipError_t launch_mla_bf16(const RowsHost &rh, bool paged, int H, float scale, const void *q,
+                           const void *kv, const int32_t *idx, int k, void *out, float *lse,
+                           int splits, void *ws, hipStream_t stream) {
+  return launch_bf16(rh, paged, H, scale, q, kv, const_cast<int32_t *>(idx), k, out, lse, splits,
+                     ws, nullptr, stream);
+}
+
+hipError_t launch_mla_bf16_select(const RowsHost &rh, bool paged, int H, float scale,
+                                  const void *q, const void *kv, int32_t *idx, int k, void *out,
+                                  float *lse, int splits, void *ws, const float *logits,
+                                  int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream) {
+  MlaSel sel;
+  sel.logits = logits;
+  sel.ld = ld;
+  sel.ws = topk_chunk_ws(topk_ws, rh.num_rows, rh.max_row_len, hist_lists);
+  sel.chunks = (rh.max_row_len + kChunk - 1) / kChunk;
+  return launch_bf16(rh, paged, H, scale, q, kv, idx, k, out, lse, splits, ws, &sel, stream);
 }
 
 }  // namespace dsa

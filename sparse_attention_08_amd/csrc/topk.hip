@@ -22,12 +22,10 @@
 //        the remaining two digits of the exact select on them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "topk_select.h"
 
 namespace dsa {
 
-constexpr int kD0Bits = kLeadDigitBits, kD1Bits = 10, kD2Bits = 10;
-constexpr int kBins = 1 << kD0Bits;        // 4096
-constexpr int kChunk = 4096;               // scores per workgroup in the few-row schedule
 constexpr int kSmallThreads = 1024;
 #ifndef DSA_TOPK_FINAL_THREADS
 #define DSA_TOPK_FINAL_THREADS 1024
@@ -36,175 +34,6 @@ constexpr int kFinalThreads = DSA_TOPK_FINAL_THREADS;   // >= kMaxChunks
 static_assert(kFinalThreads >= 256 && (1 << 10) % kFinalThreads == 0, "final select shape");
 constexpr int kMbThreads = 256;
 constexpr int kStageElems = 28672;         // single-row schedule: up to 112 KB of staged keys
-constexpr int kSurvivorCap = 10240;        // survivors selected in LDS (80 KB)
-constexpr int kMaxChunks = 256;            // chunked schedule handles rows up to 1M scores
-constexpr int kListHead = 8;               // histogram entries per thread loaded with the counts
-constexpr int kSurvHead = 4;               // survivors per thread loaded with the chunk counts
-
-// ------------------------------------------------------------------------------------
-// block-wide helpers
-// ------------------------------------------------------------------------------------
-template <int NT>
-struct BlockScratch {
-  uint32_t hist[kBins];
-  uint32_t wsum[NT / kWave];
-  uint32_t wcnt[2][NT / kWave];
-  uint32_t prefix, mask;
-  int32_t need;
-  uint32_t flag;
-};
-
-// Exclusive prefix sum over the block's threads of v; returns it and the block total.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
-                                                    BlockScratch<NT> &sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += u;
-  }
-  if (lane == 63) sh.wsum[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) {
-    const uint32_t s = sh.wsum[w];
-    before += (w < wave) ? s : 0u;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return before + inc - v;
-}
-
-// One radix digit: histogram of digit (key >> shift) & (2^BITS - 1) over the keys that
-// match (key & mask) == prefix, then the digit holding the need-th largest key.
-template <int NT, int BITS, class Acc>
-__device__ void radix_digit(const Acc &acc, int n, int shift, BlockScratch<NT> &sh) {
-  constexpr int NB = 1 << BITS;
-  constexpr int PER = NB / NT;             // consecutive bins owned per thread
-  static_assert(NB % NT == 0, "bins must split evenly");
-  for (int i = threadIdx.x; i < NB; i += NT) sh.hist[i] = 0;
-  __syncthreads();
-  const uint32_t prefix = sh.prefix, mask = sh.mask;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t u = acc.key(i);
-    if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & (NB - 1)], 1u);
-  }
-  __syncthreads();
-  // thread t owns bins NB-1-PER*t-j (j < PER): descending digit order across threads
-  uint32_t c[PER], tot = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    c[j] = sh.hist[NB - 1 - PER * threadIdx.x - j];
-    tot += c[j];
-  }
-  uint32_t all;
-  const uint32_t before = block_excl_scan<NT>(tot, all, sh);
-  const int32_t need = sh.need;
-  __syncthreads();
-  if (before < (uint32_t)need && before + tot >= (uint32_t)need) {
-    uint32_t run = before;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (run + c[j] >= (uint32_t)need) {
-        const uint32_t digit = NB - 1 - PER * threadIdx.x - j;
-        sh.prefix = prefix | (digit << shift);
-        sh.mask = mask | ((uint32_t)(NB - 1) << shift);
-        sh.need = need - (int32_t)run;
-        break;
-      }
-      run += c[j];
-    }
-  }
-  __syncthreads();
-}
-
-// Exact top-k of n keys given by acc (key(i), pos(i); items in ascending position
-// order), written to out[0..k) in ascending position order.  Requires n > k.
-// When first_digit >= 0 the caller already knows the 12-bit digit of T and that
-// `need_in_digit` keys with that digit belong to the result.
-template <int NT, class Acc>
-__device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__ out,
-                             BlockScratch<NT> &sh, int first_digit = -1, int need_in_digit = 0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (threadIdx.x == 0) {
-    if (first_digit >= 0) {
-      sh.prefix = (uint32_t)first_digit << (kD1Bits + kD2Bits);
-      sh.mask = (uint32_t)(kBins - 1) << (kD1Bits + kD2Bits);
-      sh.need = need_in_digit;
-    } else {
-      sh.prefix = 0;
-      sh.mask = 0;
-      sh.need = k;
-    }
-  }
-  __syncthreads();
-  if (first_digit < 0) radix_digit<NT, kD0Bits>(acc, n, kD1Bits + kD2Bits, sh);
-  radix_digit<NT, kD1Bits>(acc, n, kD2Bits, sh);
-  radix_digit<NT, kD2Bits>(acc, n, 0, sh);
-  const uint32_t T = sh.prefix;
-  const int32_t need_eq = sh.need;
-  // ordered write: wave w owns a contiguous span; counts, wave offsets, then ballots
-  constexpr int NW = NT / kWave;
-  const int span = (((n + NW - 1) / NW) + 63) & ~63;
-  const int lo = wave * span, hi = min(n, lo + span);
-  uint32_t gt_cnt = 0, eq_cnt = 0;
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const uint32_t u = i < hi ? acc.key(i) : 0u;
-    gt_cnt += __popcll(__ballot(i < hi && u > T));
-    eq_cnt += __popcll(__ballot(i < hi && u == T));
-  }
-  if (lane == 0) {
-    sh.wcnt[0][wave] = gt_cnt;
-    sh.wcnt[1][wave] = eq_cnt;
-  }
-  __syncthreads();
-  uint32_t eq_before = 0, sel_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    const int32_t take = max(0, min((int32_t)sh.wcnt[1][w], need_eq - (int32_t)eq_before));
-    sel_before += sh.wcnt[0][w] + (uint32_t)take;
-    eq_before += sh.wcnt[1][w];
-  }
-  const uint64_t lt = lanemask_lt();
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const uint32_t u = i < hi ? acc.key(i) : 0u;
-    const bool gt = i < hi && u > T;
-    const bool eq = i < hi && u == T;
-    const uint64_t eq_mask = __ballot(eq);
-    const uint32_t eq_rank = eq_before + __popcll(eq_mask & lt);
-    const bool sel = gt || (eq && eq_rank < (uint32_t)need_eq);
-    const uint64_t sel_mask = __ballot(sel);
-    if (sel) out[sel_before + __popcll(sel_mask & lt)] = acc.pos(i);
-    eq_before += __popcll(eq_mask);
-    sel_before += __popcll(sel_mask);
-  }
-}
-
-struct RowAcc {            // keys computed on the fly from a score row in global memory
-  const float *row;
-  __device__ uint32_t key(int i) const { return order_key(row[i]); }
-  __device__ int32_t pos(int i) const { return i; }
-};
-struct StagedAcc {         // keys staged in LDS
-  const uint32_t *keys;
-  __device__ uint32_t key(int i) const { return keys[i]; }
-  __device__ int32_t pos(int i) const { return i; }
-};
-struct SurvivorAcc {       // (key, position) survivors staged in LDS
-  const uint32_t *keys;
-  const int32_t *posn;
-  __device__ uint32_t key(int i) const { return keys[i]; }
-  __device__ int32_t pos(int i) const { return posn[i]; }
-};
-
-__device__ __forceinline__ void write_all(int32_t *out, int n, int k) {
-  for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < n ? i : -1;
-}
 
 // ------------------------------------------------------------------------------------
 // many-row schedule: one workgroup per row
@@ -236,41 +65,6 @@ __global__ __launch_bounds__(kSmallThreads) void topk_row_kernel(const float *__
 // ------------------------------------------------------------------------------------
 // few-row schedule
 // ------------------------------------------------------------------------------------
-struct MbWs {
-  uint32_t *hcnt;     // [R][C]          nonzero bins per chunk histogram
-  uint32_t *hlist;    // [R][C][kBins]   (digit << 16 | count) of the nonzero bins
-  uint32_t *meta;     // [R][2]          b*, number of scores with digit > b*
-  uint32_t *scnt;     // [R][C]          survivors per chunk
-  uint2 *slist;       // [R][C][kChunk]  (key, position) survivors per chunk
-  int C;              // chunk stride of the arrays above
-  int nh;             // histogram lists per row; 0: one per 4096-score chunk of the row
-};
-
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-__host__ __device__ inline size_t mb_ws_bytes(int R, int C) {
-  return align256(sizeof(uint32_t) * (size_t)R * C) * 2 +
-         align256(sizeof(uint32_t) * (size_t)R * C * kBins) + align256(sizeof(uint32_t) * (size_t)R * 2) +
-         sizeof(uint2) * (size_t)R * C * kChunk;
-}
-
-__host__ __device__ inline MbWs carve_ws(void *ws, int R, int C) {
-  uint8_t *p = static_cast<uint8_t *>(ws);
-  MbWs w;
-  w.hcnt = reinterpret_cast<uint32_t *>(p);
-  p += align256(sizeof(uint32_t) * (size_t)R * C);
-  w.scnt = reinterpret_cast<uint32_t *>(p);
-  p += align256(sizeof(uint32_t) * (size_t)R * C);
-  w.hlist = reinterpret_cast<uint32_t *>(p);
-  p += align256(sizeof(uint32_t) * (size_t)R * C * kBins);
-  w.meta = reinterpret_cast<uint32_t *>(p);
-  p += align256(sizeof(uint32_t) * (size_t)R * 2);
-  w.slist = reinterpret_cast<uint2 *>(p);
-  w.C = C;
-  w.nh = 0;
-  return w;
-}
-
 // (1) per-chunk histogram of the 12-bit digit, compressed to its nonzero bins
 __global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(const float *__restrict__ logits,
                                                                int64_t ld,
@@ -307,12 +101,7 @@ __global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(const float *__re
   uint32_t nz = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) nz += lh[PER * threadIdx.x + j] ? 1u : 0u;
-  uint32_t inc = nz;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += u;
-  }
+  uint32_t inc = wave_incl_scan(nz);
   if (lane == 63) wtot[wave] = inc;
   __syncthreads();
   uint32_t off = inc - nz, total = 0;
@@ -327,18 +116,6 @@ __global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(const float *__re
     if (cnt) dst[off++] = (b << 16) | cnt;
   }
   if (threadIdx.x == 0) ws.hcnt[(size_t)r * ws.C + c] = total;
-}
-
-// Chunk j of the flattened list whose exclusive prefix offsets are off[0..nc] (off[nc] =
-// total): the last j with off[j] <= e.  Binary search over LDS.
-__device__ __forceinline__ int chunk_of(const uint32_t *off, int nc, uint32_t e) {
-  int lo = 0, hi = nc - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= e) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
 }
 
 // (2) merge the row's histograms, find b*, keep this chunk's survivors in position order.
@@ -407,12 +184,7 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
     cc[j] = lh[kBins - 1 - PER * threadIdx.x - j];
     tot += cc[j];
   }
-  uint32_t inc = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += u;
-  }
+  uint32_t inc = wave_incl_scan(tot);
   if (lane == 63) wtot[wave] = inc;
   __syncthreads();
   uint32_t before = inc - tot;
@@ -464,14 +236,14 @@ __global__ __launch_bounds__(kMbThreads) void topk_filter_kernel(const float *__
   if (threadIdx.x == 0) ws.scnt[(size_t)r * ws.C + c] = stotal;
 }
 
-// (3) one workgroup per row: exact select among the survivors, gathered with independent
-// loads (chunk of each survivor found from the prefix of the per-chunk counts)
+// (3) one workgroup per row: exact select among the survivors, gathered with the chunk
+// counts in one round of loads
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_final_kernel(const float *__restrict__ logits,
-                                                                   int64_t ld,
-                                                                   const int32_t *__restrict__ row_len,
-                                                                   int k, int32_t *__restrict__ idx,
-                                                                   MbWs ws) {
+                                                        int64_t ld,
+                                                        const int32_t *__restrict__ row_len,
+                                                        int k, int32_t *__restrict__ idx,
+                                                        MbWs ws) {
   __shared__ BlockScratch<NT> sh;
   __shared__ uint32_t skey[kSurvivorCap];
   __shared__ int32_t spos[kSurvivorCap];
@@ -479,54 +251,8 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(const float *__restrict_
   const int r = blockIdx.x;
   const int n = row_len[r];
   if (n <= k) return;
-  int32_t *out = idx + (int64_t)r * k;
-  const int nblk = (n + kChunk - 1) / kChunk;
-  const int bstar = (int)ws.meta[2 * r];
-  const int above = (int)ws.meta[2 * r + 1];
-  // survivor counts of the chunks and each chunk's first survivors in one round of loads:
-  // tpc threads per chunk (nblk <= kMaxChunks <= NT), kSurvHead survivors each
-  int tpc = NT;
-  while (tpc > 1 && tpc * nblk > NT) tpc >>= 1;
-  const int ch = threadIdx.x / tpc, sub = threadIdx.x % tpc;
-  const uint2 *cl = ws.slist + ((size_t)r * ws.C + ch) * kChunk;
-  uint32_t cnt = 0;
-  uint2 head[kSurvHead];
-  if (ch < nblk) {
-    cnt = ws.scnt[(size_t)r * ws.C + ch];
-#pragma unroll
-    for (int j = 0; j < kSurvHead; ++j) head[j] = cl[sub + tpc * j];   // within the chunk's list
-  }
-  {
-    uint32_t total;
-    const uint32_t before = block_excl_scan<NT>(sub == 0 ? cnt : 0u, total, sh);
-    if (sub == 0 && ch < nblk) coff[ch] = before;
-    if (threadIdx.x == 0) coff[nblk] = total;
-  }
-  __syncthreads();
-  const int M = (int)coff[nblk];
-  if (M <= kSurvivorCap) {
-    if (ch < nblk) {
-      const int dst = (int)coff[ch];
-#pragma unroll
-      for (int j = 0; j < kSurvHead; ++j) {
-        const uint32_t e = sub + tpc * j;
-        if (e < cnt) {
-          skey[dst + e] = head[j].x;
-          spos[dst + e] = (int32_t)head[j].y;
-        }
-      }
-      for (uint32_t e = tpc * kSurvHead + sub; e < cnt; e += tpc) {
-        const uint2 v = cl[e];
-        skey[dst + e] = v.x;
-        spos[dst + e] = (int32_t)v.y;
-      }
-    }
-    __syncthreads();
-    select_block<NT>(SurvivorAcc{skey, spos}, M, k, out, sh, bstar, k - above);
-  } else {
-    // degenerate score distributions (huge ties around the threshold): whole row
-    select_block<NT>(RowAcc{logits + (int64_t)r * ld}, n, k, out, sh, bstar, k - above);
-  }
+  const SurvivorLoads<NT> L = issue_survivor_loads<NT>(ws, r, (n + kChunk - 1) / kChunk);
+  select_from_survivors<NT>(L, logits, ld, ws, r, n, k, idx + (int64_t)r * k, sh, skey, spos, coff);
 }
 
 // ------------------------------------------------------------------------------------
@@ -558,14 +284,22 @@ TopkHistDest topk_hist_dest(void *ws, int num_rows, int max_row_len, int hist_li
   return TopkHistDest{w.hcnt, w.hlist, w.C};
 }
 
+hipError_t launch_topk_filter_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                         int num_rows, int max_row_len, int k, int32_t *idx,
+                                         void *ws, int hist_lists, hipStream_t stream) {
+  const MbWs w = topk_chunk_ws(ws, num_rows, max_row_len, hist_lists);
+  dim3 grid((max_row_len + kChunk - 1) / kChunk, num_rows);
+  topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
                                   int num_rows, int max_row_len, int k, int32_t *idx, void *ws,
                                   int hist_lists, hipStream_t stream) {
-  const int C = (max_row_len + kChunk - 1) / kChunk;
-  MbWs w = carve_ws(ws, num_rows, C > hist_lists ? C : hist_lists);
-  w.nh = hist_lists;
-  dim3 grid(C, num_rows);
-  topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  hipError_t e = launch_topk_filter_after_hist(logits, ld, row_len, num_rows, max_row_len, k, idx,
+                                               ws, hist_lists, stream);
+  if (e != hipSuccess) return e;
+  const MbWs w = topk_chunk_ws(ws, num_rows, max_row_len, hist_lists);
   topk_final_kernel<kFinalThreads><<<num_rows, kFinalThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
   return hipGetLastError();
 }

@@ -161,3 +161,34 @@ def test_workspace_queries_are_consistent():
     assert few % (8 * 128 * (2 * 512 + 4)) == 0
     assert dsa.sparse_mla_workspace_size(4096, 128, 512, 2048) == 0
     assert dsa.sparse_mla_workspace_size(0, 128, 512, 2048) == 0
+
+
+def test_attention_decode_validation(lib):
+    def call(rows, idx_dtype=1, topk=2048, dtype=1, H=128, Dqk=576, Dv=512, scale=0.07, ld=None,
+             ws=None, ws_bytes=0, qs=None, ks=None, ptrs=True, name="dsa_sparse_attention_decode"):
+        p = FAKE if ptrs else None
+        ld = rows.max_row_len if ld is None else ld
+        return getattr(lib, name)(ctypes.byref(rows), idx_dtype, 64, 128, FAKE, qs, FAKE, ks, FAKE,
+                                  FAKE, ld, topk, p, dtype, H, Dqk, Dv, scale, p, p, p, None, ws,
+                                  ws_bytes, None)
+    r = _rows()
+    assert call(r, topk=0) == INVALID
+    assert call(r, topk=2049) == INVALID
+    assert call(r, scale=0.0) == INVALID
+    assert call(r, scale=float("nan")) == INVALID
+    assert call(r, Dv=600) == INVALID
+    assert call(r, ptrs=False) == INVALID
+    assert call(r, ld=99) == INVALID
+    assert call(r, idx_dtype=2) == INVALID                      # fp8 indexer without scales
+    assert call(r, name="dsa_sparse_attention_decode_paged") == INVALID   # layout mismatch
+    assert call(r, dtype=2) == UNSUPPORTED                      # no fp8 attention
+    assert call(r, H=64) == UNSUPPORTED
+    assert call(_rows(num_rows=0)) == OK
+    # few long rows: the selection's and the attention's scratch live in one workspace
+    big = _rows(num_rows=8, num_seqs=8, max_row_len=131072)
+    need = dsa.sparse_attention_decode_workspace_size(8, 131072, 2, 2048, 128, 512)
+    assert need >= dsa.indexer_topk_workspace_size(8, 131072, 2, 2048) + \
+        dsa.sparse_mla_workspace_size(8, 128, 512, 2048)
+    assert call(big, idx_dtype=2, qs=FAKE, ks=FAKE) == WORKSPACE
+    assert call(big, idx_dtype=2, qs=FAKE, ks=FAKE, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    assert dsa.sparse_attention_decode_workspace_size(8, 131072, 7, 2048, 128, 512) == 0

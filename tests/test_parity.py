@@ -181,6 +181,59 @@ def test_fused_indexer_topk_other_schedules_and_full_size():
     _fused_vs_separate(wl)
 
 
+# ------------------------------------------------------------------------ fused decode (stages 1-3)
+
+def _attention_decode_vs_separate(wl):
+    """The one-call decode against the indexer+top-k call followed by the attention call."""
+    rows = dev_rows(wl)
+    R = wl.num_rows
+    logits_s = torch.full((R, wl.max_row_len), float("nan"), dtype=torch.float32, device=DEV)
+    idx_s = dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits_s, wl.topk, q_scale=wl.q_scale,
+                             k_scale=wl.k_scale)
+    lse_s = torch.empty((R, wl.H), dtype=torch.float32, device=DEV)
+    mla = dsa.sparse_mla_decode_paged if wl.paged else dsa.sparse_mla_decode
+    out_s = mla(rows, wl.q, wl.kv, idx_s, wl.scale, wl.D_v, lse=lse_s)
+    ws = torch.empty(max(dsa.sparse_attention_decode_workspace_size(
+        R, wl.max_row_len, wl.q_idx.dtype, wl.topk, wl.H, wl.D_v), 1), dtype=torch.uint8, device=DEV)
+    for call in range(2):   # the second call finds the workspace as the first left it
+        logits = torch.full_like(logits_s, float("nan"))
+        idx = torch.full_like(idx_s, -7)
+        lse = torch.full_like(lse_s, float("nan"))
+        out = dsa.sparse_attention_decode(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, wl.q,
+                                          wl.kv, wl.scale, wl.D_v, idx=idx, lse=lse,
+                                          q_scale=wl.q_scale, k_scale=wl.k_scale, ws=ws)
+        assert torch.equal(torch.nan_to_num(logits, nan=-1.0), torch.nan_to_num(logits_s, nan=-1.0))
+        assert torch.equal(idx, idx_s)
+        assert torch.equal(out, out_s)
+        assert torch.equal(lse, lse_s)
+    return logits_s, idx_s
+
+
+@pytest.mark.parametrize("idx_dtype,paged", [("bf16", False), ("fp8", False), ("bf16", True),
+                                             ("fp8", True)])
+def test_attention_decode_matches_separate_calls(idx_dtype, paged):
+    wl = workloads.decode(FUSED_LENS, idx_dtype=idx_dtype, paged=paged, seed=93, device=DEV,
+                          name=f"decode3_{idx_dtype}_{'paged' if paged else 'contig'}")
+    say(f"fused decode {wl.name}")
+    g, idx = _attention_decode_vs_separate(wl)
+    exp = oracle.topk(np.nan_to_num(g.cpu().numpy(), nan=0.0).astype(np.float32),
+                      wl.row_len.cpu().numpy(), wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), exp)
+
+
+def test_attention_decode_other_schedules_and_full_size():
+    # short rows: the call runs the indexer+top-k call and the attention call in turn
+    wl = workloads.decode(RAGGED, idx_dtype="bf16", seed=94, device=DEV, name="decode3_short")
+    say("fused decode short rows")
+    _attention_decode_vs_separate(wl)
+    for cfg in (4, 5):
+        wl = workloads.config(cfg, device=DEV)
+        say(f"fused decode config {cfg}")
+        _attention_decode_vs_separate(wl)
+        del wl
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------------ full-size configs
 
 @pytest.mark.parametrize("cfg,which", [(2, [0, 17, 63]), (4, [0, 5]), (5, [0, 1, 9, 31])])
