@@ -7,11 +7,12 @@ scales, top-2048, bf16 latent cache 576/512, 128 heads.
 
 Timing: inputs are resident in HBM; before every timed step a 1 GiB read evicts L2 and
 the Infinity Cache (outside the timed region), then HIP events on the launch stream
-bracket the step.  The timed step is one fused indexer + top-k call and the sparse MLA
-call, captured once in a HIP graph and replayed (--no-graph: eager launches; --separate:
-the indexer and the top-k as two calls); an eager pass with events between separate stage
-calls gives the per-stage attribution and the indexer's roofline.  value = rows (tokens) /
-mean step time.
+bracket the step.  For decode the timed step is one dsa_sparse_attention_decode call
+(indexer, top-k and sparse MLA), for prefill the indexer + top-k call and the attention
+call; the step is captured once in a HIP graph and replayed (--no-graph: eager launches;
+--separate: the indexer, the top-k and the attention as three calls).  An eager pass with
+events between separate stage calls gives the per-stage attribution and the indexer's
+roofline.  value = rows (tokens) / mean step time.
 
 Prints ONE JSON line.  --config selects another of the five workloads for diagnostics.
 """
@@ -56,8 +57,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches only (default: the step is captured in a HIP graph)")
     p.add_argument("--separate", action="store_true",
-                   help="timed step calls the indexer and the top-k separately (default: one "
-                        "fused indexer + top-k call)")
+                   help="timed step calls the indexer, the top-k and the attention separately "
+                        "(default: the one-call decode)")
     p.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
                    help="no GPU work: 'trace NAME STATS_CSV CMD' writes profiles/NAME.md from a "
                         "rocprofv3 --kernel-trace --stats run; 'pmc KERNEL FETCH_CSV WRITE_CSV "
@@ -257,6 +258,15 @@ def main():
     def stage_topk():
         dsa.topk(logits, wl.row_len, wl.topk, wl.max_row_len, idx=idx, ws=tk_ws)
 
+    dec_ws_n = 0 if prefill else dsa.sparse_attention_decode_workspace_size(
+        R, wl.max_row_len, wl.q_idx.dtype, wl.topk, wl.H, wl.D_v)
+    dec_ws = torch.empty(max(dec_ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def stage_decode():
+        dsa.sparse_attention_decode(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, wl.q, wl.kv,
+                                    wl.scale, wl.D_v, idx=idx, out=out, lse=lse,
+                                    q_scale=wl.q_scale, k_scale=wl.k_scale, ws=dec_ws)
+
     def stage_mla():
         if prefill:
             dsa.sparse_mla_prefill(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=lse)
@@ -272,14 +282,17 @@ def main():
     for _ in range(args.warmup):
         stage_indexer(); stage_topk(); stage_mla()
         stage_indexer_topk(); stage_mla()
+        if not prefill:
+            stage_decode()
     torch.cuda.synchronize()
 
     def step():
         if args.separate:
-            stage_indexer(); stage_topk()
+            stage_indexer(); stage_topk(); stage_mla()
+        elif prefill:
+            stage_indexer_topk(); stage_mla()
         else:
-            stage_indexer_topk()
-        stage_mla()
+            stage_decode()
 
     # eager launches, with per-stage attribution (indexer, top-k and MLA as separate calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -374,7 +387,9 @@ def main():
                  "hbm_frac_of_step": (idx_b + mla_b) / (mean * 1e-3) / (HBM_PEAK_GBS * 1e9),
                  "algorithmic_flops_per_step": idx_f + mla_f,
                  "launch_mode": mode,
-                 "indexer_topk": "separate calls" if args.separate else "fused call",
+                 "calls": ("indexer, top-k, attention" if args.separate else
+                           "indexer+top-k, attention" if prefill else
+                           "one call (dsa_sparse_attention_decode)"),
                  "eager_ms_per_step": statistics.fmean(eager_ms),
                  "stage_ms": {"indexer": idx_mean, "topk": statistics.fmean(topk_ms),
                               "sparse_mla": statistics.fmean(mla_ms)},
