@@ -52,6 +52,10 @@ int indexer_check(const dsa_rows *rows, bool paged, int dtype, int n_heads, int 
   return DSA_OK;
 }
 
+// Batches with at least this many rows per sequence on average (prefill) take the bf16
+// indexer whose workgroups share key tiles between 8 consecutive rows.
+constexpr int kPrefillRowsPerSeq = 8;
+
 hipError_t indexer_launch(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
                           const void *q, const float *q_scale, const void *k, const float *k_scale,
                           const float *w, float *logits, int64_t ld_logits, hipStream_t s) {
@@ -59,6 +63,8 @@ hipError_t indexer_launch(const dsa_rows *rows, bool paged, int dtype, int n_hea
   if (dtype == DSA_F32)
     return dsa::launch_indexer_f32(rh, paged, n_heads, head_dim, static_cast<const float *>(q),
                                    static_cast<const float *>(k), w, logits, ld_logits, s);
+  if (dtype == DSA_BF16 && rows->num_rows >= kPrefillRowsPerSeq * rows->num_seqs)
+    return dsa::launch_indexer_prefill(rh, paged, q, k, w, logits, ld_logits, s);
   return dsa::launch_indexer_mfma(rh, paged, dtype == DSA_FP8_E4M3, q, q_scale, k, k_scale, w,
                                   logits, ld_logits, s);
 }

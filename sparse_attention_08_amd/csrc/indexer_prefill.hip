@@ -1,0 +1,229 @@
+// indexer_prefill.hip -- lightning-indexer scores for prefill-shaped batches on gfx950
+// ("DeepSeek-V3.2 技术报告摘要", section 1, DSA ① Lightning Indexer:
+// I[t,s] = sum_j w[t,j] * ReLU(q[t,j,:] . k[s,:]) over the preceding tokens s).
+//
+// When many query rows belong to one sequence they all read the same keys, so the work is a
+// contraction with reuse on both sides (C3: 2.2 TFLOP over 4 MB of keys).  A workgroup takes
+// 8 consecutive query rows, one per wave, each wave holding its row's 64 x 128 query block
+// in registers as MFMA operands, and a chunk of 2048 keys of their sequence.  32-key tiles
+// are gathered once into an LDS ring (global->LDS loads, one 1 KB load per wave per tile)
+// and feed the MFMAs of all 8 rows: per 16 keys and row, 16 mfma_f32_16x16x32_bf16 (4 head
+// blocks x 4 K-steps), then ReLU, the head weights and the 64-head sum on the accumulators.
+// Rows of a workgroup that belong to different sequences are handled one sequence at a
+// time, so any ragged batch is computed correctly.
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+constexpr int kPfRows = 8;                     // query rows per workgroup, one per wave
+constexpr int kPfThreads = kPfRows * kWave;
+constexpr int kPfKeys = 64;                    // keys per LDS stage (one 64-token page)
+constexpr int kPfStages = 4;                   // ring depth: 3 stages in flight
+constexpr int kPfChunk = 2048;                 // keys per workgroup
+constexpr int kPfRowBytes = 128 * 2;           // one bf16 key
+constexpr int kPfStageBytes = kPfKeys * kPfRowBytes;
+constexpr int kPfLoads = kPfStageBytes / (kPfRows * 1024);   // 1 KB loads per wave per stage
+static_assert(kPfLoads * kPfRows * 1024 == kPfStageBytes, "whole 1 KB loads per wave");
+static_assert(kPfChunk % 64 == 0 && 64 % kPfKeys == 0, "a stage never crosses a 64-token page");
+static_assert(kPfStages >= 2 && kPfStages <= 4, "waits below cover at most two younger stages");
+
+// Global->LDS load of 16 bytes per lane (lane l lands at lds + 16 l), as an asm statement so
+// the compiler does not drain every pending load before LDS accesses it cannot disambiguate;
+// the instruction writes no register.  Keys are re-read by the other row blocks: no
+// non-temporal hint.
+__device__ __forceinline__ void pf_dma16(const void *g, void *lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+                   : "memory");
+}
+
+// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 field layout).
+constexpr int pf_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Waits until at most n (uniform, 0 .. kPfLoads (kPfStages - 2) + kPfStages - 1) of the
+// wave's vector-memory operations are pending.
+__device__ __forceinline__ void pf_wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(pf_vmcnt(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(pf_vmcnt(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(pf_vmcnt(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(pf_vmcnt(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(pf_vmcnt(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(pf_vmcnt(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(pf_vmcnt(6)); break;
+    default: __builtin_amdgcn_s_waitcnt(pf_vmcnt(7)); break;
+  }
+}
+static_assert(kPfLoads * (kPfStages - 2) + kPfStages - 1 <= 7, "pf_wait_vm range");
+
+// Four waves per SIMD (two workgroups per CU): the register budget is 128 per lane.
+template <bool PAGED>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+indexer_prefill_kernel(
+    int R, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_len,
+    const int64_t *__restrict__ seq_start, const int32_t *__restrict__ page_table, int max_pages,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
+    float *__restrict__ logits, int64_t ld, int n_chunks, int n_blocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kPfStages][kPfStageBytes];
+  __shared__ int s_seq[kPfRows], s_len[kPfRows];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  // Workgroups are dealt to the 8 XCDs round-robin by id.  Id -> (row block, chunk) so that
+  // XCD x takes row blocks x, x + 8, ... with all their chunks in turn (a balanced share of
+  // the causal triangle), row blocks in reverse order (rows near the end have the most keys
+  // and start first).
+  const int xcd = blockIdx.x & 7, m = blockIdx.x >> 3;
+  const int chunk = m % n_chunks;
+  const int rb = (m / n_chunks) * 8 + xcd;
+  if (rb >= n_blocks) return;
+  const int k0 = chunk * kPfChunk;
+  const int my_r = (n_blocks - 1 - rb) * kPfRows + wave;
+  const bool has_row = my_r < R;
+  const int my_len = has_row ? row_len[my_r] : 0;
+  if (lane == 0) {
+    s_seq[wave] = has_row ? row_seq[my_r] : -1;
+    s_len[wave] = my_len;
+  }
+  // the wave's query operands: head 16hb + c, 16-byte chunks 4g + t (the dims of the key
+  // chunks it reads), and the weights of the heads its accumulators hold (16hb + 4g + i)
+  i32x4 qf[4][4];
+  float wt[4][4];
+  if (my_len > k0) {
+    const i32x4 *qr = reinterpret_cast<const i32x4 *>(q + (int64_t)my_r * 64 * 128);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qf[hb][t] = qr[(16 * hb + c) * 16 + 4 * g + t];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wt[hb][i] = w[(int64_t)my_r * 64 + 16 * hb + 4 * g + i];
+  }
+  // this lane's 16 bytes of load i of a stage: key (kPfLoads wave + i) 4 + lane/16 of the
+  // stage, physical chunk lane % 16 holding logical chunk (lane % 16) ^ (key % 16)
+  // (conflict-free operand reads)
+  int dkey[kPfLoads], dbyte[kPfLoads];
+#pragma unroll
+  for (int i = 0; i < kPfLoads; ++i) {
+    dkey[i] = 4 * (kPfLoads * wave + i) + (lane >> 4);
+    dbyte[i] = 16 * ((lane & 15) ^ (dkey[i] & 15));
+  }
+  __syncthreads();
+
+  uint32_t done = 0;
+  for (;;) {
+    // the next sequence of the block: the first row not yet handled, and its rows
+    int b = -1, lmax = 0;
+    uint32_t act = 0;
+#pragma unroll
+    for (int i = 0; i < kPfRows; ++i) {
+      const int sq = s_seq[i];
+      if (sq >= 0 && !((done >> i) & 1u)) {
+        if (b < 0) b = sq;
+        if (sq == b) {
+          act |= 1u << i;
+          lmax = max(lmax, s_len[i]);
+        }
+      }
+    }
+    if (b < 0) break;
+    done |= act;
+    const int kend = min(k0 + kPfChunk, lmax);
+    if (kend <= k0) continue;
+    const bool mine = ((act >> wave) & 1u) && my_len > k0;
+    const int n_st = (kend - k0 + kPfKeys - 1) / kPfKeys;
+    int page_lane = 0;   // paged: lane j holds the page of the chunk's j-th 64 tokens
+    if constexpr (PAGED) {
+      const int pg = (k0 >> 6) + lane;
+      if (lane < kPfChunk / 64 && (pg << 6) < kend)
+        page_lane = page_table[(int64_t)b * max_pages + pg];
+    }
+    const int64_t base = PAGED ? 0 : seq_start[b];
+    auto issue = [&](int st) {
+#pragma unroll
+      for (int i = 0; i < kPfLoads; ++i) {
+        const int s = min(k0 + st * kPfKeys + dkey[i], kend - 1);   // tail keys re-read the last
+        int64_t row;
+        if constexpr (PAGED)
+          row = (int64_t)__builtin_amdgcn_readlane(page_lane, (st * kPfKeys) >> 6) * kPage + (s & 63);
+        else
+          row = base + s;
+        pf_dma16(reinterpret_cast<const uint8_t *>(k) + row * kPfRowBytes + dbyte[i],
+                 ring[st % kPfStages] + 1024 * (kPfLoads * wave + i));
+      }
+    };
+    for (int st = 0; st < kPfStages - 1 && st < n_st; ++st) issue(st);
+    float *out = logits + (int64_t)my_r * ld;
+    // score stores of the last kPfStages - 1 iterations (bit 0: the previous one): they were
+    // issued after this iteration's stage load, and stores count in vmcnt too
+    uint32_t st_bits = 0;
+    for (int j = 0; j < n_st; ++j) {
+      // this wave's part of stage j has landed once no more than its later stage loads (one
+      // per stage) and later stores are pending; vector memory completes in issue order
+      const int younger = kPfLoads * min(kPfStages - 2, n_st - 1 - j) + __popc(st_bits);
+      pf_wait_vm(younger);
+      // every wave's part of stage j is in, and every wave is done with stage j-1, whose
+      // slot the next load reuses
+      lds_barrier();
+      if (j + kPfStages - 1 < n_st) issue(j + kPfStages - 1);
+      const int s0 = k0 + j * kPfKeys;
+      if (mine && s0 < my_len) {
+        const uint8_t *slot = ring[j % kPfStages];
+        float v_mine = 0.f;
+#pragma unroll 1
+        for (int u = 0; u < kPfKeys / 16; ++u) {
+          const int kk = 16 * u + c;
+          i32x4 kf[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            kf[t] = *reinterpret_cast<const i32x4 *>(slot + kk * kPfRowBytes +
+                                                     16 * ((4 * g + t) ^ (kk & 15)));
+          f32x4 acc[4];
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, qf[hb][t]), __builtin_bit_cast(bf16x8, kf[t]),
+                  acc[hb], 0, 0, 0);
+          }
+          float v = 0.f;
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], relu(acc[hb][i]), v);
+          v = sum_xor32(sum_xor16(v));   // all 64 heads of key kk
+          if (g == u) v_mine = v;
+        }
+        const int s = s0 + lane;   // lane 16g + c holds key 16g + c of the stage
+        if (lane < kPfKeys && s < my_len) out[s] = v_mine;
+      }
+      const uint32_t stored = (mine && s0 < my_len) ? 1u : 0u;
+      st_bits = ((st_bits << 1) | stored) & ((1u << (kPfStages - 1)) - 1);
+    }
+    lds_barrier();   // the next sequence reuses the ring
+  }
+}
+
+hipError_t launch_indexer_prefill(const RowsHost &rh, bool paged, const void *q, const void *k,
+                                  const float *w, float *logits, int64_t ld, hipStream_t stream) {
+  const int n_chunks = (rh.max_row_len + kPfChunk - 1) / kPfChunk;
+  const int n_blocks = (rh.num_rows + kPfRows - 1) / kPfRows;
+  const unsigned grid = 8u * (unsigned)n_chunks * (unsigned)((n_blocks + 7) / 8);
+  const uint16_t *q16 = static_cast<const uint16_t *>(q);
+  const uint16_t *k16 = static_cast<const uint16_t *>(k);
+  if (paged)
+    indexer_prefill_kernel<true><<<grid, kPfThreads, 0, stream>>>(
+        rh.num_rows, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages, q16, k16,
+        w, logits, ld, n_chunks, n_blocks);
+  else
+    indexer_prefill_kernel<false><<<grid, kPfThreads, 0, stream>>>(
+        rh.num_rows, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages, q16, k16,
+        w, logits, ld, n_chunks, n_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

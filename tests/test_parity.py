@@ -130,6 +130,23 @@ def test_paged_physical_permutation_is_bit_identical():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+# ------------------------------------------------------------------------ prefill-shaped indexer
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_indexer_shares_key_tiles(paged):
+    """Batches with many rows per sequence take the indexer whose workgroups share key tiles
+    between 8 consecutive rows: blocks that straddle sequences, rows crossing the 2048-key
+    chunk boundary, and the first and last row of every sequence."""
+    lens = [13, 29, 2100]
+    wl = workloads.prefill_batch(lens, paged=paged, seed=95, device=DEV,
+                                 name=f"prefill_batch_{'paged' if paged else 'contig'}")
+    assert wl.num_rows >= 8 * wl.num_seqs
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    which = sorted(set(range(0, 42)) | {42, 43, 49, 50, 1000, 2047 + 42, 2048 + 42, 2049 + 42,
+                                        int(starts[-1]) - 2, int(starts[-1]) - 1})
+    _check_indexer(wl, which, TOL["bf16"])
+
+
 # ------------------------------------------------------------------------ fused indexer + top-k
 
 # few rows with a long maximum length: the indexer workgroups feed the selection directly

@@ -199,6 +199,45 @@ def prefill(L, *, idx_dtype="bf16", mla_dtype="bf16", H_I=64, D_I=128, H=128, D_
         page_size=PAGE, lens=[L], **vals)
 
 
+def prefill_batch(lens, *, idx_dtype="bf16", mla_dtype="bf16", paged=False, H_I=64, D_I=128,
+                  H=128, D_qk=576, D_v=512, topk=2048, scale=None, w_div=8.0, seed=0, device="cpu",
+                  name="prefill_batch") -> Workload:
+    """Several sequences prefilled together: every token of sequence b is a query row (in
+    sequence order), row t of b attending causally to positions 0..t of b."""
+    lens = [int(x) for x in lens]
+    if not lens or min(lens) < 1:
+        raise ValueError("every sequence needs at least one token")
+    B = len(lens)
+    R = sum(lens)
+    sgen = torch.Generator()
+    sgen.manual_seed(seed)
+    if paged:
+        npages = [math.ceil(n / PAGE) for n in lens]
+        P = sum(npages)
+        perm = torch.randperm(P, generator=sgen).to(torch.int32)
+        pt = torch.full((B, max(npages)), -1, dtype=torch.int32)
+        off = 0
+        for b, n in enumerate(npages):
+            pt[b, :n] = perm[off:off + n]
+            off += n
+        kshape, kvshape = (P, PAGE, D_I), (P, PAGE, D_qk)
+        seq_start = None
+    else:
+        seq_start = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64))
+        pt = None
+        kshape, kvshape = (R, D_I), (R, D_qk)
+    vals = _draw_values({"q_idx": (R, H_I, D_I), "k_idx": kshape, "q": (R, H, D_qk), "kv": kvshape},
+                        idx_dtype, mla_dtype, w_div, seed, device)
+    row_seq = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(lens)])
+    row_len = torch.cat([torch.arange(1, n + 1, dtype=torch.int32) for n in lens])
+    return Workload(
+        name=name, mode="prefill", idx_dtype=idx_dtype, mla_dtype=mla_dtype, H_I=H_I, D_I=D_I, H=H,
+        D_qk=D_qk, D_v=D_v, topk=topk, scale=scale if scale is not None else 1.0 / math.sqrt(192.0),
+        num_seqs=B, max_row_len=max(lens), row_seq=row_seq.to(device), row_len=row_len.to(device),
+        seq_start=None if seq_start is None else seq_start.to(device),
+        page_table=None if pt is None else pt.to(device), page_size=PAGE, lens=lens, **vals)
+
+
 def c5_lengths(seed: int, B: int = 32):
     """Mixed context lengths ~ U[1024, 65536]; sequences 0-1 redrawn from U[1024, 2047]."""
     g = torch.Generator()
