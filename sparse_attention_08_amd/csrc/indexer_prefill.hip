@@ -5,10 +5,12 @@
 // When many query rows belong to one sequence they all read the same keys, so the work is a
 // contraction with reuse on both sides (C3: 2.2 TFLOP over 4 MB of keys).  A workgroup takes
 // 8 consecutive query rows, one per wave, each wave holding its row's 64 x 128 query block
-// in registers as MFMA operands, and a chunk of 2048 keys of their sequence.  32-key tiles
-// are gathered once into an LDS ring (global->LDS loads, one 1 KB load per wave per tile)
-// and feed the MFMAs of all 8 rows: per 16 keys and row, 16 mfma_f32_16x16x32_bf16 (4 head
-// blocks x 4 K-steps), then ReLU, the head weights and the 64-head sum on the accumulators.
+// in registers as MFMA operands, and a chunk of 2048 keys of their sequence.  128-key tiles
+// (32 KB) are gathered once into a double-buffered LDS stage (global->LDS loads, four 1 KB
+// loads per wave per tile) and feed the MFMAs of all 8 rows: per 16 keys and row, 16
+// mfma_f32_16x16x32_bf16 (4 head blocks x 4 K-steps), then ReLU, the head weights and the
+// 64-head sum on the accumulators.  Measured on C3 (16K prefill): 2.07 ms against 2.9 ms for
+// the decode-shaped indexer; the clock runs at ~1.9 GHz under this load.
 // Rows of a workgroup that belong to different sequences are handled one sequence at a
 // time, so any ragged batch is computed correctly.
 #include "dsa_device.h"
@@ -18,15 +20,16 @@ namespace dsa {
 
 constexpr int kPfRows = 8;                     // query rows per workgroup, one per wave
 constexpr int kPfThreads = kPfRows * kWave;
-constexpr int kPfKeys = 64;                    // keys per LDS stage (one 64-token page)
-constexpr int kPfStages = 4;                   // ring depth: 3 stages in flight
+constexpr int kPfKeys = 128;                   // keys per LDS stage (two 64-token pages)
+constexpr int kPfStages = 2;                   // double buffer: one stage in flight
 constexpr int kPfChunk = 2048;                 // keys per workgroup
 constexpr int kPfRowBytes = 128 * 2;           // one bf16 key
 constexpr int kPfStageBytes = kPfKeys * kPfRowBytes;
 constexpr int kPfLoads = kPfStageBytes / (kPfRows * 1024);   // 1 KB loads per wave per stage
 static_assert(kPfLoads * kPfRows * 1024 == kPfStageBytes, "whole 1 KB loads per wave");
-static_assert(kPfChunk % 64 == 0 && 64 % kPfKeys == 0, "a stage never crosses a 64-token page");
-static_assert(kPfStages >= 2 && kPfStages <= 4, "waits below cover at most two younger stages");
+constexpr int kPfHalves = kPfKeys / 64;         // 64-key halves: score stores per stage
+static_assert(kPfKeys % 64 == 0 && kPfChunk % kPfKeys == 0, "stages are whole 64-token pages");
+static_assert(kPfStages >= 2 && kPfStages <= 4, "ring depth");
 
 // Global->LDS load of 16 bytes per lane (lane l lands at lds + 16 l), as an asm statement so
 // the compiler does not drain every pending load before LDS accesses it cannot disambiguate;
@@ -41,8 +44,8 @@ __device__ __forceinline__ void pf_dma16(const void *g, void *lds) {
 // s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 field layout).
 constexpr int pf_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// Waits until at most n (uniform, 0 .. kPfLoads (kPfStages - 2) + kPfStages - 1) of the
-// wave's vector-memory operations are pending.
+// Waits until at most n (uniform, 0 .. kPfLoads (kPfStages - 2) + kPfHalves (kPfStages - 1))
+// of the wave's vector-memory operations are pending.
 __device__ __forceinline__ void pf_wait_vm(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(pf_vmcnt(0)); break;
@@ -55,7 +58,7 @@ __device__ __forceinline__ void pf_wait_vm(int n) {
     default: __builtin_amdgcn_s_waitcnt(pf_vmcnt(7)); break;
   }
 }
-static_assert(kPfLoads * (kPfStages - 2) + kPfStages - 1 <= 7, "pf_wait_vm range");
+static_assert(kPfLoads * (kPfStages - 2) + kPfHalves * (kPfStages - 1) <= 7, "pf_wait_vm range");
 
 // Four waves per SIMD (two workgroups per CU): the register budget is 128 per lane.
 template <bool PAGED>
@@ -146,8 +149,9 @@ indexer_prefill_kernel(
       for (int i = 0; i < kPfLoads; ++i) {
         const int s = min(k0 + st * kPfKeys + dkey[i], kend - 1);   // tail keys re-read the last
         int64_t row;
-        if constexpr (PAGED)
-          row = (int64_t)__builtin_amdgcn_readlane(page_lane, (st * kPfKeys) >> 6) * kPage + (s & 63);
+        if constexpr (PAGED)   // the 4 keys of one load lie in one page
+          row = (int64_t)__builtin_amdgcn_readlane(
+                    page_lane, (st * kPfKeys + 4 * (kPfLoads * wave + i)) >> 6) * kPage + (s & 63);
         else
           row = base + s;
         pf_dma16(reinterpret_cast<const uint8_t *>(k) + row * kPfRowBytes + dbyte[i],
@@ -156,24 +160,31 @@ indexer_prefill_kernel(
     };
     for (int st = 0; st < kPfStages - 1 && st < n_st; ++st) issue(st);
     float *out = logits + (int64_t)my_r * ld;
-    // score stores of the last kPfStages - 1 iterations (bit 0: the previous one): they were
-    // issued after this iteration's stage load, and stores count in vmcnt too
-    uint32_t st_bits = 0;
+    // score stores of the last kPfStages - 1 iterations (4 bits each, the previous one lowest):
+    // they were issued after this iteration's stage load, and stores count in vmcnt too
+    uint32_t st_hist = 0;
     for (int j = 0; j < n_st; ++j) {
-      // this wave's part of stage j has landed once no more than its later stage loads (one
-      // per stage) and later stores are pending; vector memory completes in issue order
-      const int younger = kPfLoads * min(kPfStages - 2, n_st - 1 - j) + __popc(st_bits);
+      // this wave's part of stage j has landed once no more than its later stage loads and
+      // later stores are pending; vector memory completes in issue order
+      int pending_st = 0;
+#pragma unroll
+      for (int i = 0; i < kPfStages - 1; ++i) pending_st += (st_hist >> (4 * i)) & 15;
+      const int younger = kPfLoads * min(kPfStages - 2, n_st - 1 - j) + pending_st;
       pf_wait_vm(younger);
       // every wave's part of stage j is in, and every wave is done with stage j-1, whose
       // slot the next load reuses
       lds_barrier();
       if (j + kPfStages - 1 < n_st) issue(j + kPfStages - 1);
       const int s0 = k0 + j * kPfKeys;
+      uint32_t n_stores = 0;
       if (mine && s0 < my_len) {
         const uint8_t *slot = ring[j % kPfStages];
-        float v_mine = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < kPfHalves; ++hf) {
+         float v_mine = 0.f;
 #pragma unroll 1
-        for (int u = 0; u < kPfKeys / 16; ++u) {
+         for (int u4 = 0; u4 < 4; ++u4) {
+          const int u = 4 * hf + u4;
           const int kk = 16 * u + c;
           i32x4 kf[4];
 #pragma unroll
@@ -196,13 +207,14 @@ indexer_prefill_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], relu(acc[hb][i]), v);
           v = sum_xor32(sum_xor16(v));   // all 64 heads of key kk
-          if (g == u) v_mine = v;
+          if (g == u4) v_mine = v;
+         }
+         const int s = s0 + 64 * hf + lane;   // lane 16g + c holds key 16g + c of the half
+         if (s < my_len) out[s] = v_mine;
+         n_stores += (s0 + 64 * hf < my_len) ? 1u : 0u;   // lane 0 stores: the store issues
         }
-        const int s = s0 + lane;   // lane 16g + c holds key 16g + c of the stage
-        if (lane < kPfKeys && s < my_len) out[s] = v_mine;
       }
-      const uint32_t stored = (mine && s0 < my_len) ? 1u : 0u;
-      st_bits = ((st_bits << 1) | stored) & ((1u << (kPfStages - 1)) - 1);
+      st_hist = ((st_hist << 4) | n_stores) & ((1u << (4 * (kPfStages - 1))) - 1);
     }
     lds_barrier();   // the next sequence reuses the ring
   }
