@@ -167,7 +167,7 @@ int dsa_indexer_topk_paged(const dsa_rows *rows, int dtype, int n_heads, int hea
  *            bf16 with H = 128, d_qk = 576, d_v = 512.  1 <= k <= 2048.
  * The decode entry points split the selections over several workgroups for few-row
  * batches and need ws of dsa_sparse_mla_workspace_size(R, H, d_v, k) bytes;
- * dsa_sparse_mla_prefill never splits and takes ws = NULL, ws_bytes = 0. */
+ * dsa_sparse_mla_prefill(_paged) never splits and takes ws = NULL, ws_bytes = 0. */
 size_t dsa_sparse_mla_workspace_size(int num_rows, int n_heads, int d_v, int k);
 int dsa_sparse_mla_decode(const dsa_rows *rows, int dtype, int n_heads, int d_qk, int d_v,
                           float softmax_scale, const void *q, const void *kv,
@@ -181,6 +181,12 @@ int dsa_sparse_mla_prefill(const dsa_rows *rows, int dtype, int n_heads, int d_q
                            float softmax_scale, const void *q, const void *kv,
                            const int32_t *idx, int k, void *out, float *lse,
                            void *ws, size_t ws_bytes, void *stream);
+/* Prefill (or a chunk of prefill over a cached prefix) on the 64-token paged cache
+ * ("DeepSeek-V3.2" model docs, section 5.3: bf16 cache, page size 64). */
+int dsa_sparse_mla_prefill_paged(const dsa_rows *rows, int dtype, int n_heads, int d_qk,
+                                 int d_v, float softmax_scale, const void *q, const void *kv,
+                                 const int32_t *idx, int k, void *out, float *lse,
+                                 void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Stages 1-3 of a decode batch in one call ("DeepSeek-V3.2 技术报告摘要", section 1: the

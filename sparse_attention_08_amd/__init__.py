@@ -71,7 +71,8 @@ def load_library() -> ctypes.CDLL:
     lib.dsa_topk.restype = i32
     lib.dsa_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.dsa_sparse_mla_workspace_size.restype = sz
-    for name in ("dsa_sparse_mla_decode", "dsa_sparse_mla_decode_paged", "dsa_sparse_mla_prefill"):
+    for name in ("dsa_sparse_mla_decode", "dsa_sparse_mla_decode_paged", "dsa_sparse_mla_prefill",
+                 "dsa_sparse_mla_prefill_paged"):
         f = getattr(lib, name)
         f.argtypes = [rows_p, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         f.restype = i32
@@ -277,7 +278,7 @@ def _mla(name: str, rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, ls
     _dev(out, "out", (q.dtype,))
     if lse is not None:
         _dev(lse, "lse", (torch.float32,))
-    if name != "dsa_sparse_mla_prefill":
+    if not name.startswith("dsa_sparse_mla_prefill"):
         need = sparse_mla_workspace_size(R, H, d_v, k)
         if ws is None and need > 0:
             ws = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -305,6 +306,12 @@ def sparse_mla_decode_paged(rows: Rows, q, kv, idx, scale: float, d_v: int, out=
 def sparse_mla_prefill(rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None):
     """Sparse MLA (MQA mode) for many query rows (prefill), contiguous latent cache."""
     return _mla("dsa_sparse_mla_prefill", rows, q, kv, idx, scale, d_v, out, lse, None)
+
+
+def sparse_mla_prefill_paged(rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, lse=None):
+    """Sparse MLA (MQA mode) for many query rows (prefill or a chunk over a cached prefix),
+    64-token paged latent cache."""
+    return _mla("dsa_sparse_mla_prefill_paged", rows, q, kv, idx, scale, d_v, out, lse, None)
 
 
 # --------------------------------------------------------------------------- stages 1 + 2 + 3

@@ -4,6 +4,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "dsa_launch.h"
 
 namespace {
@@ -52,9 +54,18 @@ int indexer_check(const dsa_rows *rows, bool paged, int dtype, int n_heads, int 
   return DSA_OK;
 }
 
-// Batches with at least this many rows per sequence on average (prefill) take the bf16
-// indexer whose workgroups share key tiles between 8 consecutive rows.
-constexpr int kPrefillRowsPerSeq = 8;
+// bf16 batches with many rows per sequence (prefill, chunked prefill, multi-token decode)
+// take the indexer whose workgroups share key tiles between 8 consecutive rows: from 8 rows
+// per sequence on average, or from 4 over contexts of at most 32K.  Measured on MI355X
+// against the one-row-at-a-time indexer (whose key loads stay in cache when rows share
+// sequences): 8K contexts x 4 rows 39 vs 52 us, 128K x 4 rows 58 vs 51 us, 32K x 16 rows 80
+// vs 96 us, 128K x 2 rows 87 vs 53 us.  fp8 batches always take the one-row-at-a-time
+// indexer, which measured faster at every shape tried.
+bool shares_keys(const dsa_rows *rows, int dtype) {
+  if (dtype != DSA_BF16) return false;
+  const int64_t r = rows->num_rows, s = rows->num_seqs;
+  return r >= 8 * s || (r >= 4 * s && rows->max_row_len <= 32768);
+}
 
 hipError_t indexer_launch(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
                           const void *q, const float *q_scale, const void *k, const float *k_scale,
@@ -63,7 +74,7 @@ hipError_t indexer_launch(const dsa_rows *rows, bool paged, int dtype, int n_hea
   if (dtype == DSA_F32)
     return dsa::launch_indexer_f32(rh, paged, n_heads, head_dim, static_cast<const float *>(q),
                                    static_cast<const float *>(k), w, logits, ld_logits, s);
-  if (dtype == DSA_BF16 && rows->num_rows >= kPrefillRowsPerSeq * rows->num_seqs)
+  if (shares_keys(rows, dtype))
     return dsa::launch_indexer_prefill(rh, paged, q, k, w, logits, ld_logits, s);
   return dsa::launch_indexer_mfma(rh, paged, dtype == DSA_FP8_E4M3, q, q_scale, k, k_scale, w,
                                   logits, ld_logits, s);
@@ -79,18 +90,25 @@ int indexer_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int
                                   logits, ld_logits, static_cast<hipStream_t>(stream)));
 }
 
-// Histogram lists per row when the indexer workgroups feed the top-k directly, or 0 when the
-// batch takes the separate path (f32 indexer, or the one-workgroup-per-row top-k schedule).
-int fused_hist_lists(int num_rows, int max_row_len, int dtype) {
+// Histogram lists per row when the per-row indexer's workgroups feed the top-k directly, or 0
+// when the batch takes the separate path (f32 indexer, the one-workgroup-per-row top-k
+// schedule, or the shared-key indexer).
+int hist_lists_of_shape(int num_rows, int max_row_len, int dtype) {
   if (dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return 0;
   const int nh = dsa::indexer_blocks_per_row(num_rows, max_row_len, dtype == DSA_FP8_E4M3);
   return dsa::topk_hist_fusable(num_rows, max_row_len, nh) ? nh : 0;
 }
+int fused_hist_lists(const dsa_rows *rows, int dtype) {
+  if (shares_keys(rows, dtype)) return 0;
+  return hist_lists_of_shape(rows->num_rows, rows->max_row_len, dtype);
+}
 
+// Workspace of the indexer + top-k for any batch of this shape: the size queries do not see
+// the number of sequences, so this covers both the fused and the separate top-k.
 size_t indexer_topk_ws(int num_rows, int max_row_len, int dtype, int k) {
-  const int nh = fused_hist_lists(num_rows, max_row_len, dtype);
-  return nh ? dsa::topk_fused_workspace_bytes(num_rows, max_row_len, nh)
-            : dsa::topk_workspace_bytes(num_rows, max_row_len, k);
+  const size_t sep = dsa::topk_workspace_bytes(num_rows, max_row_len, k);
+  const int nh = hist_lists_of_shape(num_rows, max_row_len, dtype);
+  return nh ? std::max(sep, dsa::topk_fused_workspace_bytes(num_rows, max_row_len, nh)) : sep;
 }
 
 int indexer_topk_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
@@ -107,7 +125,7 @@ int indexer_topk_common(const dsa_rows *rows, bool paged, int dtype, int n_heads
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = rows->num_rows, L = rows->max_row_len;
-  const int nh = fused_hist_lists(R, L, dtype);
+  const int nh = fused_hist_lists(rows, dtype);
   if (nh) {
     const dsa::TopkHistDest dest = dsa::topk_hist_dest(ws, R, L, nh);
     hipError_t e = dsa::launch_indexer_mfma_hist(to_host(rows), paged, dtype == DSA_FP8_E4M3, q,
@@ -161,9 +179,9 @@ int mla_common(const dsa_rows *rows, bool paged, MlaMode mode, int dtype, int n_
 // row repeats the row's selection, which pays while the saved launch outweighs the longer
 // attention prologue (measured: 8 rows of 128K gain, 32 rows of up to 64K lose).
 constexpr int kSelectInAttentionRows = 16;
-bool decode_fusable(int num_rows, int max_row_len, int idx_dtype, int dtype) {
-  return dtype == DSA_BF16 && num_rows <= kSelectInAttentionRows &&
-         fused_hist_lists(num_rows, max_row_len, idx_dtype) > 0;
+bool decode_fusable(const dsa_rows *rows, int idx_dtype, int dtype) {
+  return dtype == DSA_BF16 && rows->num_rows <= kSelectInAttentionRows &&
+         fused_hist_lists(rows, idx_dtype) > 0;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -201,7 +219,7 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
   void *tk_ws = tk_bytes ? wsb : nullptr;
   void *ml_ws = need > tk_bytes ? wsb + tk_bytes : nullptr;
   const size_t ml_bytes = need - tk_bytes;
-  if (!decode_fusable(R, L, idx_dtype, dtype)) {
+  if (!decode_fusable(rows, idx_dtype, dtype)) {
     st = indexer_topk_common(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
                              k_idx_scale, w, logits, ld_logits, topk, idx, tk_ws, tk_bytes, stream);
     if (st != DSA_OK) return st;
@@ -209,7 +227,7 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
                       kv, idx, topk, out, lse, ml_ws, ml_bytes, stream);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nh = fused_hist_lists(R, L, idx_dtype);
+  const int nh = fused_hist_lists(rows, idx_dtype);
   const dsa::TopkHistDest dest = dsa::topk_hist_dest(tk_ws, R, L, nh);
   hipError_t e = dsa::launch_indexer_mfma_hist(to_host(rows), paged, idx_dtype == DSA_FP8_E4M3,
                                                q_idx, q_idx_scale, k_idx, k_idx_scale, w, logits,
@@ -355,6 +373,16 @@ int dsa_sparse_mla_prefill(const dsa_rows *rows, int dtype, int n_heads, int d_q
   (void)ws;
   (void)ws_bytes;
   return mla_common(rows, false, MlaMode::kPrefill, dtype, n_heads, d_qk, d_v, softmax_scale, q,
+                    kv, idx, k, out, lse, nullptr, 0, stream);
+}
+
+int dsa_sparse_mla_prefill_paged(const dsa_rows *rows, int dtype, int n_heads, int d_qk, int d_v,
+                                 float softmax_scale, const void *q, const void *kv,
+                                 const int32_t *idx, int k, void *out, float *lse, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return mla_common(rows, true, MlaMode::kPrefill, dtype, n_heads, d_qk, d_v, softmax_scale, q,
                     kv, idx, k, out, lse, nullptr, 0, stream);
 }
 

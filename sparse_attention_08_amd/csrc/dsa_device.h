@@ -53,6 +53,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// Weighted sum over the 64 indexer heads of a 16-key score tile, on the matrix cores.
+// The tile's scores are the four 16x16 head blocks of an MFMA result: lane (g, c) holds
+// S[16 hb + 4g + i][key c] in acc[hb][i].  Two head blocks at a time, ReLU'd and rounded to
+// bf16, form the B operand (K = 32 heads) of a 16x16x32 bf16 MFMA whose A operand holds the
+// matching head weights in every row; each output row is then sum_h w[h] relu(S[h][c]), so
+// every lane (g, c) receives the score of key c, accumulated in fp32.  Lane group g's K
+// slots hold its own heads 16 hb + 4g + i in both operands, so the weights of a lane are
+// the ones it already holds.  Against an fp32 epilogue this rounds each weighted term's
+// two factors to bf16 (relative 2^-9 each) and replaces 32 VALU operations per tile by
+// 16 and two MFMAs.
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+struct HeadWeights {
+  bf16x8 a[2];   // A operands: heads of blocks {0, 1} and {2, 3}
+};
+// ReLU of two floats as a packed bf16 pair: one conversion and a packed signed 16-bit max
+// on the bits (negative values and -0 compare below 0).
+__device__ __forceinline__ uint32_t relu_bf16x2(float a, float b) {
+  i16x2 v = __builtin_bit_cast(i16x2, __builtin_convertvector((f32x2{a, b}), bf16x2));
+  v = __builtin_elementwise_max(v, (i16x2){0, 0});
+  return __builtin_bit_cast(uint32_t, v);
+}
+// wt[hb][i]: the weight of head 16 hb + 4g + i (g = lane / 16); element j of a[p] is head
+// block 2p + j / 4, row j % 4
+__device__ __forceinline__ HeadWeights head_weights(const float (&wt)[4][4]) {
+  HeadWeights hw;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const i32x4 v = {(int)pack_bf16x2(wt[2 * p][0], wt[2 * p][1]),
+                     (int)pack_bf16x2(wt[2 * p][2], wt[2 * p][3]),
+                     (int)pack_bf16x2(wt[2 * p + 1][0], wt[2 * p + 1][1]),
+                     (int)pack_bf16x2(wt[2 * p + 1][2], wt[2 * p + 1][3])};
+    hw.a[p] = __builtin_bit_cast(bf16x8, v);
+  }
+  return hw;
+}
+__device__ __forceinline__ float head_sum(const f32x4 (&acc)[4], const HeadWeights &hw) {
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const i32x4 b = {(int)relu_bf16x2(acc[2 * p][0], acc[2 * p][1]),
+                     (int)relu_bf16x2(acc[2 * p][2], acc[2 * p][3]),
+                     (int)relu_bf16x2(acc[2 * p + 1][0], acc[2 * p + 1][1]),
+                     (int)relu_bf16x2(acc[2 * p + 1][2], acc[2 * p + 1][3])};
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hw.a[p], __builtin_bit_cast(bf16x8, b), d, 0, 0, 0);
+  }
+  return d[0];
+}
+
 // Leading radix digit of the top-k select: sign, exponent and 3 mantissa bits of the key.
 constexpr int kLeadDigitBits = 12;
 constexpr int kLeadBins = 1 << kLeadDigitBits;
@@ -65,8 +113,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// max(x, 0) as a signed-integer max on the bits: negative floats (and -0) have the sign
-// bit set and compare below 0, so this is ReLU in one instruction (no NaN quieting).
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every vector
 // memory operation of the wave (vmcnt(0)), which would drain global->LDS loads that are
 // meant to stay in flight across the barrier; here only LDS operations (lgkmcnt) are
@@ -79,6 +125,8 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// max(x, 0) as a signed-integer max on the bits: negative floats (and -0) have the sign
+// bit set and compare below 0, so this is ReLU in one instruction (no NaN quieting).
 __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }

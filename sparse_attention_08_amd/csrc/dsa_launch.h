@@ -27,8 +27,8 @@ hipError_t launch_indexer_f32(const RowsHost &rows, bool paged, int H, int D, co
 hipError_t launch_indexer_mfma(const RowsHost &rows, bool paged, bool fp8, const void *q,
                                const float *q_scale, const void *k, const float *k_scale,
                                const float *w, float *logits, int64_t ld, hipStream_t stream);
-// bf16, 64 heads x 128 dims, for batches with many rows per sequence (prefill): workgroups
-// of 8 consecutive rows share each key tile.
+// bf16, 64 heads x 128 dims, for batches with many rows per sequence (prefill, chunked
+// prefill, multi-token decode): workgroups of 8 consecutive rows share each key tile.
 hipError_t launch_indexer_prefill(const RowsHost &rows, bool paged, const void *q, const void *k,
                                   const float *w, float *logits, int64_t ld, hipStream_t stream);
 // Workgroups per row of the MFMA indexer grid for this batch shape.

@@ -72,8 +72,9 @@ hipError_t launch_indexer_f32(const RowsHost &rh, bool paged, int H, int D, cons
 // contraction is the plain dot product.
 //   bf16: 4 x v_mfma_f32_16x16x32_bf16 per head block (K = 32 each)
 //   fp8 : 1 x v_mfma_scale_f32_16x16x128_f8f6f4 per head block (K = 128, unit scales)
-// Epilogue per key: v = sum_{hb,i} w'[head] * max(acc, 0) over the lane's 16 heads,
-// then a 4-lane sum across g; fp8 multiplies by the key's scale, and w' = w * q_scale.
+// Epilogue per tile: ReLU and the head weights w' (w' = w * q_scale for fp8) summed over
+// the 64 heads by two bf16 MFMAs with the weights as the A operand (head_sum); fp8 then
+// multiplies by the key's scale.
 // ------------------------------------------------------------------------------------
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
@@ -143,7 +144,13 @@ typedef void __attribute__((address_space(3))) *lds_void_ptr;
 constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Global->LDS loads of 16 (keys) and 4 (fp8 scales) bytes per lane: lane l lands at
-// lds + l * size.  Keys are streamed once, so the key loads carry the non-temporal hint.
+// lds + l * size.  When every row has a sequence of its own, each key is read once and the
+// key loads carry the non-temporal hint, which keeps the scores and the attention's cache
+// lines in L2 and the Infinity Cache for the later stages (measured: plain loads cost 3 to
+// 10 us per decode step).  When rows share sequences (several query tokens per sequence)
+// the key loads are plain: rows of one sequence read the same keys at about the same time
+// from workgroups on the same XCD, and the later reads hit in L2 (measured: two rows per
+// sequence then cost about as much as one).
 // Written as two-instruction asm statements rather than the builtin: the compiler treats
 // every LDS write it cannot disambiguate from a pending global->LDS load as aliasing it
 // and would wait for all of them first (draining the rings).  The instructions write no
@@ -152,9 +159,16 @@ constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0
 __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
 }
+template <bool NT>
 __device__ __forceinline__ void dma16(const void *g, void *lds) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds_addr(lds))
-                   : "memory");
+  if constexpr (NT)
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g),
+                     "s"(lds_addr(lds))
+                     : "memory");
+  else
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                     "s"(lds_addr(lds))
+                     : "memory");
 }
 __device__ __forceinline__ void dma4(const void *g, void *lds) {
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
@@ -184,26 +198,35 @@ struct DmaLane {
 // base_row: contiguous layout, cache row of position 0; paged layout: page holds the cache
 // page of the group (a group never crosses a 64-token page).  Keys past s_last (the row's
 // last position) re-read s_last, which stays in cache.
-template <bool FP8, bool PAGED>
-__device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__restrict__ k,
-                                            const float *__restrict__ k_scale, int64_t base_row,
-                                            int page, int64_t s0, int64_t s_last,
-                                            const DmaLane<FP8> &dl, int lane) {
+template <bool FP8, bool PAGED, bool NT>
+__device__ __forceinline__ void issue_group_loads(uint8_t *slot, const uint8_t *__restrict__ k,
+                                                  const float *__restrict__ k_scale, int64_t row0,
+                                                  int last, const DmaLane<FP8> &dl, int lane) {
   using C = IdxCfg<FP8>;
-  const int64_t row0 = PAGED ? (int64_t)page * kPage + (s0 & 63) : base_row + s0;
   const uint8_t *gbase = k + row0 * C::kRowBytes;
-  const int last = (int)min<int64_t>(s_last - s0, C::kKeys - 1);   // last valid key offset
   if (last == C::kKeys - 1) {            // the whole group lies inside the row
 #pragma unroll
-    for (int j = 0; j < DmaLane<FP8>::kJ; ++j) dma16(gbase + dl.byte[j], slot + 1024 * j);
+    for (int j = 0; j < DmaLane<FP8>::kJ; ++j) dma16<NT>(gbase + dl.byte[j], slot + 1024 * j);
     if constexpr (FP8) dma4(k_scale + row0 + min(lane, C::kKeys - 1), slot + kGroupBytes);
   } else {
 #pragma unroll
     for (int j = 0; j < DmaLane<FP8>::kJ; ++j)
-      dma16(gbase + dl.byte[j] + (min(dl.key[j], last) - dl.key[j]) * C::kRowBytes,
-            slot + 1024 * j);
+      dma16<NT>(gbase + dl.byte[j] + (min(dl.key[j], last) - dl.key[j]) * C::kRowBytes,
+                slot + 1024 * j);
     if constexpr (FP8) dma4(k_scale + row0 + min(lane, last), slot + kGroupBytes);
   }
+}
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__restrict__ k,
+                                            const float *__restrict__ k_scale, int64_t base_row,
+                                            int page, int64_t s0, int64_t s_last,
+                                            const DmaLane<FP8> &dl, int lane, bool cached) {
+  const int64_t row0 = PAGED ? (int64_t)page * kPage + (s0 & 63) : base_row + s0;
+  const int last = min((int)(s_last - s0), IdxCfg<FP8>::kKeys - 1);   // last valid key offset
+  if (cached)
+    issue_group_loads<FP8, PAGED, false>(slot, k, k_scale, row0, last, dl, lane);
+  else
+    issue_group_loads<FP8, PAGED, true>(slot, k, k_scale, row0, last, dl, lane);
 }
 
 // MFMA + fused epilogue for the group in `slot`; returns in lane (g, c) the score of key
@@ -211,7 +234,7 @@ __device__ __forceinline__ void issue_group(uint8_t *slot, const uint8_t *__rest
 template <bool FP8>
 __device__ __forceinline__ float consume_group(const uint8_t *slot,
                                                const i32x4 (&qf)[4][IdxCfg<FP8>::kChunks],
-                                               const float (&wt)[4][4], int lane) {
+                                               const HeadWeights &hw, int lane) {
   using C = IdxCfg<FP8>;
   const int c = lane & 15, g = lane >> 4;
   float mine = 0.f;
@@ -240,12 +263,7 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
                                                             acc[hb], 0, 0, 0);
       }
     }
-    float v = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], relu(acc[hb][i]), v);
-    v = sum_xor32(sum_xor16(v));   // sum over the 4 lane rows: all 64 heads
+    const float v = head_sum(acc, hw);   // all 64 heads of key c, in every lane (., c)
     if (g == u) mine = v;
   }
   if constexpr (FP8) mine *= reinterpret_cast<const float *>(slot + kGroupBytes)[lane];
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kern
     RowsDev rows, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, const float *__restrict__ w,
     float *__restrict__ logits, int64_t ld, uint32_t *__restrict__ hcnt,
-    uint32_t *__restrict__ hlist, int hstride) {
+    uint32_t *__restrict__ hlist, int hstride, int cached) {
   using C = IdxCfg<FP8>;
   constexpr int kQChunks = kIdxHeads * C::kRowBytes / 16;
   constexpr int kThreads = C::kWaves * kWave;
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kern
     const int n_pro = min(C::kDepth - 1, n_groups);
     for (int d = 0; d < n_pro; ++d)
       issue_group<FP8, PAGED>(ring + d * C::kSlotBytes, k, k_scale, base_row, group_page(d),
-                              group_start(d), s_last, dl, lane);
+                              group_start(d), s_last, dl, lane, cached);
   }
   if constexpr (HIST)
     for (int i = threadIdx.x; i < kLeadBins; i += kThreads) hist[i] = 0;
@@ -335,19 +353,20 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kern
         const int64_t hj = (int64_t)r * kIdxHeads + hb * 16 + 4 * g + i;
         wt[hb][i] = FP8 ? w[hj] * q_scale[hj] : w[hj];
       }
+    const HeadWeights hw = head_weights(wt);
     float *out = logits + (int64_t)r * ld;
     for (int i = 0; i < n_groups; ++i) {
       if (i + C::kDepth - 1 < n_groups) {
         issue_group<FP8, PAGED>(ring + ((i + C::kDepth - 1) % C::kDepth) * C::kSlotBytes, k, k_scale,
                                 base_row, group_page(i + C::kDepth - 1), group_start(i + C::kDepth - 1),
-                                s_last, dl, lane);
+                                s_last, dl, lane, cached);
         // group i is older than the C::kDepth-1 groups issued after it: loads complete in order
         __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (C::kDepth - 1)));
       } else {
         // tail: nothing is issued past the wave's groups, so wait for every load in flight
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
       }
-      const float v = consume_group<FP8>(ring + (i % C::kDepth) * C::kSlotBytes, qf, wt, lane);
+      const float v = consume_group<FP8>(ring + (i % C::kDepth) * C::kSlotBytes, qf, hw, lane);
       const int64_t s = group_start(i) + lane;
       if (lane < C::kKeys && s < len) {
         out[s] = v;
@@ -400,7 +419,7 @@ template <bool FP8, bool PAGED, bool HIST>
 static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const RowsDev &rows,
                              const uint8_t *q8, const float *q_scale, const uint8_t *k8,
                              const float *k_scale, const float *w, float *logits, int64_t ld,
-                             uint32_t *hcnt, uint32_t *hlist, int hstride) {
+                             uint32_t *hcnt, uint32_t *hlist, int hstride, int cached) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
@@ -410,7 +429,7 @@ static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const Ro
     attr_set = true;
   }
   indexer_mfma_kernel<FP8, PAGED, HIST><<<grid, IdxCfg<FP8>::kWaves * kWave, shm, stream>>>(
-      rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
+      rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
   return hipGetLastError();
 }
 
@@ -444,11 +463,12 @@ static hipError_t launch_indexer(const RowsHost &rh, bool paged, bool fp8, const
   const size_t shm = indexer_lds_bytes(fp8, HIST);
   const uint8_t *q8 = static_cast<const uint8_t *>(q);
   const uint8_t *k8 = static_cast<const uint8_t *>(k);
+  const int cached = rh.num_rows > rh.num_seqs;   // rows share sequences: keep keys in cache
   if (fp8)
-    return paged ? launch_one<true, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride)
-                 : launch_one<true, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
-  return paged ? launch_one<false, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride)
-               : launch_one<false, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride);
+    return paged ? launch_one<true, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached)
+                 : launch_one<true, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
+  return paged ? launch_one<false, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached)
+               : launch_one<false, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
 }
 
 hipError_t launch_indexer_mfma(const RowsHost &rh, bool paged, bool fp8, const void *q,

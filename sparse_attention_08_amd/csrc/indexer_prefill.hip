@@ -1,18 +1,19 @@
-// indexer_prefill.hip -- lightning-indexer scores for prefill-shaped batches on gfx950
-// ("DeepSeek-V3.2 技术报告摘要", section 1, DSA ① Lightning Indexer:
-// I[t,s] = sum_j w[t,j] * ReLU(q[t,j,:] . k[s,:]) over the preceding tokens s).
+// indexer_prefill.hip -- bf16 lightning-indexer scores for batches with many query rows per
+// sequence on gfx950: prefill, chunked prefill, multi-token decode ("DeepSeek-V3.2 技术报告
+// 摘要", section 1, DSA ① Lightning Indexer: I[t,s] = sum_j w[t,j] * ReLU(q[t,j,:] . k[s,:])
+// over the preceding tokens s).
 //
-// When many query rows belong to one sequence they all read the same keys, so the work is a
-// contraction with reuse on both sides (C3: 2.2 TFLOP over 4 MB of keys).  A workgroup takes
-// 8 consecutive query rows, one per wave, each wave holding its row's 64 x 128 query block
-// in registers as MFMA operands, and a chunk of 2048 keys of their sequence.  128-key tiles
-// (32 KB) are gathered once into a double-buffered LDS stage (global->LDS loads, four 1 KB
-// loads per wave per tile) and feed the MFMAs of all 8 rows: per 16 keys and row, 16
+// Rows of one sequence all read the same keys, so the keys are shared: a workgroup takes 8
+// consecutive query rows, one per wave, each wave holding its row's 64 x 128 query block in
+// registers as MFMA operands, and a chunk of up to 2048 keys of their sequence.  128-key
+// tiles are gathered once into a double-buffered LDS stage (global->LDS loads, 1 KB per
+// instruction) and feed the MFMAs of all 8 rows: per 16 keys and row, 16
 // mfma_f32_16x16x32_bf16 (4 head blocks x 4 K-steps), then ReLU, the head weights and the
-// 64-head sum on the accumulators.  Measured on C3 (16K prefill): 2.07 ms against 2.9 ms for
-// the decode-shaped indexer; the clock runs at ~1.9 GHz under this load.
-// Rows of a workgroup that belong to different sequences are handled one sequence at a
-// time, so any ragged batch is computed correctly.
+// 64-head sum by two bf16 MFMAs (head_sum).  Rows of a workgroup that belong to different
+// sequences are handled one sequence at a time, so any ragged batch is computed correctly.
+// Measured on the 16K prefill: 2.0 ms against 2.9 ms for the one-row-at-a-time indexer; the
+// clock runs at ~1.9 GHz under this load.  For fp8 keys the one-row-at-a-time indexer with
+// cached key loads measured faster at every batch shape tried, so this kernel is bf16 only.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -20,32 +21,35 @@ namespace dsa {
 
 constexpr int kPfRows = 8;                     // query rows per workgroup, one per wave
 constexpr int kPfThreads = kPfRows * kWave;
+constexpr int kPfRowBytes = 256;               // one bf16 key (128 dims)
 constexpr int kPfKeys = 128;                   // keys per LDS stage (two 64-token pages)
-constexpr int kPfStages = 2;                   // double buffer: one stage in flight
-constexpr int kPfChunk = 2048;                 // keys per workgroup
-constexpr int kPfRowBytes = 128 * 2;           // one bf16 key
 constexpr int kPfStageBytes = kPfKeys * kPfRowBytes;
+constexpr int kPfStages = 2;                   // double buffer: one stage in flight
 constexpr int kPfLoads = kPfStageBytes / (kPfRows * 1024);   // 1 KB loads per wave per stage
+constexpr int kPfChunk = 2048;                 // keys per workgroup (at most)
+constexpr int kPfMinChunk = 256;               // ... and at least, when the grid is small
+constexpr int kPfHalves = kPfKeys / 64;        // 64-key halves: score stores per stage
+static_assert(kPfKeys % 64 == 0 && kPfMinChunk % kPfKeys == 0, "stages are whole 64-token pages");
+static_assert(kPfChunk / 64 <= 64, "one page per lane");
 static_assert(kPfLoads * kPfRows * 1024 == kPfStageBytes, "whole 1 KB loads per wave");
-constexpr int kPfHalves = kPfKeys / 64;         // 64-key halves: score stores per stage
-static_assert(kPfKeys % 64 == 0 && kPfChunk % kPfKeys == 0, "stages are whole 64-token pages");
 static_assert(kPfStages >= 2 && kPfStages <= 4, "ring depth");
+static_assert(kPfLoads * (kPfStages - 2) + kPfHalves * (kPfStages - 1) <= 7, "pf_wait_vm range");
 
 // Global->LDS load of 16 bytes per lane (lane l lands at lds + 16 l), as an asm statement so
 // the compiler does not drain every pending load before LDS accesses it cannot disambiguate;
-// the instruction writes no register.  Keys are re-read by the other row blocks: no
-// non-temporal hint.
+// the instruction writes no register.
+__device__ __forceinline__ uint32_t pf_lds(const void *lds) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+}
 __device__ __forceinline__ void pf_dma16(const void *g, void *lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
-  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(pf_lds(lds))
                    : "memory");
 }
 
 // s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 field layout).
 constexpr int pf_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// Waits until at most n (uniform, 0 .. kPfLoads (kPfStages - 2) + kPfHalves (kPfStages - 1))
-// of the wave's vector-memory operations are pending.
+// Waits until at most n (uniform, 0 .. 7) of the wave's vector-memory operations are pending.
 __device__ __forceinline__ void pf_wait_vm(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(pf_vmcnt(0)); break;
@@ -58,7 +62,6 @@ __device__ __forceinline__ void pf_wait_vm(int n) {
     default: __builtin_amdgcn_s_waitcnt(pf_vmcnt(7)); break;
   }
 }
-static_assert(kPfLoads * (kPfStages - 2) + kPfHalves * (kPfStages - 1) <= 7, "pf_wait_vm range");
 
 // Four waves per SIMD (two workgroups per CU): the register budget is 128 per lane.
 template <bool PAGED>
@@ -67,21 +70,30 @@ indexer_prefill_kernel(
     int R, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_len,
     const int64_t *__restrict__ seq_start, const int32_t *__restrict__ page_table, int max_pages,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ w,
-    float *__restrict__ logits, int64_t ld, int n_chunks, int n_blocks) {
+    float *__restrict__ logits, int64_t ld, int chunk_keys, int n_chunks, int n_blocks,
+    int by_chunk) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kPfStages][kPfStageBytes];
   __shared__ int s_seq[kPfRows], s_len[kPfRows];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  // Workgroups are dealt to the 8 XCDs round-robin by id.  Id -> (row block, chunk) so that
-  // XCD x takes row blocks x, x + 8, ... with all their chunks in turn (a balanced share of
-  // the causal triangle), row blocks in reverse order (rows near the end have the most keys
-  // and start first).
-  const int xcd = blockIdx.x & 7, m = blockIdx.x >> 3;
-  const int chunk = m % n_chunks;
-  const int rb = (m / n_chunks) * 8 + xcd;
-  if (rb >= n_blocks) return;
-  const int k0 = chunk * kPfChunk;
+  // Workgroups are dealt to the 8 XCDs round-robin by id.  Many row blocks (prefill): id ->
+  // (row block, chunk) so that XCD x takes row blocks x, x + 8, ... with all their chunks in
+  // turn (a balanced share of the causal triangle), row blocks in reverse order (rows near
+  // the end have the most keys and start first).  Fewer than 8 row blocks (a few query rows
+  // per sequence over long contexts): consecutive ids are consecutive chunks of one block,
+  // so every XCD streams its share of each block.
+  int chunk, rb;
+  if (by_chunk) {
+    chunk = blockIdx.x % n_chunks;
+    rb = n_blocks - 1 - (int)(blockIdx.x / n_chunks);
+  } else {
+    const int xcd = blockIdx.x & 7, m = blockIdx.x >> 3;
+    chunk = m % n_chunks;
+    rb = (m / n_chunks) * 8 + xcd;
+    if (rb >= n_blocks) return;
+  }
+  const int k0 = chunk * chunk_keys;
   const int my_r = (n_blocks - 1 - rb) * kPfRows + wave;
   const bool has_row = my_r < R;
   const int my_len = has_row ? row_len[my_r] : 0;
@@ -92,7 +104,7 @@ indexer_prefill_kernel(
   // the wave's query operands: head 16hb + c, 16-byte chunks 4g + t (the dims of the key
   // chunks it reads), and the weights of the heads its accumulators hold (16hb + 4g + i)
   i32x4 qf[4][4];
-  float wt[4][4];
+  float wt[4][4] = {};
   if (my_len > k0) {
     const i32x4 *qr = reinterpret_cast<const i32x4 *>(q + (int64_t)my_r * 64 * 128);
 #pragma unroll
@@ -104,9 +116,10 @@ indexer_prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) wt[hb][i] = w[(int64_t)my_r * 64 + 16 * hb + 4 * g + i];
   }
-  // this lane's 16 bytes of load i of a stage: key (kPfLoads wave + i) 4 + lane/16 of the
-  // stage, physical chunk lane % 16 holding logical chunk (lane % 16) ^ (key % 16)
-  // (conflict-free operand reads)
+  const HeadWeights hw = head_weights(wt);
+  // this lane's 16 bytes of load i of a stage: key 4 (kPfLoads wave + i) + lane / 16 of the
+  // stage, physical chunk lane % 16 holding logical chunk (lane % 16) ^ (key % 16): the 16
+  // keys an MFMA operand read touches at one logical chunk land on distinct bank groups
   int dkey[kPfLoads], dbyte[kPfLoads];
 #pragma unroll
   for (int i = 0; i < kPfLoads; ++i) {
@@ -133,14 +146,14 @@ indexer_prefill_kernel(
     }
     if (b < 0) break;
     done |= act;
-    const int kend = min(k0 + kPfChunk, lmax);
+    const int kend = min(k0 + chunk_keys, lmax);
     if (kend <= k0) continue;
     const bool mine = ((act >> wave) & 1u) && my_len > k0;
     const int n_st = (kend - k0 + kPfKeys - 1) / kPfKeys;
     int page_lane = 0;   // paged: lane j holds the page of the chunk's j-th 64 tokens
     if constexpr (PAGED) {
       const int pg = (k0 >> 6) + lane;
-      if (lane < kPfChunk / 64 && (pg << 6) < kend)
+      if (lane < chunk_keys / 64 && (pg << 6) < kend)
         page_lane = page_table[(int64_t)b * max_pages + pg];
     }
     const int64_t base = PAGED ? 0 : seq_start[b];
@@ -161,7 +174,7 @@ indexer_prefill_kernel(
     for (int st = 0; st < kPfStages - 1 && st < n_st; ++st) issue(st);
     float *out = logits + (int64_t)my_r * ld;
     // score stores of the last kPfStages - 1 iterations (4 bits each, the previous one lowest):
-    // they were issued after this iteration's stage load, and stores count in vmcnt too
+    // they were issued after this iteration's stage loads, and stores count in vmcnt too
     uint32_t st_hist = 0;
     for (int j = 0; j < n_st; ++j) {
       // this wave's part of stage j has landed once no more than its later stage loads and
@@ -169,8 +182,7 @@ indexer_prefill_kernel(
       int pending_st = 0;
 #pragma unroll
       for (int i = 0; i < kPfStages - 1; ++i) pending_st += (st_hist >> (4 * i)) & 15;
-      const int younger = kPfLoads * min(kPfStages - 2, n_st - 1 - j) + pending_st;
-      pf_wait_vm(younger);
+      pf_wait_vm(kPfLoads * min(kPfStages - 2, n_st - 1 - j) + pending_st);
       // every wave's part of stage j is in, and every wave is done with stage j-1, whose
       // slot the next load reuses
       lds_barrier();
@@ -181,37 +193,31 @@ indexer_prefill_kernel(
         const uint8_t *slot = ring[j % kPfStages];
 #pragma unroll
         for (int hf = 0; hf < kPfHalves; ++hf) {
-         float v_mine = 0.f;
+          float v_mine = 0.f;
 #pragma unroll 1
-         for (int u4 = 0; u4 < 4; ++u4) {
-          const int u = 4 * hf + u4;
-          const int kk = 16 * u + c;
-          i32x4 kf[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            kf[t] = *reinterpret_cast<const i32x4 *>(slot + kk * kPfRowBytes +
-                                                     16 * ((4 * g + t) ^ (kk & 15)));
-          f32x4 acc[4];
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) {
-            acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int u4 = 0; u4 < 4; ++u4) {
+            const int kk = 16 * (4 * hf + u4) + c;
+            i32x4 kf[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-              acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, qf[hb][t]), __builtin_bit_cast(bf16x8, kf[t]),
-                  acc[hb], 0, 0, 0);
+              kf[t] = *reinterpret_cast<const i32x4 *>(slot + kk * kPfRowBytes +
+                                                       16 * ((4 * g + t) ^ (kk & 15)));
+            f32x4 acc[4];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+              acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, qf[hb][t]), __builtin_bit_cast(bf16x8, kf[t]),
+                    acc[hb], 0, 0, 0);
+            }
+            const float v = head_sum(acc, hw);   // all 64 heads of key kk, in every lane (., c)
+            if (g == u4) v_mine = v;
           }
-          float v = 0.f;
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wt[hb][i], relu(acc[hb][i]), v);
-          v = sum_xor32(sum_xor16(v));   // all 64 heads of key kk
-          if (g == u4) v_mine = v;
-         }
-         const int s = s0 + 64 * hf + lane;   // lane 16g + c holds key 16g + c of the half
-         if (s < my_len) out[s] = v_mine;
-         n_stores += (s0 + 64 * hf < my_len) ? 1u : 0u;   // lane 0 stores: the store issues
+          const int s = s0 + 64 * hf + lane;   // lane 16g + c holds key 16g + c of the half
+          if (s < my_len) out[s] = v_mine;
+          n_stores += (s0 + 64 * hf < my_len) ? 1u : 0u;   // lane 0 stores: the store issues
         }
       }
       st_hist = ((st_hist << 4) | n_stores) & ((1u << (4 * (kPfStages - 1))) - 1);
@@ -222,19 +228,26 @@ indexer_prefill_kernel(
 
 hipError_t launch_indexer_prefill(const RowsHost &rh, bool paged, const void *q, const void *k,
                                   const float *w, float *logits, int64_t ld, hipStream_t stream) {
-  const int n_chunks = (rh.max_row_len + kPfChunk - 1) / kPfChunk;
   const int n_blocks = (rh.num_rows + kPfRows - 1) / kPfRows;
-  const unsigned grid = 8u * (unsigned)n_chunks * (unsigned)((n_blocks + 7) / 8);
+  // key chunks of 2048, halved while the grid would hold fewer than 1024 workgroups
+  int chunk_keys = kPfChunk;
+  while (chunk_keys > kPfMinChunk &&
+         (int64_t)n_blocks * ((rh.max_row_len + chunk_keys - 1) / chunk_keys) < 1024)
+    chunk_keys /= 2;
+  const int n_chunks = (rh.max_row_len + chunk_keys - 1) / chunk_keys;
+  const int by_chunk = n_blocks < 8;
+  const unsigned grid = by_chunk ? (unsigned)n_chunks * (unsigned)n_blocks
+                                 : 8u * (unsigned)n_chunks * (unsigned)((n_blocks + 7) / 8);
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
   const uint16_t *k16 = static_cast<const uint16_t *>(k);
   if (paged)
     indexer_prefill_kernel<true><<<grid, kPfThreads, 0, stream>>>(
-        rh.num_rows, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages, q16, k16,
-        w, logits, ld, n_chunks, n_blocks);
+        rh.num_rows, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages, q16, k16, w,
+        logits, ld, chunk_keys, n_chunks, n_blocks, by_chunk);
   else
     indexer_prefill_kernel<false><<<grid, kPfThreads, 0, stream>>>(
-        rh.num_rows, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages, q16, k16,
-        w, logits, ld, n_chunks, n_blocks);
+        rh.num_rows, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages, q16, k16, w,
+        logits, ld, chunk_keys, n_chunks, n_blocks, by_chunk);
   return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ def gpu_mla(wl, idx, lse=True):
     out = torch.empty((wl.num_rows, wl.H, wl.D_v), dtype=wl.q.dtype, device=wl.q.device)
     l = torch.empty((wl.num_rows, wl.H), dtype=torch.float32, device=wl.q.device) if lse else None
     if wl.mode == "prefill":
-        dsa.sparse_mla_prefill(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=l)
+        fn = dsa.sparse_mla_prefill_paged if wl.paged else dsa.sparse_mla_prefill
+        fn(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=l)
     elif wl.paged:
         dsa.sparse_mla_decode_paged(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=l)
     else:

@@ -153,6 +153,9 @@ def test_mla_validation(lib):
     assert _mla(lib, _rows(num_rows=0)) == OK
     assert _mla(lib, _rows(), name="dsa_sparse_mla_decode_paged") == INVALID   # layout mismatch
     assert _mla(lib, _rows(paged=True), name="dsa_sparse_mla_prefill") == INVALID
+    assert _mla(lib, _rows(), name="dsa_sparse_mla_prefill_paged") == INVALID   # layout mismatch
+    assert _mla(lib, _rows(paged=True), name="dsa_sparse_mla_prefill_paged", k=0) == INVALID
+    assert _mla(lib, _rows(num_rows=0, paged=True), name="dsa_sparse_mla_prefill_paged") == OK
 
 
 def test_workspace_queries_are_consistent():

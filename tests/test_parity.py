@@ -5,6 +5,7 @@ Tolerances: indexer and attention outputs max-abs-relative <= 1e-5 (fp32) / 2e-2
 rounded to fp32 and on the GPU's own scores.  Attention is compared on the same index
 set on both sides.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -132,19 +133,81 @@ def test_paged_physical_permutation_is_bit_identical():
 
 # ------------------------------------------------------------------------ prefill-shaped indexer
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_prefill_indexer_shares_key_tiles(paged):
-    """Batches with many rows per sequence take the indexer whose workgroups share key tiles
-    between 8 consecutive rows: blocks that straddle sequences, rows crossing the 2048-key
-    chunk boundary, and the first and last row of every sequence."""
+@pytest.mark.parametrize("idx_dtype,paged", [("bf16", False), ("bf16", True), ("fp8", False),
+                                             ("fp8", True)])
+def test_prefill_indexer_shares_key_tiles(idx_dtype, paged):
+    """Batches with many rows per sequence: bf16 takes the indexer whose workgroups share key
+    tiles between 8 consecutive rows (blocks that straddle sequences, rows crossing key-chunk
+    boundaries), fp8 the one-row-at-a-time indexer with cached key loads; the first and last
+    row of every sequence are checked."""
     lens = [13, 29, 2100]
-    wl = workloads.prefill_batch(lens, paged=paged, seed=95, device=DEV,
-                                 name=f"prefill_batch_{'paged' if paged else 'contig'}")
+    wl = workloads.prefill_batch(lens, idx_dtype=idx_dtype, paged=paged, seed=95, device=DEV,
+                                 name=f"prefill_batch_{idx_dtype}_{'paged' if paged else 'contig'}")
     assert wl.num_rows >= 8 * wl.num_seqs
     starts = np.concatenate([[0], np.cumsum(lens)])
     which = sorted(set(range(0, 42)) | {42, 43, 49, 50, 1000, 2047 + 42, 2048 + 42, 2049 + 42,
                                         int(starts[-1]) - 2, int(starts[-1]) - 1})
-    _check_indexer(wl, which, TOL["bf16"])
+    _check_indexer(wl, which, TOL[idx_dtype])
+
+
+def test_chunked_prefill_over_paged_prefix():
+    """New tokens over cached prefixes in a paged cache: the paged indexer (key-sharing kernel),
+    the top-k and the paged attention, each against the oracle on sampled rows."""
+    wl = workloads.prefill_batch([3000, 700], new=[300, 40], paged=True, seed=96, device=DEV,
+                                 name="chunked_prefill_paged")
+    assert wl.num_rows >= 8 * wl.num_seqs and int(wl.row_len.min()) > 600
+    which = [0, 1, 7, 8, 150, 298, 299, 300, 301, 320, 339]
+    g, ref, _ = _check_indexer(wl, which, TOL["bf16"])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g.copy())
+    _check_mla(wl, idx, which, TOL["bf16"])
+
+
+# ------------------------------------------------------------------------ multi-token decode
+
+# a few new tokens per sequence (speculative or multi-token decode) over cached contexts
+MTP_LENS, MTP_NEW = [5000, 1300, 70, 9000, 2049], [4, 2, 3, 4, 2]
+
+
+@pytest.mark.parametrize("idx_dtype,paged", [("bf16", False), ("fp8", False), ("bf16", True),
+                                             ("fp8", True)])
+def test_multi_token_decode(idx_dtype, paged):
+    """Several query rows per sequence share the key stream: the key-sharing indexer in bf16 and
+    fp8 (workgroups of 8 rows straddling three sequences, rows on both sides of the 2048-key
+    chunk boundary), the top-k and the split attention on every row, and the one-call decode
+    against the separate calls."""
+    wl = workloads.prefill_batch(MTP_LENS, new=MTP_NEW, idx_dtype=idx_dtype, paged=paged, seed=97,
+                                 device=DEV,
+                                 name=f"mtp_{idx_dtype}_{'paged' if paged else 'contig'}")
+    wl = dataclasses.replace(wl, mode="decode")
+    assert wl.num_rows >= 2 * wl.num_seqs
+    which = list(range(wl.num_rows))
+    g, ref, _ = _check_indexer(wl, which, TOL[idx_dtype])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g.copy())
+    _check_mla(wl, idx, which, TOL["bf16"])
+    say(f"one-call decode {wl.name}")
+    _, idx1 = _attention_decode_vs_separate(wl)
+    assert torch.equal(idx1, idx)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_multi_token_decode_shared_keys(paged):
+    """16 rows per sequence over two sequences (bf16): the key-sharing indexer with fewer than 8
+    row blocks (consecutive workgroups take consecutive key chunks of a block, chunks shrunk
+    to 256 keys to fill the grid), a block straddling the two sequences; every row against the
+    oracle, then the top-k, the split attention and the one-call decode."""
+    wl = workloads.prefill_batch([5000, 9000], new=[12, 20], paged=paged, seed=98, device=DEV,
+                                 name=f"mtp_shared_{'paged' if paged else 'contig'}")
+    wl = dataclasses.replace(wl, mode="decode")
+    assert wl.num_rows >= 8 * wl.num_seqs
+    which = list(range(wl.num_rows))
+    g, ref, _ = _check_indexer(wl, which, TOL["bf16"])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g.copy())
+    _check_mla(wl, idx, which, TOL["bf16"])
+    say(f"one-call decode {wl.name}")
+    _attention_decode_vs_separate(wl)
 
 
 # ------------------------------------------------------------------------ fused indexer + top-k

@@ -199,16 +199,21 @@ def prefill(L, *, idx_dtype="bf16", mla_dtype="bf16", H_I=64, D_I=128, H=128, D_
         page_size=PAGE, lens=[L], **vals)
 
 
-def prefill_batch(lens, *, idx_dtype="bf16", mla_dtype="bf16", paged=False, H_I=64, D_I=128,
-                  H=128, D_qk=576, D_v=512, topk=2048, scale=None, w_div=8.0, seed=0, device="cpu",
-                  name="prefill_batch") -> Workload:
-    """Several sequences prefilled together: every token of sequence b is a query row (in
-    sequence order), row t of b attending causally to positions 0..t of b."""
+def prefill_batch(lens, *, new=None, idx_dtype="bf16", mla_dtype="bf16", paged=False, H_I=64,
+                  D_I=128, H=128, D_qk=576, D_v=512, topk=2048, scale=None, w_div=8.0, seed=0,
+                  device="cpu", name="prefill_batch") -> Workload:
+    """Several sequences prefilled together: the last new[b] tokens of sequence b (all of them
+    when new is None) are query rows, in sequence order; row t of b attends causally to
+    positions 0..t of b.  new[b] < lens[b] is a chunk of prefill over a cached prefix."""
     lens = [int(x) for x in lens]
     if not lens or min(lens) < 1:
         raise ValueError("every sequence needs at least one token")
+    new = list(lens) if new is None else [int(x) for x in new]
+    if len(new) != len(lens) or min(new) < 1 or any(n > l for n, l in zip(new, lens)):
+        raise ValueError("each sequence needs 1 .. len query rows")
     B = len(lens)
-    R = sum(lens)
+    R = sum(new)
+    N = sum(lens)
     sgen = torch.Generator()
     sgen.manual_seed(seed)
     if paged:
@@ -225,11 +230,12 @@ def prefill_batch(lens, *, idx_dtype="bf16", mla_dtype="bf16", paged=False, H_I=
     else:
         seq_start = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64))
         pt = None
-        kshape, kvshape = (R, D_I), (R, D_qk)
+        kshape, kvshape = (N, D_I), (N, D_qk)
     vals = _draw_values({"q_idx": (R, H_I, D_I), "k_idx": kshape, "q": (R, H, D_qk), "kv": kvshape},
                         idx_dtype, mla_dtype, w_div, seed, device)
-    row_seq = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(lens)])
-    row_len = torch.cat([torch.arange(1, n + 1, dtype=torch.int32) for n in lens])
+    row_seq = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(new)])
+    row_len = torch.cat([torch.arange(l - n + 1, l + 1, dtype=torch.int32)
+                         for n, l in zip(new, lens)])
     return Workload(
         name=name, mode="prefill", idx_dtype=idx_dtype, mla_dtype=mla_dtype, H_I=H_I, D_I=D_I, H=H,
         D_qk=D_qk, D_v=D_v, topk=topk, scale=scale if scale is not None else 1.0 / math.sqrt(192.0),
