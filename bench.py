@@ -38,9 +38,15 @@ KERNEL_SOURCES = {"indexer_mfma_kernel": "sparse_attention_08_amd/csrc/indexer.h
                   "topk_rows_kernel": "sparse_attention_08_amd/csrc/topk.hip"}
 
 
+DEVICE_HEADER = "sparse_attention_08_amd/csrc/dsa_device.h"   # device helpers every kernel inlines
+
+
 def source_hash(kernel: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCES[kernel], DEVICE_HEADER):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
