@@ -70,6 +70,10 @@ def _load():
                                        vp, vp, ctypes.POINTER(_Rows), vp, i32, vp, vp, ctypes.c_int]
         lib.oref_cache_row.argtypes = [ctypes.POINTER(_Rows), i32, i64]
         lib.oref_cache_row.restype = i64
+        lib.oref_bf16_codes.argtypes = [vp, vp, i64]
+        lib.oref_e4m3_codes.argtypes = [vp, vp, i64]
+        lib.oref_prep_keys.argtypes = [i32, vp, vp, i64, vp, i32, ctypes.c_int, vp, vp, vp, vp, vp]
+        lib.oref_prep_queries.argtypes = [i32, vp, vp, i32, ctypes.c_int, i32, vp, vp, vp, i32, vp]
         _lib = lib
     return _lib
 
@@ -237,3 +241,61 @@ def max_abs_rel(x, ref) -> float:
     if den == 0.0:
         return num
     return num / den
+
+
+# --------------------------------------------------------------------------- input prep
+
+def bf16_codes(x) -> np.ndarray:
+    """fp32 values -> bf16 codes (nearest, ties to the even code)."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oref_bf16_codes(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def e4m3_codes(x) -> np.ndarray:
+    """fp32 values -> OCP E4M3FN codes (nearest finite, ties to the even code)."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().oref_e4m3_codes(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def prep_keys(idx_dtype: str, pos, rows_out, cos_sin, k_in, kv_in, k_cache, kv_cache,
+              k_scale=None):
+    """Key-side prep for new tokens, written into copies of k_cache / kv_cache (and k_scale);
+    returns the updated copies.  k_in [T,128] and kv_in [T,576] are bf16 bits (uint16); the
+    caches are [rows,128] (uint16 bf16 or uint8 e4m3) and [rows,576] uint16."""
+    enc = _enc(idx_dtype)
+    pos = _c(pos, np.int32)
+    rows_out = _c(rows_out, np.int64)
+    cos_sin = _c(cos_sin, np.float32)
+    k_in = _c(k_in, np.uint16)
+    kv_in = _c(kv_in, np.uint16)
+    k_cache = np.array(k_cache, dtype=np.uint16 if enc == BF16 else np.uint8, copy=True, order="C")
+    kv_cache = np.array(kv_cache, dtype=np.uint16, copy=True, order="C")
+    ks = None if k_scale is None else np.array(k_scale, dtype=np.float32, copy=True, order="C")
+    rc = _load().oref_prep_keys(pos.size, _ptr(pos), _ptr(rows_out), kv_cache.shape[0],
+                                _ptr(cos_sin), cos_sin.shape[0], enc, _ptr(k_in), _ptr(k_cache),
+                                _ptr(ks), _ptr(kv_in), _ptr(kv_cache))
+    if rc:
+        raise ValueError("oref_prep_keys rejected its arguments")
+    return k_cache, kv_cache, ks
+
+
+def prep_queries(idx_dtype: str, pos, cos_sin, qi_in, q):
+    """Query-side prep: returns (qi_out, qi_scale or None, q rotated).  qi_in [R,H_I,128] and
+    q [R,H,576] are bf16 bits (uint16)."""
+    enc = _enc(idx_dtype)
+    pos = _c(pos, np.int32)
+    cos_sin = _c(cos_sin, np.float32)
+    qi_in = _c(qi_in, np.uint16)
+    q = np.array(q, dtype=np.uint16, copy=True, order="C")
+    R, HI = int(qi_in.shape[0]), int(qi_in.shape[1])
+    qi_out = np.zeros(qi_in.shape, dtype=np.uint16 if enc == BF16 else np.uint8)
+    qs = np.zeros((R, HI), dtype=np.float32) if enc == E4M3 else None
+    rc = _load().oref_prep_queries(R, _ptr(pos), _ptr(cos_sin), cos_sin.shape[0], enc, HI,
+                                   _ptr(qi_in), _ptr(qi_out), _ptr(qs), int(q.shape[1]), _ptr(q))
+    if rc:
+        raise ValueError("oref_prep_queries rejected its arguments")
+    return qi_out, qs, q

@@ -370,3 +370,163 @@ int oref_dense_mqa(int dtype, int n_heads, int d_qk, int d_v, double scale,
     run_rows(dense_row, &c, n_which, n_threads);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Indexer-input and cache-write prep (definitions in dsa_oracle.h).         */
+/* ------------------------------------------------------------------------ */
+
+static float f32_from_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t bits_of_f32(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* The two bf16 values around f are f with its low 16 bits cleared (toward
+ * zero) and the next one away from zero; take the nearer, ties to the even
+ * code. */
+uint16_t oref_bf16_code(float f)
+{
+    if (isnan(f)) return 0x7fc0;
+    const uint32_t u = bits_of_f32(f);
+    const uint32_t lo = u & 0xffff0000u;
+    const uint32_t hi = lo + 0x10000u;
+    const double v = fabs((double)f);
+    const double vlo = fabs((double)f32_from_bits(lo));
+    const double vhi = ((hi >> 23) & 0xff) == 0xff ? INFINITY : fabs((double)f32_from_bits(hi));
+    const double dlo = v - vlo, dhi = vhi - v;
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return ((lo >> 16) & 1) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);
+}
+
+/* Search of the 127 finite non-negative e4m3 codes for the nearest value. */
+uint8_t oref_e4m3_code(float f)
+{
+    const double v = fabs((double)f);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7e; ++c) {
+        const double d = fabs(e4m3_value((uint8_t)c) - v);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(signbit(f) ? (best | 0x80) : best);
+}
+
+/* One rotated pair, every product and sum rounded to fp32 once. */
+static void rope_pair(float a, float b, float c, float s, float *ya, float *yb)
+{
+    const float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+    *ya = ac - bs;
+    *yb = bc + as;
+}
+
+static float bf16_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+/* A 128-dim indexer vector: dims 0..63 rotated non-interleaved, the rest kept;
+ * written as bf16 codes or as e4m3 codes with their scale. */
+static void indexer_vector(const uint16_t *in, const float *cs, int idx_dtype, void *out,
+                           float *scale_out)
+{
+    float y[128];
+    for (int j = 0; j < 128; ++j) y[j] = bf16_f32(in[j]);
+    for (int i = 0; i < 32; ++i) {
+        float a, b;
+        rope_pair(y[i], y[i + 32], cs[i], cs[32 + i], &a, &b);
+        y[i] = a;
+        y[i + 32] = b;
+    }
+    if (idx_dtype == OREF_BF16) {
+        uint16_t *o = (uint16_t *)out;
+        for (int j = 0; j < 128; ++j) o[j] = j < 64 ? oref_bf16_code(y[j]) : in[j];
+        return;
+    }
+    float amax = 0.0f;
+    for (int j = 0; j < 128; ++j)
+        if (fabsf(y[j]) > amax) amax = fabsf(y[j]);
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint8_t *o = (uint8_t *)out;
+    for (int j = 0; j < 128; ++j) o[j] = oref_e4m3_code(y[j] / scale);
+    *scale_out = scale;
+}
+
+/* A 576-dim MLA vector: dims 512..575 rotated interleaved, the rest kept. */
+static void mla_vector(const uint16_t *in, const float *cs, uint16_t *out)
+{
+    for (int j = 0; j < 512; ++j) out[j] = in[j];
+    for (int i = 0; i < 32; ++i) {
+        float a, b;
+        rope_pair(bf16_f32(in[512 + 2 * i]), bf16_f32(in[513 + 2 * i]), cs[i], cs[32 + i], &a, &b);
+        out[512 + 2 * i] = oref_bf16_code(a);
+        out[513 + 2 * i] = oref_bf16_code(b);
+    }
+}
+
+int oref_prep_keys(int32_t n_tok, const int32_t *pos, const int64_t *rows_out, int64_t cache_rows,
+                   const float *cos_sin, int32_t max_pos, int idx_dtype,
+                   const uint16_t *k_in, void *k_cache, float *k_scale,
+                   const uint16_t *kv_in, uint16_t *kv_cache)
+{
+    if (n_tok < 0 || max_pos <= 0 || (idx_dtype != OREF_BF16 && idx_dtype != OREF_E4M3))
+        return 1;
+    const size_t elt = idx_dtype == OREF_BF16 ? 2 : 1;
+    for (int32_t t = 0; t < n_tok; ++t) {
+        const int32_t p = pos[t];
+        const int64_t r = rows_out[t];
+        if (p < 0 || p >= max_pos || r < 0 || r >= cache_rows) continue;
+        const float *cs = cos_sin + (int64_t)p * 64;
+        indexer_vector(k_in + (int64_t)t * 128, cs, idx_dtype,
+                       (uint8_t *)k_cache + (size_t)r * 128 * elt, k_scale ? k_scale + r : NULL);
+        mla_vector(kv_in + (int64_t)t * 576, cs, kv_cache + (size_t)r * 576);
+    }
+    return 0;
+}
+
+int oref_prep_queries(int32_t n_rows, const int32_t *pos, const float *cos_sin, int32_t max_pos,
+                      int idx_dtype, int32_t n_idx_heads, const uint16_t *qi_in, void *qi_out,
+                      float *qi_scale, int32_t n_heads, uint16_t *q)
+{
+    if (n_rows < 0 || max_pos <= 0 || n_idx_heads <= 0 || n_heads <= 0 ||
+        (idx_dtype != OREF_BF16 && idx_dtype != OREF_E4M3))
+        return 1;
+    const size_t elt = idx_dtype == OREF_BF16 ? 2 : 1;
+    uint16_t *tmp = (uint16_t *)malloc(576 * sizeof(uint16_t));
+    if (!tmp) return 2;
+    for (int32_t r = 0; r < n_rows; ++r) {
+        const int32_t p = pos[r];
+        if (p < 0 || p >= max_pos) continue;
+        const float *cs = cos_sin + (int64_t)p * 64;
+        for (int32_t h = 0; h < n_idx_heads; ++h) {
+            const int64_t v = (int64_t)r * n_idx_heads + h;
+            indexer_vector(qi_in + v * 128, cs, idx_dtype, (uint8_t *)qi_out + (size_t)v * 128 * elt,
+                           qi_scale ? qi_scale + v : NULL);
+        }
+        for (int32_t h = 0; h < n_heads; ++h) {
+            uint16_t *qh = q + ((int64_t)r * n_heads + h) * 576;
+            mla_vector(qh, cs, tmp);
+            memcpy(qh, tmp, 576 * sizeof(uint16_t));
+        }
+    }
+    free(tmp);
+    return 0;
+}
+
+void oref_bf16_codes(const float *src, uint16_t *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = oref_bf16_code(src[i]);
+}
+
+void oref_e4m3_codes(const float *src, uint8_t *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = oref_e4m3_code(src[i]);
+}

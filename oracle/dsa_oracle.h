@@ -19,6 +19,9 @@
  *       attention output".
  *  [S]  "DeepSeek-V3.2" (miles model docs), section 1 "Model Introduction"
  *       (shapes) and section 5.3 "Rollout & SGLang" (bf16 cache, page 64).
+ *  [E]  "DeepSeek-V3.2-Exp" README, section "更新" (the 2025-11-17 update):
+ *       the indexer's RoPE takes its input in the non-interleaved layout, the
+ *       MLA's RoPE in the interleaved layout.
  */
 #ifndef DSA_ORACLE_H
 #define DSA_ORACLE_H
@@ -77,6 +80,53 @@ int oref_dense_mqa(int dtype, int n_heads, int d_qk, int d_v, double scale,
                    const void *q, const void *kv,
                    const oref_rows *rows, const int32_t *which, int32_t n_which,
                    double *out, double *lse, int n_threads);
+
+/* ------------------------------------------------------------------------ */
+/* Indexer-input and cache-write prep ([E] RoPE layouts, [R] ① FP8 indexer,  */
+/* [S] 5.3 cache).  These steps end in a rounding decision (a bf16 or e4m3   */
+/* code), so they are computed in fp32 exactly as defined below, each       */
+/* operation rounded once (no fused multiply-add), and the codes chosen      */
+/* from the definitions of the formats.                                      */
+/*                                                                           */
+/* cos_sin row p (p < max_pos) holds cos(p*theta_i) for i < 32, then         */
+/* sin(p*theta_i) for i < 32: the caller's frequency schedule.               */
+/* RoPE on a 64-dim part x, pair i (i < 32) rotated by angle i of the row:    */
+/*   non-interleaved: (x[i], x[i+32])     interleaved: (x[2i], x[2i+1])      */
+/*   (a, b) -> (a*cos - b*sin, b*cos + a*sin)                                */
+/* Indexer vectors (128 dims): dims 0..63 carry the rotation, 64..127 not.   */
+/* MLA vectors (576 dims): dims 512..575 carry the rotation.                 */
+/* fp8 quantisation of a 128-dim vector y: amax = max |y_j|,                  */
+/*   scale = amax / 448 (1 when amax = 0), code_j = e4m3 nearest to          */
+/*   y_j / scale, ties to the even code.                                     */
+/* ------------------------------------------------------------------------ */
+
+/* fp32 -> bf16 code: the nearest bf16 value, ties to the even code. */
+uint16_t oref_bf16_code(float f);
+/* fp32 -> OCP E4M3FN code: the nearest finite e4m3 value (|v| <= 448),
+ * ties to the even code; values beyond 448 take 448. */
+uint8_t oref_e4m3_code(float f);
+void oref_bf16_codes(const float *src, uint16_t *dst, int64_t n);
+void oref_e4m3_codes(const float *src, uint8_t *dst, int64_t n);
+
+/* Key side, per new token t: the indexer key k_in[t] (bf16, 128 dims) rotated
+ * (non-interleaved) and written to k_cache row rows_out[t] as bf16
+ * (idx_dtype OREF_BF16) or as e4m3 codes plus k_scale[row] (OREF_E4M3); the
+ * MLA entry kv_in[t] (bf16, 576 dims) with its last 64 dims rotated
+ * (interleaved) written to kv_cache row rows_out[t].  Tokens whose position is
+ * outside [0, max_pos) or whose row is outside [0, cache_rows) are skipped. */
+int oref_prep_keys(int32_t n_tok, const int32_t *pos, const int64_t *rows_out, int64_t cache_rows,
+                   const float *cos_sin, int32_t max_pos, int idx_dtype,
+                   const uint16_t *k_in, void *k_cache, float *k_scale,
+                   const uint16_t *kv_in, uint16_t *kv_cache);
+
+/* Query side, per row r at position pos[r]: each of the n_idx_heads indexer
+ * heads of qi_in[r] (bf16, 128 dims) rotated (non-interleaved) and written as
+ * bf16, or as e4m3 codes with qi_scale[r, head]; each of the n_heads MLA heads
+ * of q[r] (bf16, 576 dims) rotated in place on its last 64 dims
+ * (interleaved).  Rows with a position outside [0, max_pos) are skipped. */
+int oref_prep_queries(int32_t n_rows, const int32_t *pos, const float *cos_sin, int32_t max_pos,
+                      int idx_dtype, int32_t n_idx_heads, const uint16_t *qi_in, void *qi_out,
+                      float *qi_scale, int32_t n_heads, uint16_t *q);
 
 #ifdef __cplusplus
 }
