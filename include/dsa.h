@@ -221,6 +221,47 @@ int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int i
                                       void *out, float *lse, void *ws, size_t ws_bytes,
                                       void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Indexer-input and cache-write prep: the step in front of the indexer for every new token
+ * ("DeepSeek-V3.2 技术报告摘要", section 1, DSA ①: indexer keys and queries, FP8 supported;
+ * "DeepSeek-V3.2-Exp" README, section "更新": the indexer's RoPE takes the non-interleaved
+ * layout, the MLA's RoPE the interleaved one; "DeepSeek-V3.2" model docs, section 5.3: the
+ * bf16 latent cache in 64-token pages).
+ *
+ * cos_sin: [max_position, 64] f32, row p = cos(p*theta_i) for i < 32, then sin(p*theta_i)
+ *   for i < 32 (the caller's frequency schedule).
+ * RoPE of a 64-dim part x at position p, pair i rotated by angle i of row p:
+ *   indexer vectors (128 dims): dims 0..63, pairs (x[i], x[i+32])       (non-interleaved)
+ *   MLA vectors (576 dims):     dims 512..575, pairs (x[512+2i], x[513+2i]) (interleaved)
+ *   (a, b) -> (a cos - b sin, b cos + a sin), each product and sum one fp32 operation.
+ * fp8 (idx_dtype DSA_FP8_E4M3): an indexer vector y is stored as e4m3 codes of y / scale
+ *   (round to nearest even) with scale = max|y| / 448 (1 for a zero vector), as f32.
+ * bf16 outputs are the rotated values rounded to nearest even; unrotated dims are copied.
+ *
+ * dsa_prep_cache_write: for each of num_tokens new tokens t at positions[t], writes cache
+ *   row cache_rows[t] (the physical row: seq_start + position, or page * 64 + position % 64):
+ *   k_idx_in [T, 128] bf16 -> k_idx_cache [num_cache_rows, 128] (bf16, or e4m3 with
+ *   k_idx_scale [num_cache_rows] f32); kv_in [T, 576] bf16 -> kv_cache [num_cache_rows, 576]
+ *   bf16.  Tokens with a position outside [0, max_position) or a row outside
+ *   [0, num_cache_rows) are skipped (padding).  Two tokens naming one row race.
+ * dsa_prep_queries: for each of num_rows query rows at positions[r]: q_idx_in [R, 64, 128]
+ *   bf16 -> q_idx [R, 64, 128] (bf16, or e4m3 with q_idx_scale [R, 64] f32; q_idx may be
+ *   q_idx_in for bf16), and the n_heads MLA heads of q [R, n_heads, 576] bf16 rotated in
+ *   place.  Rows with a position outside [0, max_position) are left as they are.
+ * All pointers are device pointers owned by the caller; the calls are asynchronous on
+ * `stream`.  Errors: DSA_ERR_INVALID_ARG for negative counts, missing pointers, a scale
+ * buffer missing for fp8 or given for bf16, max_position < 1, num_cache_rows < 1 or
+ * n_heads < 1;
+ * DSA_ERR_UNSUPPORTED for idx_dtype other than bf16 / fp8; num_tokens / num_rows == 0 is a
+ * no-op. */
+int dsa_prep_cache_write(int num_tokens, const int32_t *positions, const int64_t *cache_rows,
+                         int64_t num_cache_rows, const float *cos_sin, int max_position,
+                         int idx_dtype, const void *k_idx_in, void *k_idx_cache,
+                         float *k_idx_scale, const void *kv_in, void *kv_cache, void *stream);
+int dsa_prep_queries(int num_rows, const int32_t *positions, const float *cos_sin,
+                     int max_position, int idx_dtype, const void *q_idx_in, void *q_idx,
+                     float *q_idx_scale, int n_heads, void *q, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

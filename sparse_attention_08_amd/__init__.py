@@ -83,6 +83,10 @@ def load_library() -> ctypes.CDLL:
         f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                       i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
         f.restype = i32
+    lib.dsa_prep_cache_write.argtypes = [i32, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.dsa_prep_cache_write.restype = i32
+    lib.dsa_prep_queries.argtypes = [i32, vp, vp, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.dsa_prep_queries.restype = i32
     _lib = lib
     return lib
 
@@ -364,3 +368,57 @@ def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, k
         _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check(s, name)
     return out
+
+
+# --------------------------------------------------------------------------- input prep
+
+def prep_cache_write(positions, cache_rows, cos_sin, k_idx_in, k_idx_cache, kv_in, kv_cache,
+                     k_idx_scale=None):
+    """RoPE + (fp8) quantisation + cache write for new tokens: indexer keys ``k_idx_in``
+    [T, 128] bf16 into ``k_idx_cache`` (bf16, or fp8 e4m3 / uint8 with ``k_idx_scale``) and
+    latent entries ``kv_in`` [T, 576] bf16 into ``kv_cache``, at the flat cache rows
+    ``cache_rows`` [T] int64 (contiguous [N, ...] or paged [P, 64, ...] caches alike)."""
+    lib = load_library()
+    _dev(positions, "positions", (torch.int32,))
+    _dev(cache_rows, "cache_rows", (torch.int64,))
+    _dev(cos_sin, "cos_sin", (torch.float32,))
+    _dev(k_idx_in, "k_idx_in", (torch.bfloat16,))
+    _dev(kv_in, "kv_in", (torch.bfloat16,))
+    _dev(k_idx_cache, "k_idx_cache", (torch.bfloat16, torch.float8_e4m3fn, torch.uint8))
+    _dev(kv_cache, "kv_cache", (torch.bfloat16,))
+    if k_idx_scale is not None:
+        _dev(k_idx_scale, "k_idx_scale", (torch.float32,))
+    T = int(positions.numel())
+    if k_idx_in.numel() != T * 128 or kv_in.numel() != T * 576 or cache_rows.numel() != T:
+        raise ValueError("k_idx_in must be [T, 128], kv_in [T, 576] and cache_rows [T]")
+    n_rows = kv_cache.numel() // 576
+    if k_idx_cache.numel() != n_rows * 128 or cos_sin.shape[-1] != 64:
+        raise ValueError("k_idx_cache must hold as many 128-dim rows as kv_cache 576-dim rows, "
+                         "and cos_sin must be [max_position, 64]")
+    s = lib.dsa_prep_cache_write(T, _ptr(positions), _ptr(cache_rows), n_rows, _ptr(cos_sin),
+                                 int(cos_sin.shape[0]), dtype_code(k_idx_cache), _ptr(k_idx_in),
+                                 _ptr(k_idx_cache), _ptr(k_idx_scale), _ptr(kv_in), _ptr(kv_cache),
+                                 _stream())
+    _check(s, "dsa_prep_cache_write")
+
+
+def prep_queries(positions, cos_sin, q_idx_in, q_idx, q, q_idx_scale=None):
+    """RoPE + (fp8) quantisation of the query rows: indexer queries ``q_idx_in`` [R, 64, 128]
+    bf16 into ``q_idx`` (bf16, or fp8 e4m3 / uint8 with ``q_idx_scale`` [R, 64]), and the MLA
+    queries ``q`` [R, H, 576] bf16 rotated in place."""
+    lib = load_library()
+    _dev(positions, "positions", (torch.int32,))
+    _dev(cos_sin, "cos_sin", (torch.float32,))
+    _dev(q_idx_in, "q_idx_in", (torch.bfloat16,))
+    _dev(q_idx, "q_idx", (torch.bfloat16, torch.float8_e4m3fn, torch.uint8))
+    _dev(q, "q", (torch.bfloat16,))
+    if q_idx_scale is not None:
+        _dev(q_idx_scale, "q_idx_scale", (torch.float32,))
+    R = int(positions.numel())
+    if q_idx_in.numel() != R * 64 * 128 or q_idx.numel() != R * 64 * 128 or q.dim() != 3 \
+            or q.shape[0] != R or q.shape[2] != 576 or cos_sin.shape[-1] != 64:
+        raise ValueError("q_idx_in / q_idx must be [R, 64, 128], q [R, H, 576], cos_sin [P, 64]")
+    s = lib.dsa_prep_queries(R, _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]),
+                             dtype_code(q_idx), _ptr(q_idx_in), _ptr(q_idx), _ptr(q_idx_scale),
+                             int(q.shape[1]), _ptr(q), _stream())
+    _check(s, "dsa_prep_queries")

@@ -386,4 +386,38 @@ int dsa_sparse_mla_prefill_paged(const dsa_rows *rows, int dtype, int n_heads, i
                     kv, idx, k, out, lse, nullptr, 0, stream);
 }
 
+int dsa_prep_cache_write(int num_tokens, const int32_t *positions, const int64_t *cache_rows,
+                         int64_t num_cache_rows, const float *cos_sin, int max_position,
+                         int idx_dtype, const void *k_idx_in, void *k_idx_cache,
+                         float *k_idx_scale, const void *kv_in, void *kv_cache, void *stream) {
+  if (num_tokens < 0 || max_position < 1 || num_cache_rows < 1) return DSA_ERR_INVALID_ARG;
+  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3)
+    return DSA_ERR_INVALID_ARG;
+  if (idx_dtype == DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return DSA_OK;
+  if (!positions || !cache_rows || !cos_sin || !k_idx_in || !k_idx_cache || !kv_in || !kv_cache)
+    return DSA_ERR_INVALID_ARG;
+  if ((idx_dtype == DSA_FP8_E4M3) != (k_idx_scale != nullptr)) return DSA_ERR_INVALID_ARG;
+  return status_of(dsa::launch_prep_keys(num_tokens, positions, cache_rows, num_cache_rows,
+                                         cos_sin, max_position, idx_dtype == DSA_FP8_E4M3,
+                                         k_idx_in, k_idx_cache, k_idx_scale, kv_in, kv_cache,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int dsa_prep_queries(int num_rows, const int32_t *positions, const float *cos_sin,
+                     int max_position, int idx_dtype, const void *q_idx_in, void *q_idx,
+                     float *q_idx_scale, int n_heads, void *q, void *stream) {
+  if (num_rows < 0 || max_position < 1 || n_heads < 1) return DSA_ERR_INVALID_ARG;
+  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3)
+    return DSA_ERR_INVALID_ARG;
+  if (idx_dtype == DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (num_rows == 0) return DSA_OK;
+  if (!positions || !cos_sin || !q_idx_in || !q_idx || !q) return DSA_ERR_INVALID_ARG;
+  if ((idx_dtype == DSA_FP8_E4M3) != (q_idx_scale != nullptr)) return DSA_ERR_INVALID_ARG;
+  return status_of(dsa::launch_prep_queries(num_rows, positions, cos_sin, max_position,
+                                            idx_dtype == DSA_FP8_E4M3, q_idx_in, q_idx,
+                                            q_idx_scale, n_heads, q,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

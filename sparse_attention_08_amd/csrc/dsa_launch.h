@@ -83,4 +83,17 @@ hipError_t launch_mla_bf16_select(const RowsHost &rows, bool paged, int H, float
                                   float *lse, int splits, void *ws, const float *logits,
                                   int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream);
 
+// ---- indexer-input and cache-write prep ----
+// One new token per entry: indexer key (bf16 [T,128]) rotated and written as bf16 or e4m3
+// (+ scale) to cache row rows[t], latent entry (bf16 [T,576]) rotated and written there too.
+hipError_t launch_prep_keys(int T, const int32_t *pos, const int64_t *rows, int64_t cache_rows,
+                            const float *cos_sin, int max_pos, bool fp8, const void *k_in,
+                            void *k_cache, float *k_scale, const void *kv_in, void *kv_cache,
+                            hipStream_t stream);
+// Query rows: 64 indexer heads rotated to bf16 or e4m3 (+ per-head scale), n_heads MLA heads
+// rotated in place.
+hipError_t launch_prep_queries(int R, const int32_t *pos, const float *cos_sin, int max_pos,
+                               bool fp8, const void *qi_in, void *qi_out, float *qi_scale,
+                               int n_heads, void *q, hipStream_t stream);
+
 }  // namespace dsa

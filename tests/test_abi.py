@@ -195,3 +195,27 @@ def test_attention_decode_validation(lib):
     assert call(big, idx_dtype=2, qs=FAKE, ks=FAKE) == WORKSPACE
     assert call(big, idx_dtype=2, qs=FAKE, ks=FAKE, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
     assert dsa.sparse_attention_decode_workspace_size(8, 131072, 7, 2048, 128, 512) == 0
+
+
+def test_prep_validation(lib):
+    def keys(T=4, pos=True, rows=True, n_rows=64, cs=True, max_pos=128, dt=1, scale=None,
+             ptrs=True):
+        p = FAKE if ptrs else None
+        return lib.dsa_prep_cache_write(T, FAKE if pos else None, FAKE if rows else None, n_rows,
+                                        FAKE if cs else None, max_pos, dt, p, p, scale, p, p, None)
+
+    def queries(R=2, max_pos=128, dt=1, scale=None, H=128, ptrs=True):
+        p = FAKE if ptrs else None
+        return lib.dsa_prep_queries(R, FAKE, FAKE if ptrs else None, max_pos, dt, p, p, scale, H,
+                                    p, None)
+    assert keys(T=0) == OK and queries(R=0) == OK                 # empty: nothing launched
+    assert keys(T=-1) == INVALID and queries(R=-1) == INVALID
+    assert keys(pos=False) == INVALID and keys(rows=False) == INVALID and keys(cs=False) == INVALID
+    assert keys(ptrs=False) == INVALID and queries(ptrs=False) == INVALID
+    assert keys(n_rows=0) == INVALID
+    assert keys(max_pos=0) == INVALID and queries(max_pos=0) == INVALID
+    assert keys(dt=2) == INVALID and queries(dt=2) == INVALID     # fp8 without scales
+    assert keys(dt=1, scale=FAKE) == INVALID and queries(scale=FAKE) == INVALID
+    assert keys(dt=0) == UNSUPPORTED and queries(dt=0) == UNSUPPORTED
+    assert keys(dt=5) == INVALID and queries(dt=5) == INVALID
+    assert queries(H=0) == INVALID

@@ -280,3 +280,85 @@ def config(n: int, device="cpu", seed: Optional[int] = None) -> Workload:
         return decode(c5_lengths(seed), paged=True, seed=seed, device=device,
                       name="c5_paged_mixed_decode_b32")
     raise ValueError(f"no config {n}")
+
+
+# --------------------------------------------------------------------------- input prep
+
+@dataclass
+class PrepBatch:
+    """New tokens about to be written into the caches, and their query rows (one per token)."""
+    idx_dtype: str            # "bf16" | "fp8": the indexer cache format
+    positions: torch.Tensor   # int32 [T]
+    cache_rows: torch.Tensor  # int64 [T]: flat cache row of each token (-1: padding)
+    cos_sin: torch.Tensor     # f32 [max_pos, 64]: cos then sin of the 32 angles per position
+    k_idx_in: torch.Tensor    # bf16 [T, 128]
+    kv_in: torch.Tensor       # bf16 [T, 576]
+    k_cache: torch.Tensor     # [rows, 128]: bf16, or uint8 e4m3 codes (fp8); random contents
+    k_scale: Optional[torch.Tensor]   # f32 [rows] (fp8)
+    kv_cache: torch.Tensor    # bf16 [rows, 576]; random contents
+    q_idx_in: torch.Tensor    # bf16 [T, 64, 128]
+    q: torch.Tensor           # bf16 [T, H, 576]
+    seq_start: Optional[torch.Tensor]    # int64 [B] (contiguous cache) or None
+    page_table: Optional[torch.Tensor]   # int32 [B, max_pages] (paged cache) or None
+
+
+def rope_table(max_pos: int, base: float = 10000.0) -> torch.Tensor:
+    """A frequency schedule for the tests: angle i of position p is p * base^(-i/32)."""
+    i = torch.arange(32, dtype=torch.float64)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * base ** (-i / 32.0)[None, :]
+    return torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32)
+
+
+def prep_batch(lens, new, *, idx_dtype="fp8", paged=False, H=128, pad=0, seed=0,
+               device="cpu") -> PrepBatch:
+    """The last new[b] tokens of sequences of lengths lens[b], their cache rows in a contiguous
+    cache (sequences back to back) or a paged one (a random permutation of 64-token pages),
+    plus ``pad`` padding tokens (row -1); the caches start with random contents."""
+    lens = [int(x) for x in lens]
+    new = [int(x) for x in new]
+    if len(new) != len(lens) or min(new) < 1 or any(n > l for n, l in zip(new, lens)):
+        raise ValueError("each sequence needs 1 .. len new tokens")
+    sgen = torch.Generator()
+    sgen.manual_seed(seed)
+    pos = torch.cat([torch.arange(l - n, l, dtype=torch.int64) for n, l in zip(new, lens)])
+    seq = torch.cat([torch.full((n,), b, dtype=torch.int64) for b, n in enumerate(new)])
+    if paged:
+        pages = [(l + PAGE - 1) // PAGE for l in lens]
+        perm = torch.randperm(sum(pages), generator=sgen)
+        first = np.concatenate([[0], np.cumsum(pages)[:-1]]).astype(np.int64)
+        phys = perm[torch.from_numpy(first)[seq] + pos // PAGE]
+        rows = phys * PAGE + pos % PAGE
+        n_rows = sum(pages) * PAGE
+        page_table = torch.full((len(lens), max(pages)), -1, dtype=torch.int32)
+        for b, (f, n) in enumerate(zip(first, pages)):
+            page_table[b, :n] = perm[f:f + n].to(torch.int32)
+        start = None
+    else:
+        start = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64))
+        rows = start[seq] + pos
+        n_rows = sum(lens)
+        page_table = None
+    rows = torch.cat([rows, torch.full((pad,), -1, dtype=torch.int64)])
+    pos = torch.cat([pos, torch.zeros(pad, dtype=torch.int64)]).to(torch.int32)
+    T = int(pos.numel())
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    k_idx_in = _normal((T, 128), gen, device).to(torch.bfloat16)
+    kv_in = _normal((T, 576), gen, device).to(torch.bfloat16)
+    q_idx_in = _normal((T, 64, 128), gen, device).to(torch.bfloat16)
+    q = _normal((T, H, 576), gen, device).to(torch.bfloat16)
+    kv_cache = _normal((n_rows, 576), gen, device).to(torch.bfloat16)
+    if idx_dtype == "fp8":
+        codes = torch.randint(0, 0x7F, (n_rows, 128), generator=gen, device=device, dtype=torch.int32)
+        sign = torch.randint(0, 2, (n_rows, 128), generator=gen, device=device, dtype=torch.int32)
+        k_cache = (codes | (sign << 7)).to(torch.uint8)
+        k_scale = torch.rand((n_rows,), generator=gen, device=device, dtype=torch.float32)
+    elif idx_dtype == "bf16":
+        k_cache = _normal((n_rows, 128), gen, device).to(torch.bfloat16)
+        k_scale = None
+    else:
+        raise ValueError(idx_dtype)
+    return PrepBatch(idx_dtype, pos.to(device), rows.to(device),
+                     rope_table(max(lens) + 1).to(device), k_idx_in, kv_in, k_cache, k_scale,
+                     kv_cache, q_idx_in, q, None if start is None else start.to(device),
+                     None if page_table is None else page_table.to(device))
