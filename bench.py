@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="timed step calls the indexer, the top-k and the attention separately "
                         "(default: the one-call decode)")
+    p.add_argument("--prep", action="store_true",
+                   help="time the indexer-input and cache-write prep of the workload's new tokens "
+                        "(one per decode row; every token of a prefill) instead of the hot path")
     p.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
                    help="no GPU work: 'trace NAME STATS_CSV CMD' writes profiles/NAME.md from a "
                         "rocprofv3 --kernel-trace --stats run; 'pmc KERNEL FETCH_CSV WRITE_CSV "
@@ -175,6 +178,69 @@ def summarize_pmc(kernel, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
                 f"| kernel source sha256[:16] | `{d['source_sha']}` |\n")
 
 
+def prep_bench(args):
+    """One JSON line: the prep step (dsa_prep: keys, latent entries and queries of the new
+    tokens in one launch) of a workload, captured in a HIP graph and replayed after a cache
+    flush."""
+    import torch
+
+    import sparse_attention_08_amd as dsa
+    import workloads
+
+    if args.config == 1:
+        raise SystemExit("the prep is defined for the 64 x 128 indexer and 576-d entries")
+    spec = {2: ([8192] * 64, [1] * 64, "bf16", False), 3: ([16384], [16384], "bf16", False),
+            4: ([131072] * 8, [1] * 8, "fp8", False),
+            5: (None, None, "bf16", True)}[args.config]
+    lens, new, dt, paged = spec
+    if lens is None:
+        lens = workloads.c5_lengths(1000 + args.config)
+        new = [1] * len(lens)
+    b = workloads.prep_batch(lens, new, idx_dtype=dt, paged=paged, seed=1000 + args.config,
+                             device="cuda")
+    T = int(b.positions.numel())
+    kc, kvc = b.k_cache, b.kv_cache
+    fp8 = dt == "fp8"
+    qi = torch.empty((T, 64, 128), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+    qs = torch.empty((T, 64), dtype=torch.float32, device="cuda") if fp8 else None
+
+    def step():
+        dsa.prep(b.positions, b.cache_rows, b.cos_sin, b.k_idx_in, kc, b.kv_in, kvc, b.q_idx_in, qi,
+                 b.q, k_idx_scale=b.k_scale, q_idx_scale=qs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step()
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        if flush is not None:
+            flush.sum()
+        e[0].record(); graph.replay(); e[1].record()
+    torch.cuda.synchronize()
+    ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+    eb = 1 if fp8 else 2
+    key_b = T * (256 + 1152 + 4 + 8 + 256 + 128 * eb + (4 if fp8 else 0) + 1152)
+    qry_b = T * (4 + 256 + 64 * 256 + 64 * 128 * eb + (256 if fp8 else 0) + 2 * 128 * 128)
+    print(json.dumps({
+        "metric": "indexer-input and cache-write prep time per step", "value": ms * 1e3,
+        "unit": "us", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "dtype": dt, "data": "synthetic", "launch_mode": "hip_graph",
+        "config": {"workload": f"prep of config {args.config}", "new_tokens": T,
+                   "context": max(lens), "paged": paged,
+                   "cache_flushed_between_steps": flush is not None},
+        "algorithmic_bytes_per_step": key_b + qry_b,
+        "hbm_frac_of_step": (key_b + qry_b) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}))
+
+
 def cpu_baseline(wl_host, n_rows: int):
     """The fp64 oracle (as it stands) on the first n_rows rows of the same batch."""
     import numpy as np
@@ -220,6 +286,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is a single-GPU "
               f"build and measures no multi-GPU configuration.", file=sys.stderr)
         sys.exit(2)
+    if args.prep:
+        prep_bench(args)
+        return
     import torch
 
     import sparse_attention_08_amd as dsa

@@ -261,6 +261,13 @@ int dsa_prep_cache_write(int num_tokens, const int32_t *positions, const int64_t
 int dsa_prep_queries(int num_rows, const int32_t *positions, const float *cos_sin,
                      int max_position, int idx_dtype, const void *q_idx_in, void *q_idx,
                      float *q_idx_scale, int n_heads, void *q, void *stream);
+/* Both of the above in one launch for num_tokens new tokens that are also the query rows
+ * (decode, or a prefill chunk): positions[t] serves the key side and query row t. */
+int dsa_prep(int num_tokens, const int32_t *positions, const int64_t *cache_rows,
+             int64_t num_cache_rows, const float *cos_sin, int max_position, int idx_dtype,
+             const void *k_idx_in, void *k_idx_cache, float *k_idx_scale, const void *kv_in,
+             void *kv_cache, const void *q_idx_in, void *q_idx, float *q_idx_scale, int n_heads,
+             void *q, void *stream);
 
 #ifdef __cplusplus
 }

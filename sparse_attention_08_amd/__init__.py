@@ -87,6 +87,9 @@ def load_library() -> ctypes.CDLL:
     lib.dsa_prep_cache_write.restype = i32
     lib.dsa_prep_queries.argtypes = [i32, vp, vp, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.dsa_prep_queries.restype = i32
+    lib.dsa_prep.argtypes = [i32, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                             vp, vp]
+    lib.dsa_prep.restype = i32
     _lib = lib
     return lib
 
@@ -422,3 +425,36 @@ def prep_queries(positions, cos_sin, q_idx_in, q_idx, q, q_idx_scale=None):
                              dtype_code(q_idx), _ptr(q_idx_in), _ptr(q_idx), _ptr(q_idx_scale),
                              int(q.shape[1]), _ptr(q), _stream())
     _check(s, "dsa_prep_queries")
+
+
+def prep(positions, cache_rows, cos_sin, k_idx_in, k_idx_cache, kv_in, kv_cache, q_idx_in, q_idx,
+         q, k_idx_scale=None, q_idx_scale=None):
+    """:func:`prep_cache_write` and :func:`prep_queries` for new tokens that are also the query
+    rows (decode, or a prefill chunk), in one launch."""
+    lib = load_library()
+    for t, n, d in ((positions, "positions", (torch.int32,)), (cache_rows, "cache_rows", (torch.int64,)),
+                    (cos_sin, "cos_sin", (torch.float32,)), (k_idx_in, "k_idx_in", (torch.bfloat16,)),
+                    (kv_in, "kv_in", (torch.bfloat16,)), (kv_cache, "kv_cache", (torch.bfloat16,)),
+                    (q_idx_in, "q_idx_in", (torch.bfloat16,)), (q, "q", (torch.bfloat16,))):
+        _dev(t, n, d)
+    for t, n in ((k_idx_cache, "k_idx_cache"), (q_idx, "q_idx")):
+        _dev(t, n, (torch.bfloat16, torch.float8_e4m3fn, torch.uint8))
+    for t, n in ((k_idx_scale, "k_idx_scale"), (q_idx_scale, "q_idx_scale")):
+        if t is not None:
+            _dev(t, n, (torch.float32,))
+    if dtype_code(k_idx_cache) != dtype_code(q_idx):
+        raise ValueError("k_idx_cache and q_idx must have the same format")
+    T = int(positions.numel())
+    n_rows = kv_cache.numel() // 576
+    if k_idx_in.numel() != T * 128 or kv_in.numel() != T * 576 or cache_rows.numel() != T \
+            or q_idx_in.numel() != T * 64 * 128 or q_idx.numel() != T * 64 * 128 or q.dim() != 3 \
+            or q.shape[0] != T or q.shape[2] != 576 or k_idx_cache.numel() != n_rows * 128 \
+            or cos_sin.shape[-1] != 64:
+        raise ValueError("shapes: k_idx_in [T,128], kv_in [T,576], cache_rows [T], q_idx_in / "
+                         "q_idx [T,64,128], q [T,H,576], caches of equal rows, cos_sin [P,64]")
+    s = lib.dsa_prep(T, _ptr(positions), _ptr(cache_rows), n_rows, _ptr(cos_sin),
+                     int(cos_sin.shape[0]), dtype_code(k_idx_cache), _ptr(k_idx_in),
+                     _ptr(k_idx_cache), _ptr(k_idx_scale), _ptr(kv_in), _ptr(kv_cache),
+                     _ptr(q_idx_in), _ptr(q_idx), _ptr(q_idx_scale), int(q.shape[1]), _ptr(q),
+                     _stream())
+    _check(s, "dsa_prep")

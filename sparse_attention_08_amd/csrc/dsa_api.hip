@@ -242,6 +242,37 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
   return status_of(e);
 }
 
+int prep_keys_check(const dsa::PrepKeys &k, bool fp8) {
+  if (k.T < 0 || k.cache_rows < 1) return DSA_ERR_INVALID_ARG;
+  if (k.T == 0) return DSA_OK;
+  if (!k.pos || !k.rows || !k.k_in || !k.k_cache || !k.kv_in || !k.kv_cache)
+    return DSA_ERR_INVALID_ARG;
+  return (fp8 != (k.k_scale != nullptr)) ? DSA_ERR_INVALID_ARG : DSA_OK;
+}
+
+int prep_queries_check(const dsa::PrepQueries &q, bool fp8) {
+  if (q.R < 0 || q.n_heads < 1) return DSA_ERR_INVALID_ARG;
+  if (q.R == 0) return DSA_OK;
+  if (!q.pos || !q.qi_in || !q.qi_out || !q.q) return DSA_ERR_INVALID_ARG;
+  return (fp8 != (q.qi_scale != nullptr)) ? DSA_ERR_INVALID_ARG : DSA_OK;
+}
+
+int prep_common(const dsa::PrepKeys &keys, const dsa::PrepQueries &queries, const float *cos_sin,
+                int max_position, int idx_dtype, void *stream) {
+  if (max_position < 1) return DSA_ERR_INVALID_ARG;
+  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3)
+    return DSA_ERR_INVALID_ARG;
+  const bool fp8 = idx_dtype == DSA_FP8_E4M3;
+  int st = prep_keys_check(keys, fp8);
+  if (st == DSA_OK) st = prep_queries_check(queries, fp8);
+  if (st != DSA_OK) return st;
+  if (idx_dtype == DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (keys.T == 0 && queries.R == 0) return DSA_OK;
+  if (!cos_sin) return DSA_ERR_INVALID_ARG;
+  return status_of(dsa::launch_prep(queries, keys, cos_sin, max_position, fp8,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,34 +421,29 @@ int dsa_prep_cache_write(int num_tokens, const int32_t *positions, const int64_t
                          int64_t num_cache_rows, const float *cos_sin, int max_position,
                          int idx_dtype, const void *k_idx_in, void *k_idx_cache,
                          float *k_idx_scale, const void *kv_in, void *kv_cache, void *stream) {
-  if (num_tokens < 0 || max_position < 1 || num_cache_rows < 1) return DSA_ERR_INVALID_ARG;
-  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3)
-    return DSA_ERR_INVALID_ARG;
-  if (idx_dtype == DSA_F32) return DSA_ERR_UNSUPPORTED;
-  if (num_tokens == 0) return DSA_OK;
-  if (!positions || !cache_rows || !cos_sin || !k_idx_in || !k_idx_cache || !kv_in || !kv_cache)
-    return DSA_ERR_INVALID_ARG;
-  if ((idx_dtype == DSA_FP8_E4M3) != (k_idx_scale != nullptr)) return DSA_ERR_INVALID_ARG;
-  return status_of(dsa::launch_prep_keys(num_tokens, positions, cache_rows, num_cache_rows,
-                                         cos_sin, max_position, idx_dtype == DSA_FP8_E4M3,
-                                         k_idx_in, k_idx_cache, k_idx_scale, kv_in, kv_cache,
-                                         static_cast<hipStream_t>(stream)));
+  const dsa::PrepKeys keys{num_tokens, positions, cache_rows, num_cache_rows,
+                           k_idx_in, k_idx_cache, k_idx_scale, kv_in, kv_cache};
+  const dsa::PrepQueries none{0, nullptr, nullptr, nullptr, nullptr, 1, nullptr};
+  return prep_common(keys, none, cos_sin, max_position, idx_dtype, stream);
 }
 
 int dsa_prep_queries(int num_rows, const int32_t *positions, const float *cos_sin,
                      int max_position, int idx_dtype, const void *q_idx_in, void *q_idx,
                      float *q_idx_scale, int n_heads, void *q, void *stream) {
-  if (num_rows < 0 || max_position < 1 || n_heads < 1) return DSA_ERR_INVALID_ARG;
-  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3)
-    return DSA_ERR_INVALID_ARG;
-  if (idx_dtype == DSA_F32) return DSA_ERR_UNSUPPORTED;
-  if (num_rows == 0) return DSA_OK;
-  if (!positions || !cos_sin || !q_idx_in || !q_idx || !q) return DSA_ERR_INVALID_ARG;
-  if ((idx_dtype == DSA_FP8_E4M3) != (q_idx_scale != nullptr)) return DSA_ERR_INVALID_ARG;
-  return status_of(dsa::launch_prep_queries(num_rows, positions, cos_sin, max_position,
-                                            idx_dtype == DSA_FP8_E4M3, q_idx_in, q_idx,
-                                            q_idx_scale, n_heads, q,
-                                            static_cast<hipStream_t>(stream)));
+  const dsa::PrepKeys none{0, nullptr, nullptr, 1, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const dsa::PrepQueries queries{num_rows, positions, q_idx_in, q_idx, q_idx_scale, n_heads, q};
+  return prep_common(none, queries, cos_sin, max_position, idx_dtype, stream);
+}
+
+int dsa_prep(int num_tokens, const int32_t *positions, const int64_t *cache_rows,
+             int64_t num_cache_rows, const float *cos_sin, int max_position, int idx_dtype,
+             const void *k_idx_in, void *k_idx_cache, float *k_idx_scale, const void *kv_in,
+             void *kv_cache, const void *q_idx_in, void *q_idx, float *q_idx_scale, int n_heads,
+             void *q, void *stream) {
+  const dsa::PrepKeys keys{num_tokens, positions, cache_rows, num_cache_rows,
+                           k_idx_in, k_idx_cache, k_idx_scale, kv_in, kv_cache};
+  const dsa::PrepQueries queries{num_tokens, positions, q_idx_in, q_idx, q_idx_scale, n_heads, q};
+  return prep_common(keys, queries, cos_sin, max_position, idx_dtype, stream);
 }
 
 }  // extern "C"

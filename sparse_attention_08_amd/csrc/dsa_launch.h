@@ -84,16 +84,32 @@ hipError_t launch_mla_bf16_select(const RowsHost &rows, bool paged, int H, float
                                   int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream);
 
 // ---- indexer-input and cache-write prep ----
-// One new token per entry: indexer key (bf16 [T,128]) rotated and written as bf16 or e4m3
-// (+ scale) to cache row rows[t], latent entry (bf16 [T,576]) rotated and written there too.
-hipError_t launch_prep_keys(int T, const int32_t *pos, const int64_t *rows, int64_t cache_rows,
-                            const float *cos_sin, int max_pos, bool fp8, const void *k_in,
-                            void *k_cache, float *k_scale, const void *kv_in, void *kv_cache,
-                            hipStream_t stream);
-// Query rows: 64 indexer heads rotated to bf16 or e4m3 (+ per-head scale), n_heads MLA heads
-// rotated in place.
-hipError_t launch_prep_queries(int R, const int32_t *pos, const float *cos_sin, int max_pos,
-                               bool fp8, const void *qi_in, void *qi_out, float *qi_scale,
-                               int n_heads, void *q, hipStream_t stream);
+// Query rows (R of them, R may be 0): 64 indexer heads rotated to bf16 or e4m3 (+ per-head
+// scale), n_heads MLA heads rotated in place.
+struct PrepQueries {
+  int R;
+  const int32_t *pos;
+  const void *qi_in;
+  void *qi_out;
+  float *qi_scale;
+  int n_heads;
+  void *q;
+};
+// New tokens (T of them, T may be 0): indexer key (bf16 [T,128]) rotated and written as bf16 or
+// e4m3 (+ scale) to cache row rows[t], latent entry (bf16 [T,576]) rotated and written there.
+struct PrepKeys {
+  int T;
+  const int32_t *pos;
+  const int64_t *rows;
+  int64_t cache_rows;
+  const void *k_in;
+  void *k_cache;
+  float *k_scale;
+  const void *kv_in;
+  void *kv_cache;
+};
+// Both sides in one launch.
+hipError_t launch_prep(const PrepQueries &queries, const PrepKeys &keys, const float *cos_sin,
+                       int max_pos, bool fp8, hipStream_t stream);
 
 }  // namespace dsa

@@ -76,82 +76,83 @@ __device__ __forceinline__ void indexer_vec(uint32_t w, const IdxAngles &an, uin
   }
 }
 
-// One wave: dims 512..575 of the 576-dim MLA vector `in` rotated (interleaved) into `out`;
-// with COPY the latent dims 0..511 are copied too (16 bytes per lane).  `in` may be `out`.
-template <bool COPY>
-__device__ __forceinline__ void mla_vec(const uint16_t *in, const float *cs, uint16_t *out,
-                                        int lane) {
-  if constexpr (COPY)
-    reinterpret_cast<i32x4 *>(out)[lane] = reinterpret_cast<const i32x4 *>(in)[lane];
-  if (lane < 32) {
-    const uint32_t w = reinterpret_cast<const uint32_t *>(in + 512)[lane];
-    float ya, yb;
-    rot_pair(bf16_bits_to_f32(w & 0xffffu), bf16_bits_to_f32(w >> 16), cs[lane], cs[32 + lane], ya,
-             yb);
-    reinterpret_cast<uint32_t *>(out + 512)[lane] = pack_bf16x2(ya, yb);
-  }
-}
-
+// Key side, one wave per token t: every input load (the token's position and cache row, its
+// indexer key and latent entry) is issued before the position is checked.
 template <bool FP8>
-__global__ __launch_bounds__(kPrepThreads) void prep_keys_kernel(
-    int T, const int32_t *__restrict__ pos, const int64_t *__restrict__ rows, int64_t cache_rows,
-    const float *__restrict__ cos_sin, int max_pos, const uint16_t *__restrict__ k_in,
-    uint8_t *__restrict__ k_cache, float *__restrict__ k_scale, const uint16_t *__restrict__ kv_in,
-    uint16_t *__restrict__ kv_cache) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
-  if (t >= T) return;
+__device__ __forceinline__ void prep_key_wave(int t, const int32_t *__restrict__ pos,
+                                              const int64_t *__restrict__ rows, int64_t cache_rows,
+                                              const float *__restrict__ cos_sin, int max_pos,
+                                              const uint16_t *__restrict__ k_in,
+                                              uint8_t *__restrict__ k_cache,
+                                              float *__restrict__ k_scale,
+                                              const uint16_t *__restrict__ kv_in,
+                                              uint16_t *__restrict__ kv_cache, int lane) {
   const int p = pos[t];
   const int64_t r = rows[t];
+  const uint32_t w = reinterpret_cast<const uint32_t *>(k_in + (int64_t)t * 128)[lane];
+  const uint16_t *kvt = kv_in + (int64_t)t * 576;
+  const i32x4 latent = reinterpret_cast<const i32x4 *>(kvt)[lane];
+  const uint32_t tail = lane < 32 ? reinterpret_cast<const uint32_t *>(kvt + 512)[lane] : 0u;
   if (p < 0 || p >= max_pos || r < 0 || r >= cache_rows) return;   // uniform per wave
   const float *cs = cos_sin + (int64_t)p * 64;
-  const uint32_t w = reinterpret_cast<const uint32_t *>(k_in + (int64_t)t * 128)[lane];
   const IdxAngles an = idx_angles(cs, lane);
-  mla_vec<true>(kv_in + (int64_t)t * 576, cs, kv_cache + r * 576, lane);
+  uint16_t *kvr = kv_cache + r * 576;
+  reinterpret_cast<i32x4 *>(kvr)[lane] = latent;
+  if (lane < 32) {
+    float ya, yb;
+    rot_pair(bf16_bits_to_f32(tail & 0xffffu), bf16_bits_to_f32(tail >> 16), cs[lane],
+             cs[32 + lane], ya, yb);
+    reinterpret_cast<uint32_t *>(kvr + 512)[lane] = pack_bf16x2(ya, yb);
+  }
   indexer_vec<FP8>(w, an, k_cache + r * 128 * (FP8 ? 1 : 2), FP8 ? k_scale + r : nullptr, lane);
 }
 
-// Grid (rows, 4): part y of row r rotates indexer heads 16y .. 16y + 15 (4 per wave) and a
-// quarter of the MLA heads (one pair per thread and step, in place).
+// Query side, one workgroup per (row r, part): part rotates indexer heads 16 part .. + 15 (4
+// per wave) and a quarter of the MLA heads (one pair per thread and step, in place).  Every
+// load of the share is issued before the position is checked and before the first store
+// (the outputs may alias the inputs, so the compiler would not hoist them itself).
 template <bool FP8>
-__global__ __launch_bounds__(kPrepThreads) void prep_queries_kernel(
-    int R, const int32_t *__restrict__ pos, const float *__restrict__ cos_sin, int max_pos,
-    const uint16_t *qi_in, uint8_t *qi_out, float *__restrict__ qi_scale, int n_heads,
-    uint16_t *q) {
-  const int r = blockIdx.x, part = blockIdx.y;
-  const int p = pos[r];
-  if (p < 0 || p >= max_pos) return;
-  const float *cs = cos_sin + (int64_t)p * 64;
+__device__ __forceinline__ void prep_query_block(int r, int part,
+                                                 const int32_t *__restrict__ pos,
+                                                 const float *__restrict__ cos_sin, int max_pos,
+                                                 const uint16_t *qi_in, uint8_t *qi_out,
+                                                 float *__restrict__ qi_scale, int n_heads,
+                                                 uint16_t *q) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // every load of the workgroup's share is issued before the first store (the outputs may
-  // alias the inputs, so the compiler would not hoist them itself)
+  const int p = pos[r];
   const int64_t v0 = (int64_t)r * 64 + 16 * part + 4 * wave;
   uint32_t w[4];
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh) w[hh] = reinterpret_cast<const uint32_t *>(qi_in + (v0 + hh) * 128)[lane];
+  for (int hh = 0; hh < 4; ++hh)
+    w[hh] = reinterpret_cast<const uint32_t *>(qi_in + (v0 + hh) * 128)[lane];
   const int per_part = (n_heads + 3) / 4;
   const int h0 = part * per_part, h1 = min(n_heads, h0 + per_part);
+  const int n_pairs = max(h1 - h0, 0) * 32;
   constexpr int kPairSteps = 4;   // pairs per thread held at once: 32 heads per part
+  const int i = threadIdx.x & 31;   // a thread's pairs all use angle i
   uint32_t *pr[kPairSteps];
   uint32_t pv[kPairSteps];
-  const int i = threadIdx.x & 31;   // the angle is the same for every step of a thread
-  const float c = cs[i], sn = cs[32 + i];
-  const IdxAngles an = idx_angles(cs, lane);
-  for (int j0 = 0; j0 < (h1 - h0) * 32; j0 += kPairSteps * kPrepThreads) {
+  auto load_pairs = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < kPairSteps; ++u) {
       const int j = j0 + u * kPrepThreads + threadIdx.x;
-      pr[u] = j < (h1 - h0) * 32
-                  ? reinterpret_cast<uint32_t *>(q + ((int64_t)r * n_heads + h0 + (j >> 5)) * 576 + 512) + i
-                  : nullptr;
+      pr[u] = j < n_pairs ? reinterpret_cast<uint32_t *>(
+                                q + ((int64_t)r * n_heads + h0 + (j >> 5)) * 576 + 512) + i
+                          : nullptr;
       pv[u] = pr[u] ? *pr[u] : 0u;
     }
-    if (j0 == 0) {
+  };
+  load_pairs(0);
+  if (p < 0 || p >= max_pos) return;   // uniform per workgroup
+  const float *cs = cos_sin + (int64_t)p * 64;
+  const float c = cs[i], sn = cs[32 + i];
+  const IdxAngles an = idx_angles(cs, lane);
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-        indexer_vec<FP8>(w[hh], an, qi_out + (v0 + hh) * 128 * (FP8 ? 1 : 2),
-                         FP8 ? qi_scale + v0 + hh : nullptr, lane);
-    }
+  for (int hh = 0; hh < 4; ++hh)
+    indexer_vec<FP8>(w[hh], an, qi_out + (v0 + hh) * 128 * (FP8 ? 1 : 2),
+                     FP8 ? qi_scale + v0 + hh : nullptr, lane);
+  for (int j0 = 0; j0 < n_pairs; j0 += kPairSteps * kPrepThreads) {
+    if (j0 > 0) load_pairs(j0);
 #pragma unroll
     for (int u = 0; u < kPairSteps; ++u) {
       if (!pr[u]) continue;
@@ -160,45 +161,49 @@ __global__ __launch_bounds__(kPrepThreads) void prep_queries_kernel(
       *pr[u] = pack_bf16x2(ya, yb);
     }
   }
-  if (h1 <= h0) {   // no MLA heads in this part (fewer than 4 heads in all)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh)
-      indexer_vec<FP8>(w[hh], an, qi_out + (v0 + hh) * 128 * (FP8 ? 1 : 2),
-                       FP8 ? qi_scale + v0 + hh : nullptr, lane);
+}
+
+// One launch for both sides: workgroups [0, 4 R) take the query rows, the rest take the new
+// tokens' keys (kPrepWaves tokens each).
+template <bool FP8>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(
+    int R, int T, const int32_t *__restrict__ q_pos, const int32_t *__restrict__ k_pos,
+    const float *__restrict__ cos_sin, int max_pos, const uint16_t *qi_in, uint8_t *qi_out,
+    float *__restrict__ qi_scale, int n_heads, uint16_t *q, const int64_t *__restrict__ rows,
+    int64_t cache_rows, const uint16_t *__restrict__ k_in, uint8_t *__restrict__ k_cache,
+    float *__restrict__ k_scale, const uint16_t *__restrict__ kv_in,
+    uint16_t *__restrict__ kv_cache) {
+  const int b = blockIdx.x;
+  if (b < 4 * R) {
+    prep_query_block<FP8>(b >> 2, b & 3, q_pos, cos_sin, max_pos, qi_in, qi_out, qi_scale,
+                          n_heads, q);
+    return;
   }
+  const int t = (b - 4 * R) * kPrepWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  prep_key_wave<FP8>(t, k_pos, rows, cache_rows, cos_sin, max_pos, k_in, k_cache, k_scale, kv_in,
+                     kv_cache, threadIdx.x & 63);
 }
 
-hipError_t launch_prep_keys(int T, const int32_t *pos, const int64_t *rows, int64_t cache_rows,
-                            const float *cos_sin, int max_pos, bool fp8, const void *k_in,
-                            void *k_cache, float *k_scale, const void *kv_in, void *kv_cache,
-                            hipStream_t stream) {
-  const unsigned grid = (unsigned)((T + kPrepWaves - 1) / kPrepWaves);
-  const uint16_t *ki = static_cast<const uint16_t *>(k_in);
-  const uint16_t *kvi = static_cast<const uint16_t *>(kv_in);
-  uint8_t *kc = static_cast<uint8_t *>(k_cache);
-  uint16_t *kvc = static_cast<uint16_t *>(kv_cache);
+hipError_t launch_prep(const PrepQueries &qa, const PrepKeys &ka, const float *cos_sin,
+                       int max_pos, bool fp8, hipStream_t stream) {
+  const unsigned grid = 4u * (unsigned)qa.R + (unsigned)((ka.T + kPrepWaves - 1) / kPrepWaves);
+  if (grid == 0) return hipSuccess;
+  const auto *qi = static_cast<const uint16_t *>(qa.qi_in);
+  auto *qo = static_cast<uint8_t *>(qa.qi_out);
+  auto *qq = static_cast<uint16_t *>(qa.q);
+  const auto *ki = static_cast<const uint16_t *>(ka.k_in);
+  auto *kc = static_cast<uint8_t *>(ka.k_cache);
+  const auto *kvi = static_cast<const uint16_t *>(ka.kv_in);
+  auto *kvc = static_cast<uint16_t *>(ka.kv_cache);
   if (fp8)
-    prep_keys_kernel<true><<<grid, kPrepThreads, 0, stream>>>(T, pos, rows, cache_rows, cos_sin,
-                                                              max_pos, ki, kc, k_scale, kvi, kvc);
+    prep_kernel<true><<<grid, kPrepThreads, 0, stream>>>(
+        qa.R, ka.T, qa.pos, ka.pos, cos_sin, max_pos, qi, qo, qa.qi_scale, qa.n_heads, qq, ka.rows,
+        ka.cache_rows, ki, kc, ka.k_scale, kvi, kvc);
   else
-    prep_keys_kernel<false><<<grid, kPrepThreads, 0, stream>>>(T, pos, rows, cache_rows, cos_sin,
-                                                               max_pos, ki, kc, k_scale, kvi, kvc);
-  return hipGetLastError();
-}
-
-hipError_t launch_prep_queries(int R, const int32_t *pos, const float *cos_sin, int max_pos,
-                               bool fp8, const void *qi_in, void *qi_out, float *qi_scale,
-                               int n_heads, void *q, hipStream_t stream) {
-  const dim3 grid((unsigned)R, 4);
-  const uint16_t *qi = static_cast<const uint16_t *>(qi_in);
-  uint8_t *qo = static_cast<uint8_t *>(qi_out);
-  uint16_t *qq = static_cast<uint16_t *>(q);
-  if (fp8)
-    prep_queries_kernel<true><<<grid, kPrepThreads, 0, stream>>>(R, pos, cos_sin, max_pos, qi, qo,
-                                                                 qi_scale, n_heads, qq);
-  else
-    prep_queries_kernel<false><<<grid, kPrepThreads, 0, stream>>>(R, pos, cos_sin, max_pos, qi, qo,
-                                                                  qi_scale, n_heads, qq);
+    prep_kernel<false><<<grid, kPrepThreads, 0, stream>>>(
+        qa.R, ka.T, qa.pos, ka.pos, cos_sin, max_pos, qi, qo, qa.qi_scale, qa.n_heads, qq, ka.rows,
+        ka.cache_rows, ki, kc, ka.k_scale, kvi, kvc);
   return hipGetLastError();
 }
 

@@ -219,3 +219,12 @@ def test_prep_validation(lib):
     assert keys(dt=0) == UNSUPPORTED and queries(dt=0) == UNSUPPORTED
     assert keys(dt=5) == INVALID and queries(dt=5) == INVALID
     assert queries(H=0) == INVALID
+
+    def both(T=4, dt=1, ks=None, qs=None, H=128, ptrs=True):
+        p = FAKE if ptrs else None
+        return lib.dsa_prep(T, FAKE, FAKE, 64, FAKE, 128, dt, p, p, ks, p, p, p, p, qs, H, p, None)
+    assert both(T=0) == OK
+    assert both(T=-2) == INVALID and both(ptrs=False) == INVALID and both(H=0) == INVALID
+    assert both(dt=2, ks=FAKE) == INVALID and both(dt=2, qs=FAKE) == INVALID   # one scale missing
+    assert both(dt=1, qs=FAKE) == INVALID
+    assert both(dt=0) == UNSUPPORTED

@@ -72,6 +72,26 @@ def test_prep_bit_exact(idx_dtype, paged):
         assert np.array_equal(raw(qs), eqs)
 
 
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_one_call_prep_equals_the_two_calls(idx_dtype):
+    """dsa_prep (both sides in one launch) writes the same bytes as dsa_prep_cache_write followed
+    by dsa_prep_queries."""
+    b = workloads.prep_batch([900, 65, 3000], [33, 1, 64], idx_dtype=idx_dtype, paged=True,
+                             seed=46, device=DEV)
+    kc, kvc, ks = _gpu_keys(b)
+    qi, qs, q = _gpu_queries(b)
+    kc2, kvc2, q2 = b.k_cache.clone(), b.kv_cache.clone(), b.q.clone()
+    ks2 = None if b.k_scale is None else b.k_scale.clone()
+    qi2, qs2 = torch.zeros_like(qi), None if qs is None else torch.zeros_like(qs)
+    say(f"one-call prep {idx_dtype}")
+    dsa.prep(b.positions, b.cache_rows, b.cos_sin, b.k_idx_in, kc2, b.kv_in, kvc2, b.q_idx_in, qi2,
+             q2, k_idx_scale=ks2, q_idx_scale=qs2)
+    assert torch.equal(kc2, kc) and torch.equal(kvc2, kvc) and torch.equal(q2, q)
+    assert torch.equal(qi2, qi)
+    if idx_dtype == "fp8":
+        assert torch.equal(ks2, ks) and torch.equal(qs2, qs)
+
+
 def test_prep_in_place_bf16_queries_and_positions_out_of_range():
     """bf16 indexer queries rotated in place equal the out-of-place result; a position outside
     the table leaves its row untouched (keys and queries)."""
