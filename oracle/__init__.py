@@ -74,6 +74,9 @@ def _load():
         lib.oref_e4m3_codes.argtypes = [vp, vp, i64]
         lib.oref_prep_keys.argtypes = [i32, vp, vp, i64, vp, i32, ctypes.c_int, vp, vp, vp, vp, vp]
         lib.oref_prep_queries.argtypes = [i32, vp, vp, i32, ctypes.c_int, i32, vp, vp, vp, i32, vp]
+        lib.oref_mha_decompress.argtypes = [i32, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int]
+        lib.oref_mha.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.POINTER(_Rows), vp, i32, dbl, vp,
+                                 i32, vp, vp, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -299,3 +302,43 @@ def prep_queries(idx_dtype: str, pos, cos_sin, qi_in, q):
     if rc:
         raise ValueError("oref_prep_queries rejected its arguments")
     return qi_out, qs, q
+
+
+# --------------------------------------------------------------------------- masked MHA mode
+
+def mha_decompress(kv, w_uk, w_uv, n_threads=None):
+    """Per-head keys [rows, H, 192] and values [rows, H, 128] (fp64) of the latent cache rows
+    kv [rows, 576] (bf16 bits) with W_UK, W_UV [H, 128, 512] (bf16 bits)."""
+    kv = _c(kv, np.uint16).reshape(-1, 576)
+    w_uk = _c(w_uk, np.uint16)
+    w_uv = _c(w_uv, np.uint16)
+    H = int(w_uk.shape[0])
+    n = int(kv.shape[0])
+    k = np.empty((n, H, 192), dtype=np.float64)
+    v = np.empty((n, H, 128), dtype=np.float64)
+    rc = _load().oref_mha_decompress(n, H, _ptr(kv), _ptr(w_uk), _ptr(w_uv), _ptr(k), _ptr(v),
+                                     n_threads or default_threads())
+    if rc:
+        raise ValueError("oref_mha_decompress rejected its arguments")
+    return k, v
+
+
+def mha(q, k, v, rows: Rows, scale: float, idx=None, which=None, n_threads=None):
+    """Masked MHA over decompressed keys / values: out [n_which, H, 128], lse [n_which, H].
+    q [R, H, 192] bf16 bits; idx [R, topk] (a set per row) or None for dense causal."""
+    q = _c(q, np.uint16)
+    H = int(q.shape[1])
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    wh = _which(rows, which)
+    idx_c = None if idx is None else _c(idx, np.int32)
+    topk = 0 if idx_c is None else int(idx_c.shape[1])
+    out = np.zeros((wh.size, H, 128), dtype=np.float64)
+    lse = np.zeros((wh.size, H), dtype=np.float64)
+    st = rows._struct()
+    rc = _load().oref_mha(H, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st), _ptr(idx_c), topk,
+                          float(scale), _ptr(wh), wh.size, _ptr(out), _ptr(lse),
+                          n_threads or default_threads())
+    if rc:
+        raise ValueError("oref_mha rejected its arguments")
+    return out, lse

@@ -530,3 +530,119 @@ void oref_e4m3_codes(const float *src, uint8_t *dst, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) dst[i] = oref_e4m3_code(src[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Masked MHA mode for short prefill ([R], "短序列优化": short prefill runs  */
+/* DSA as masked MHA).  Per head h the latent entry c_s (512) and RoPE key   */
+/* kr_s (64) of position s give the 192-dim key [W_UK[h] c_s | kr_s] and the */
+/* 128-dim value W_UV[h] c_s ([M] "Multi-head latent attention": 128 heads,  */
+/* 128 nope + 64 rope query/key dims, 128 value dims).  A row attends over   */
+/* its top-k positions (as a set), or over every position below its length  */
+/* when no idx is given (dense causal: what the top-k selects whenever the  */
+/* row has at most k positions).                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int H;
+    const uint16_t *kv, *w_uk, *w_uv;
+    double *k, *v;
+} decomp_ctx;
+
+static void decompress_row(void *p, int32_t n)
+{
+    const decomp_ctx *c = (const decomp_ctx *)p;
+    double lat[576];
+    for (int j = 0; j < 576; ++j) lat[j] = bf16_value(c->kv[(int64_t)n * 576 + j]);
+    for (int h = 0; h < c->H; ++h) {
+        double *kk = c->k + ((int64_t)n * c->H + h) * 192;
+        double *vv = c->v + ((int64_t)n * c->H + h) * 128;
+        for (int d = 0; d < 128; ++d) {
+            const uint16_t *wk = c->w_uk + ((int64_t)h * 128 + d) * 512;
+            const uint16_t *wv = c->w_uv + ((int64_t)h * 128 + d) * 512;
+            double sk = 0.0, sv = 0.0;
+            for (int j = 0; j < 512; ++j) {
+                sk += bf16_value(wk[j]) * lat[j];
+                sv += bf16_value(wv[j]) * lat[j];
+            }
+            kk[d] = sk;
+            vv[d] = sv;
+        }
+        for (int d = 0; d < 64; ++d) kk[128 + d] = lat[512 + d];
+    }
+}
+
+int oref_mha_decompress(int32_t n_cache_rows, int n_heads, const uint16_t *kv, const uint16_t *w_uk,
+                        const uint16_t *w_uv, double *k, double *v, int n_threads)
+{
+    if (n_cache_rows < 0 || n_heads <= 0) return 1;
+    decomp_ctx c = {n_heads, kv, w_uk, w_uv, k, v};
+    run_rows(decompress_row, &c, n_cache_rows, n_threads);
+    return 0;
+}
+
+typedef struct {
+    int H;
+    const uint16_t *q;
+    const double *k, *v;
+    const oref_rows *rows;
+    const int32_t *idx;
+    int32_t topk;
+    double scale;
+    const int32_t *which;
+    double *out, *lse;
+} mha_ctx;
+
+static void mha_row(void *p, int32_t i)
+{
+    const mha_ctx *c = (const mha_ctx *)p;
+    const int32_t r = c->which[i];
+    const int32_t b = c->rows->row_seq[r];
+    const int64_t n = c->rows->row_len[r];
+    /* the attended positions: the set of valid idx entries, or 0 .. n-1 */
+    unsigned char *in = (unsigned char *)calloc((size_t)(n > 0 ? n : 1), 1);
+    for (int64_t s = 0; s < n; ++s) in[s] = c->idx ? 0 : 1;
+    if (c->idx)
+        for (int32_t j = 0; j < c->topk; ++j) {
+            const int64_t s = c->idx[(int64_t)r * c->topk + j];
+            if (s >= 0 && s < n) in[s] = 1;
+        }
+    double *z = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int h = 0; h < c->H; ++h) {
+        double qh[192];
+        for (int d = 0; d < 192; ++d) qh[d] = bf16_value(c->q[((int64_t)r * c->H + h) * 192 + d]);
+        double *o = c->out + ((int64_t)i * c->H + h) * 128;
+        double m = -INFINITY;
+        for (int64_t s = 0; s < n; ++s) {
+            if (!in[s]) continue;
+            const double *kk = c->k + (oref_cache_row(c->rows, b, s) * c->H + h) * 192;
+            double dot = 0.0;
+            for (int d = 0; d < 192; ++d) dot += qh[d] * kk[d];
+            z[s] = c->scale * dot;
+            if (z[s] > m) m = z[s];
+        }
+        double l = 0.0;
+        for (int d = 0; d < 128; ++d) o[d] = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            if (!in[s]) continue;
+            const double w = exp(z[s] - m);
+            const double *vv = c->v + (oref_cache_row(c->rows, b, s) * c->H + h) * 128;
+            l += w;
+            for (int d = 0; d < 128; ++d) o[d] += w * vv[d];
+        }
+        if (l > 0.0)
+            for (int d = 0; d < 128; ++d) o[d] /= l;
+        if (c->lse) c->lse[(int64_t)i * c->H + h] = l > 0.0 ? m + log(l) : -INFINITY;
+    }
+    free(z);
+    free(in);
+}
+
+int oref_mha(int n_heads, const uint16_t *q, const double *k, const double *v,
+             const oref_rows *rows, const int32_t *idx, int32_t topk, double scale,
+             const int32_t *which, int32_t n_which, double *out, double *lse, int n_threads)
+{
+    if (n_heads <= 0 || (idx && topk <= 0)) return 1;
+    mha_ctx c = {n_heads, q, k, v, rows, idx, topk, scale, which, out, lse};
+    run_rows(mha_row, &c, n_which, n_threads);
+    return 0;
+}

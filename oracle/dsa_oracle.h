@@ -128,6 +128,23 @@ int oref_prep_queries(int32_t n_rows, const int32_t *pos, const float *cos_sin, 
                       int idx_dtype, int32_t n_idx_heads, const uint16_t *qi_in, void *qi_out,
                       float *qi_scale, int32_t n_heads, uint16_t *q);
 
+/* ------------------------------------------------------------------------ */
+/* Masked MHA mode for short prefill ([R] "短序列优化"; [M] "Multi-head      */
+/* latent attention").  Decompression, per cache row n and head h:           */
+/*   k[n,h] = [W_UK[h] . c_n (128) | kr_n (64)],  v[n,h] = W_UV[h] . c_n (128) */
+/* with kv rows [c_n (512) | kr_n (64)] bf16 and W_UK, W_UV [H, 128, 512]     */
+/* bf16; k, v in fp64 [rows, H, 192] / [rows, H, 128].                       */
+/* Attention of row r, head h over the set of its valid idx entries (idx     */
+/* [R, topk]), or over every position below row_len when idx is NULL:        */
+/*   z_s = scale * q[r,h] . k[row(s),h];  out = softmax(z) . v;  lse = ln sum */
+/* q is [R, H, 192] bf16; out [n_which, H, 128], lse [n_which, H].          */
+/* ------------------------------------------------------------------------ */
+int oref_mha_decompress(int32_t n_cache_rows, int n_heads, const uint16_t *kv, const uint16_t *w_uk,
+                        const uint16_t *w_uv, double *k, double *v, int n_threads);
+int oref_mha(int n_heads, const uint16_t *q, const double *k, const double *v,
+             const oref_rows *rows, const int32_t *idx, int32_t topk, double scale,
+             const int32_t *which, int32_t n_which, double *out, double *lse, int n_threads);
+
 #ifdef __cplusplus
 }
 #endif
