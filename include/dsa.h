@@ -222,6 +222,41 @@ int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int i
                                       void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Masked MHA mode for short prefill ("DeepSeek-V3.2 技术报告摘要", section 1, "短序列优化":
+ * short prefill runs DSA as masked MHA; "DeepSeek-V3.2 -- Model techniques map",
+ * "Multi-head latent attention": 128 nope + 64 rope query/key dims, 128 value dims per head).
+ * Every latent cache row n ([c_n (512) | kr_n (64)], the layout of the MLA calls) is first
+ * decompressed per head h: K[n,h] = [W_UK[h] c_n | kr_n] (192 dims), V[n,h] = W_UV[h] c_n
+ * (128 dims), rounded to bf16.  Row r, head h then attends over the set of its valid idx
+ * entries (idx [R, k] int32), or, with idx = NULL, over every position below row_len[r]
+ * (dense causal: what the top-k selects when the row has at most k positions):
+ *   z_s = softmax_scale * q[r,h,:] . K[row(s),h,:];  out[r,h,:] = softmax(z) . V;
+ *   lse[r,h] = ln sum_s exp(z_s) (-inf for an empty set; lse may be NULL).
+ * q: [R, n_heads, 192] bf16 (nope 128 | rope 64); kv: [num_cache_rows, 576] bf16 (contiguous
+ * [N, 576] or paged [P, 64, 576], num_cache_rows = N or 64 P); w_uk, w_uv: [n_heads, 128, 512]
+ * bf16 (row d of head h is the 512-vector producing key / value dim d); out: [R, n_heads,
+ * 128] bf16.  ws: device scratch of dsa_mha_prefill_workspace_size(num_cache_rows, n_heads,
+ * R, max_row_len, idx != NULL) bytes (the decompressed keys and values, 2 x 256 B per cache
+ * row and head, and the top-k masks); calls sharing a workspace must not run concurrently.
+ * max_row_len <= 65536.  dsa_prefill_dense_mode(max_row_len, topk) is 1 when every row has
+ * at most topk positions, i.e. when the dense mode (idx = NULL) equals DSA exactly.
+ * Errors: DSA_ERR_INVALID_ARG for a bad row description, missing pointers, n_heads < 1,
+ * num_cache_rows < 1, a non-finite or non-positive scale, k outside [1, 2048] with idx;
+ * DSA_ERR_UNSUPPORTED for max_row_len > 65536; DSA_ERR_WORKSPACE for a missing or small ws;
+ * DSA_ERR_HIP when the decompression GEMM (rocBLAS) or a launch fails. */
+int dsa_prefill_dense_mode(int max_row_len, int topk);
+size_t dsa_mha_prefill_workspace_size(int64_t num_cache_rows, int n_heads, int num_rows,
+                                      int max_row_len, int masked);
+int dsa_mha_prefill(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
+                    float softmax_scale, const void *q, const void *kv, const void *w_uk,
+                    const void *w_uv, const int32_t *idx, int k, void *out, float *lse, void *ws,
+                    size_t ws_bytes, void *stream);
+int dsa_mha_prefill_paged(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
+                          float softmax_scale, const void *q, const void *kv, const void *w_uk,
+                          const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Indexer-input and cache-write prep: the step in front of the indexer for every new token
  * ("DeepSeek-V3.2 技术报告摘要", section 1, DSA ①: indexer keys and queries, FP8 supported;
  * "DeepSeek-V3.2-Exp" README, section "更新": the indexer's RoPE takes the non-interleaved

@@ -90,6 +90,14 @@ def load_library() -> ctypes.CDLL:
     lib.dsa_prep.argtypes = [i32, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                              vp, vp]
     lib.dsa_prep.restype = i32
+    lib.dsa_prefill_dense_mode.argtypes = [i32, i32]
+    lib.dsa_prefill_dense_mode.restype = i32
+    lib.dsa_mha_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    lib.dsa_mha_prefill_workspace_size.restype = sz
+    for name in ("dsa_mha_prefill", "dsa_mha_prefill_paged"):
+        f = getattr(lib, name)
+        f.argtypes = [rows_p, i64, i32, ctypes.c_float, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        f.restype = i32
     _lib = lib
     return lib
 
@@ -458,3 +466,54 @@ def prep(positions, cache_rows, cos_sin, k_idx_in, k_idx_cache, kv_in, kv_cache,
                      _ptr(q_idx_in), _ptr(q_idx), _ptr(q_idx_scale), int(q.shape[1]), _ptr(q),
                      _stream())
     _check(s, "dsa_prep")
+
+
+# --------------------------------------------------------------------------- masked MHA mode
+
+def prefill_dense_mode(max_row_len: int, topk: int) -> bool:
+    """True when every row has at most ``topk`` positions: the dense MHA mode is then exactly
+    DSA (the top-k selects everything)."""
+    return bool(load_library().dsa_prefill_dense_mode(int(max_row_len), int(topk)))
+
+
+def mha_prefill_workspace_size(num_cache_rows: int, n_heads: int, num_rows: int,
+                               max_row_len: int, masked: bool) -> int:
+    return int(load_library().dsa_mha_prefill_workspace_size(
+        int(num_cache_rows), int(n_heads), int(num_rows), int(max_row_len), int(bool(masked))))
+
+
+def mha_prefill(rows: Rows, q, kv, w_uk, w_uv, scale: float, idx=None, out=None, lse=None,
+                ws=None):
+    """Masked MHA mode: q [R, H, 192] bf16 against the latent cache ``kv`` decompressed through
+    ``w_uk`` / ``w_uv`` [H, 128, 512]; over each row's top-k set ``idx`` [R, k] or, with
+    idx None, over every position below its length.  Returns out [R, H, 128] bf16."""
+    lib = load_library()
+    _dev(q, "q", (torch.bfloat16,))
+    _dev(kv, "kv", (torch.bfloat16,))
+    _dev(w_uk, "w_uk", (torch.bfloat16,))
+    _dev(w_uv, "w_uv", (torch.bfloat16,))
+    if q.dim() != 3 or q.shape[2] != 192:
+        raise ValueError("q must be [R, H, 192]")
+    R, H = int(q.shape[0]), int(q.shape[1])
+    if w_uk.shape != (H, 128, 512) or w_uv.shape != (H, 128, 512) or kv.shape[-1] != 576:
+        raise ValueError("w_uk / w_uv must be [H, 128, 512] and kv rows 576 wide")
+    n_cache = kv.numel() // 576
+    k = 0
+    if idx is not None:
+        _dev(idx, "idx", (torch.int32,))
+        k = int(idx.shape[1])
+    if out is None:
+        out = torch.empty((R, H, 128), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", (torch.bfloat16,))
+    if lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+    need = mha_prefill_workspace_size(n_cache, H, R, rows.max_row_len, idx is not None)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = rows.struct()
+    name = "dsa_mha_prefill_paged" if rows.paged else "dsa_mha_prefill"
+    s = getattr(lib, name)(ctypes.byref(st), n_cache, H, float(scale), _ptr(q), _ptr(kv),
+                           _ptr(w_uk), _ptr(w_uv), _ptr(idx), k, _ptr(out), _ptr(lse), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream())
+    _check(s, name)
+    return out

@@ -242,6 +242,27 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
   return status_of(e);
 }
 
+constexpr int kMhaMaxRowLen = 65536;   // the attended range's pages are staged in LDS
+
+int mha_common(const dsa_rows *rows, bool paged, int64_t num_cache_rows, int n_heads,
+               float softmax_scale, const void *q, const void *kv, const void *w_uk,
+               const void *w_uv, const int32_t *idx, int k, void *out, float *lse, void *ws,
+               size_t ws_bytes, void *stream) {
+  if (!rows_ok(rows, paged)) return DSA_ERR_INVALID_ARG;
+  if (num_cache_rows < 1 || n_heads < 1) return DSA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DSA_ERR_INVALID_ARG;
+  if (idx && (k < 1 || k > DSA_MAX_TOPK)) return DSA_ERR_INVALID_ARG;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !kv || !w_uk || !w_uv || !out) return DSA_ERR_INVALID_ARG;
+  if (rows->max_row_len > kMhaMaxRowLen) return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa::mha_workspace_bytes(num_cache_rows, n_heads, rows->num_rows,
+                                               rows->max_row_len, idx != nullptr);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  return status_of(dsa::launch_mha_prefill(to_host(rows), paged, num_cache_rows, n_heads,
+                                           softmax_scale, q, kv, w_uk, w_uv, idx, k, out, lse, ws,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int prep_keys_check(const dsa::PrepKeys &k, bool fp8) {
   if (k.T < 0 || k.cache_rows < 1) return DSA_ERR_INVALID_ARG;
   if (k.T == 0) return DSA_OK;
@@ -415,6 +436,32 @@ int dsa_sparse_mla_prefill_paged(const dsa_rows *rows, int dtype, int n_heads, i
   (void)ws_bytes;
   return mla_common(rows, true, MlaMode::kPrefill, dtype, n_heads, d_qk, d_v, softmax_scale, q,
                     kv, idx, k, out, lse, nullptr, 0, stream);
+}
+
+int dsa_prefill_dense_mode(int max_row_len, int topk) {
+  return (max_row_len >= 1 && topk >= 1 && max_row_len <= topk) ? 1 : 0;
+}
+
+size_t dsa_mha_prefill_workspace_size(int64_t num_cache_rows, int n_heads, int num_rows,
+                                      int max_row_len, int masked) {
+  if (num_cache_rows < 1 || n_heads < 1 || num_rows < 0 || max_row_len < 1) return 0;
+  return dsa::mha_workspace_bytes(num_cache_rows, n_heads, num_rows, max_row_len, masked != 0);
+}
+
+int dsa_mha_prefill(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
+                    float softmax_scale, const void *q, const void *kv, const void *w_uk,
+                    const void *w_uv, const int32_t *idx, int k, void *out, float *lse, void *ws,
+                    size_t ws_bytes, void *stream) {
+  return mha_common(rows, false, num_cache_rows, n_heads, softmax_scale, q, kv, w_uk, w_uv, idx,
+                    k, out, lse, ws, ws_bytes, stream);
+}
+
+int dsa_mha_prefill_paged(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
+                          float softmax_scale, const void *q, const void *kv, const void *w_uk,
+                          const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream) {
+  return mha_common(rows, true, num_cache_rows, n_heads, softmax_scale, q, kv, w_uk, w_uv, idx,
+                    k, out, lse, ws, ws_bytes, stream);
 }
 
 int dsa_prep_cache_write(int num_tokens, const int32_t *positions, const int64_t *cache_rows,

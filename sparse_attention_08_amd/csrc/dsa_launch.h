@@ -83,6 +83,17 @@ hipError_t launch_mla_bf16_select(const RowsHost &rows, bool paged, int H, float
                                   float *lse, int splits, void *ws, const float *logits,
                                   int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream);
 
+// ---- masked MHA mode (short prefill) ----
+// Workspace: decompressed K_nope and V ([cache_rows, H, 128] bf16 each) and, with idx, the
+// rows' top-k sets as bit masks.
+size_t mha_workspace_bytes(int64_t cache_rows, int H, int R, int max_row_len, bool masked);
+// q [R, H, 192] bf16; kv latent cache rows [cache_rows, 576] bf16; W_UK, W_UV [H, 128, 512]
+// bf16; idx [R, k] or nullptr (dense causal); out [R, H, 128] bf16, lse [R, H] (optional).
+hipError_t launch_mha_prefill(const RowsHost &rows, bool paged, int64_t cache_rows, int H,
+                              float scale, const void *q, const void *kv, const void *w_uk,
+                              const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
+                              void *ws, hipStream_t stream);
+
 // ---- indexer-input and cache-write prep ----
 // Query rows (R of them, R may be 0): 64 indexer heads rotated to bf16 or e4m3 (+ per-head
 // scale), n_heads MLA heads rotated in place.

@@ -1,0 +1,383 @@
+// mha.hip -- masked MHA mode for short prefill on gfx950 ("DeepSeek-V3.2 技术报告摘要",
+// section 1, "短序列优化": for short prefill DSA is run as masked MHA; "DeepSeek-V3.2 -- Model
+// techniques map", "Multi-head latent attention": per head 128 nope + 64 rope query/key dims
+// and 128 value dims, decompressed from the 512-dim latent).
+//
+// Step 1 decompresses every latent cache row n: K_nope[n, h] = W_UK[h] c_n and V[n, h] =
+// W_UV[h] c_n (128 dims each, bf16), two plain GEMMs on rocBLAS.  Step 2 attends: row r,
+// head h, over its sequence's positions s (all s < row_len, or the set of its top-k entries):
+// z_s = scale [q_nope | q_rope] . [K_nope[s, h] | kr_s], out = softmax(z) V, lse = ln sum e^z.
+//
+// Attention kernel: a workgroup owns 64 consecutive query rows (4 waves x 16) of one head.
+// Key tiles of 32 positions (K_nope 8 KB + RoPE keys 4 KB + V 8 KB) go through a
+// double-buffered LDS ring with global->LDS loads, each 1 KB instruction filled by one wave.
+// Each wave computes the transposed score tile S^T = K . Q^T (keys as MFMA rows, its 16 rows
+// as columns, q in registers), an online softmax in the log2 domain, and O^T += V^T . P^T
+// with V^T read through the transposing LDS read; key rows of the score blocks are permuted
+// (block kb, row 4g + i <-> key 8g + 4kb + i) so each lane's weights are the B operand of
+// the value product as they stand.  Rows of one workgroup that belong to different
+// sequences are handled one sequence at a time.
+#include <mutex>
+
+#include <rocblas/rocblas.h>
+
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+constexpr int kMhaWaves = 4;
+constexpr int kMhaThreads = kMhaWaves * kWave;
+constexpr int kMhaRows = 16 * kMhaWaves;       // query rows per workgroup
+constexpr int kMhaKeys = 32;                   // keys per tile
+constexpr int kNopeBytes = kMhaKeys * 256;     // 32 x 128 dims bf16
+constexpr int kRopeBytes = kMhaKeys * 128;     // 32 x 64 dims bf16
+constexpr int kValBytes = kMhaKeys * 256;      // 32 x 128 dims bf16
+constexpr int kMhaStage = kNopeBytes + kRopeBytes + kValBytes;   // 20 KB
+constexpr int kMhaDma = kMhaStage / 1024;      // 20 instructions of 1 KB
+static_assert(kMhaDma % kMhaWaves == 0, "the DMA instructions split evenly over the waves");
+constexpr int kMhaDmaPerWave = kMhaDma / kMhaWaves;   // 5
+constexpr int kMhaMaxPages = 1024;             // pages of one sequence held in LDS (64K tokens)
+
+// Chunk swizzles (16-byte chunk x of key row j sits at x ^ swz(j)): the score operand reads
+// (16 permuted key rows, one chunk per lane group) then touch 32 distinct 16-byte slots per
+// half-wave, the condition measured for conflict-free ds_read_b128 on gfx950.
+__device__ __forceinline__ int nope_swz(int j) { return (j & 3) | ((j >> 1) & 12); }
+__device__ __forceinline__ int rope_swz(int j) { return ((j >> 3) & 3) << 1; }
+// Value rows: the 32-byte column pair a transposing read takes from 8 rows (keys 8g + 0..3 for
+// two lane groups) lands in 8 distinct 32-byte bank windows.
+__device__ __forceinline__ int val_swz(int j) { return ((j & 3) | (((j >> 3) & 1) << 2)) << 1; }
+
+__device__ __forceinline__ void mha_dma16(const void *src, const void *lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la)
+                   : "memory");
+}
+
+typedef bf16x4 __attribute__((address_space(3))) *mha_lds_bf16x4_ptr;
+
+// s_waitcnt with vmcnt <= n, other counters unconstrained (gfx9 field layout).
+constexpr int mha_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+
+struct MhaShared {
+  uint8_t stage[2][kMhaStage];
+  int32_t pages[kMhaMaxPages];
+  int32_t seq[kMhaRows];
+  int32_t len[kMhaRows];
+};
+
+template <bool PAGED, bool MASKED>
+__global__ __launch_bounds__(kMhaThreads) void mha_prefill_kernel(
+    int R, int H, int n_row_tiles, const int32_t *__restrict__ row_seq,
+    const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
+    const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
+    const uint16_t *__restrict__ q, const uint8_t *__restrict__ k_nope,
+    const uint8_t *__restrict__ vals, const uint8_t *__restrict__ kv,
+    const uint32_t *__restrict__ mask, int mask_words, uint16_t *__restrict__ out,
+    float *__restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) MhaShared sh;
+  // longest row tiles (most keys) first; the heads of one row tile are consecutive workgroups
+  const int rt = n_row_tiles - 1 - (int)(blockIdx.x / H);
+  const int h = blockIdx.x % H;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int r0 = rt * kMhaRows;
+  const int my_r = r0 + 16 * wave + c;   // this lane's query row (column c of the wave's tiles)
+  const bool row_ok = my_r < R;
+  if (threadIdx.x < kMhaRows) {
+    const int rr = r0 + threadIdx.x;
+    sh.seq[threadIdx.x] = rr < R ? row_seq[rr] : -1;
+    sh.len[threadIdx.x] = rr < R ? row_len[rr] : 0;
+  }
+  // q^T operand: row my_r, dims 32t + 8g .. + 8 (t < 4: nope, t = 4, 5: rope)
+  bf16x8 qf[6];
+  {
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+        q + ((int64_t)(row_ok ? my_r : 0) * H + h) * 192 + 8 * g);
+#pragma unroll
+    for (int t = 0; t < 6; ++t) qf[t] = qp[4 * t];
+  }
+  __syncthreads();
+  const int my_seq = sh.seq[16 * wave + c];
+  const int my_len = sh.len[16 * wave + c];
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // score operand rows: block kb, lane row c <-> key 8 (c >> 2) + (c & 3) + 4 kb; lane group g
+  // reads logical chunk 4t + g (nope: t < 4, 256-byte rows) or 4(t - 4) + g (rope, 128-byte
+  // rows), stored at chunk ^ swz(key)
+  const int arow0 = 8 * (c >> 2) + (c & 3);
+  int a_nope[2], a_rope[2], s_nope[2], s_rope[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int a = arow0 + 4 * kb;
+    a_nope[kb] = a * 256;
+    s_nope[kb] = nope_swz(a);
+    a_rope[kb] = kNopeBytes + a * 128;
+    s_rope[kb] = rope_swz(a);
+  }
+  // value operand: transposing reads of keys 8g + (c >> 2) (and + 4: same swizzle), dims
+  // 16 nb + 4 (c & 3): logical chunk 2 nb + ((c & 3) >> 1) at chunk ^ val_swz(key)
+  const int vrow = 8 * g + (c >> 2);
+  const int v_off = kNopeBytes + kRopeBytes + vrow * 256 + 8 * (c & 3);
+  const int v_sw = val_swz(vrow) >> 1;
+  // this wave's DMA instructions: i = wave + 4 u (u < 5); 0..7 nope (4 keys each), 8..11 rope
+  // (8 keys each), 12..19 values (4 keys each)
+  int d_key[kMhaDmaPerWave], d_src[kMhaDmaPerWave];
+#pragma unroll
+  for (int u = 0; u < kMhaDmaPerWave; ++u) {
+    const int i = wave + kMhaWaves * u;
+    if (i < 8) {
+      d_key[u] = 4 * i + (lane >> 4);
+      d_src[u] = 16 * ((lane & 15) ^ nope_swz(d_key[u]));
+    } else if (i < 12) {
+      d_key[u] = 8 * (i - 8) + (lane >> 3);
+      d_src[u] = 16 * ((lane & 7) ^ rope_swz(d_key[u]));
+    } else {
+      d_key[u] = 4 * (i - 12) + (lane >> 4);
+      d_src[u] = 16 * ((lane & 15) ^ val_swz(d_key[u]));
+    }
+  }
+
+  uint64_t done = 0;
+  for (;;) {
+    // the next sequence among the workgroup's rows and its longest row
+    int b = -1, kmax = 0;
+    for (int i = 0; i < kMhaRows; ++i) {
+      const int sq = sh.seq[i];
+      if (sq < 0 || ((done >> i) & 1ull)) continue;
+      if (b < 0) b = sq;
+      if (sq == b) {
+        kmax = max(kmax, sh.len[i]);
+        done |= 1ull << i;
+      }
+    }
+    if (b < 0) break;
+    const bool mine = my_seq == b;
+    const int n_tiles = (kmax + kMhaKeys - 1) / kMhaKeys;
+    int64_t base = 0;
+    // every wave is done with the previous sequence's tiles (the ring is reused from slot 0)
+    // and page list
+    __syncthreads();
+    if constexpr (PAGED) {
+      const int n_pages = (kmax + 63) / 64;
+      for (int i = threadIdx.x; i < n_pages; i += kMhaThreads)
+        sh.pages[i] = page_table[(int64_t)b * max_pages + i];
+      __syncthreads();
+    } else {
+      base = seq_start[b];
+    }
+    auto cache_row = [&](int s) -> int64_t {
+      if constexpr (PAGED)
+        return (int64_t)sh.pages[s >> 6] * 64 + (s & 63);
+      else
+        return base + s;
+    };
+    auto issue = [&](int tile) {
+      uint8_t *st = sh.stage[tile & 1];
+#pragma unroll
+      for (int u = 0; u < kMhaDmaPerWave; ++u) {
+        const int i = wave + kMhaWaves * u;
+        const int s = min(tile * kMhaKeys + d_key[u], kmax - 1);   // tail keys re-read the last
+        const int64_t cr = cache_row(s);
+        const uint8_t *src;
+        if (i < 8) src = k_nope + (cr * H + h) * 256 + d_src[u];
+        else if (i < 12) src = kv + cr * 1152 + 1024 + d_src[u];
+        else src = vals + (cr * H + h) * 256 + d_src[u];
+        mha_dma16(src, st + 1024 * i);
+      }
+    };
+    issue(0);
+    uint32_t mword = 0;
+    if constexpr (MASKED)
+      if (mine) mword = mask[(int64_t)my_r * mask_words];
+    for (int j = 0; j < n_tiles; ++j) {
+      // this wave's part of tile j has landed (nothing younger in flight yet), and every
+      // wave is done with tile j - 1, whose slot the next load reuses
+      __builtin_amdgcn_s_waitcnt(mha_vmcnt(0));
+      lds_barrier();
+      if (j + 1 < n_tiles) issue(j + 1);
+      uint32_t mnext = 0;
+      if constexpr (MASKED)
+        if (mine && j + 1 < n_tiles) mnext = mask[(int64_t)my_r * mask_words + j + 1];
+      const uint8_t *st = sh.stage[j & 1];
+      // ---- S^T for the tile's 32 keys (2 blocks of 16) x the wave's 16 rows
+      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 6; ++t) {
+        bf16x8 x0, x1;
+        if (t < 4) {
+          x0 = *reinterpret_cast<const bf16x8 *>(st + a_nope[0] + 16 * ((4 * t + g) ^ s_nope[0]));
+          x1 = *reinterpret_cast<const bf16x8 *>(st + a_nope[1] + 16 * ((4 * t + g) ^ s_nope[1]));
+        } else {
+          x0 = *reinterpret_cast<const bf16x8 *>(st + a_rope[0] +
+                                                 16 * ((4 * (t - 4) + g) ^ s_rope[0]));
+          x1 = *reinterpret_cast<const bf16x8 *>(st + a_rope[1] +
+                                                 16 * ((4 * (t - 4) + g) ^ s_rope[1]));
+        }
+        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[t], sc0, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[t], sc1, 0, 0, 0);
+      }
+      // ---- mask: key s = 32 j + 8g + 4 kb + i is attended by row my_r iff the row belongs
+      // to this sequence, s < len, and (masked mode) bit s of the row's mask is set
+      float p[8];
+      {
+        const int s0 = j * kMhaKeys + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sl = 8 * g + 4 * kb + i;
+            bool ok = mine && (s0 + 4 * kb + i) < my_len;
+            if constexpr (MASKED) ok = ok && ((mword >> sl) & 1u);
+            const float z = kb ? sc1[i] : sc0[i];
+            p[4 * kb + i] = ok ? z * scale_log2 : -INFINITY;
+          }
+      }
+      // ---- online softmax (log2 domain): the reference maximum only moves when the tile
+      // maximum exceeds it by more than 8, so weights stay <= 2^8 and rescales are rare
+      float mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
+                       fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+      mx = max_xor32(max_xor16(mx));
+      const bool any = mx > -INFINITY;
+      const bool move = any && (m_run == -INFINITY || mx > m_run + 8.f);
+      if (__ballot(move && m_run > -INFINITY)) {
+        const float alpha = (move && m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
+        l_part *= alpha;
+      }
+      if (move) m_run = mx;
+      const float neg_m = m_run > -INFINITY ? -m_run : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(p[i] + neg_m);
+      l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      const bf16x8 pf = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+      // ---- O^T += V^T . P^T, value rows 16 nb + c
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const uint8_t *va = st + v_off + 32 * (nb ^ v_sw);
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)va);
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)(va + 4 * 256));
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), pf, oacc[nb], 0, 0, 0);
+      }
+      mword = mnext;
+    }
+  }
+
+  // ---- epilogue: lane (g, c) holds row my_r, value dims 16 nb + 4g + i
+  const float l = sum_xor32(sum_xor16(l_part));
+  if (!row_ok) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t *o = out + ((int64_t)my_r * H + h) * 128 + 4 * g;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const uint2 v = make_uint2(pack_bf16x2(oacc[nb][0] * inv, oacc[nb][1] * inv),
+                               pack_bf16x2(oacc[nb][2] * inv, oacc[nb][3] * inv));
+    *reinterpret_cast<uint2 *>(o + 16 * nb) = v;
+  }
+  if (lse && g == 0)
+    lse[(int64_t)my_r * H + h] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// Mask bits of the top-k sets: word w of row r holds positions 32 w .. 32 w + 31.
+__global__ __launch_bounds__(256) void mha_mask_clear_kernel(uint32_t *__restrict__ mask,
+                                                             int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    mask[i] = 0u;
+}
+__global__ __launch_bounds__(256) void mha_mask_set_kernel(const int32_t *__restrict__ idx, int k,
+                                                           const int32_t *__restrict__ row_len,
+                                                           uint32_t *__restrict__ mask,
+                                                           int mask_words) {
+  const int r = blockIdx.x;
+  const int len = row_len[r];
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const int s = idx[(int64_t)r * k + j];
+    if (s >= 0 && s < len) atomicOr(&mask[(int64_t)r * mask_words + (s >> 5)], 1u << (s & 31));
+  }
+}
+
+// One rocBLAS handle per device, created on first use.
+static rocblas_handle mha_blas_handle(int device) {
+  static std::mutex mu;
+  static rocblas_handle handles[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0 || device >= 64) return nullptr;
+  if (!handles[device] && rocblas_create_handle(&handles[device]) != rocblas_status_success)
+    handles[device] = nullptr;
+  return handles[device];
+}
+
+size_t mha_workspace_bytes(int64_t cache_rows, int H, int R, int max_row_len, bool masked) {
+  const size_t kv = (size_t)cache_rows * H * 128 * 2;   // K_nope and V, bf16 each
+  const size_t m = masked ? (size_t)R * ((max_row_len + 31) / 32) * 4 : 0;
+  return 2 * ((kv + 255) & ~(size_t)255) + m;
+}
+
+hipError_t launch_mha_prefill(const RowsHost &rh, bool paged, int64_t cache_rows, int H,
+                              float scale, const void *q, const void *kv, const void *w_uk,
+                              const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
+                              void *ws, hipStream_t stream) {
+  const size_t kv_bytes = (((size_t)cache_rows * H * 128 * 2) + 255) & ~(size_t)255;
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  uint16_t *k_nope = reinterpret_cast<uint16_t *>(wsb);
+  uint16_t *vals = reinterpret_cast<uint16_t *>(wsb + kv_bytes);
+  uint32_t *mask = idx ? reinterpret_cast<uint32_t *>(wsb + 2 * kv_bytes) : nullptr;
+  const int mask_words = (rh.max_row_len + 31) / 32;
+  // decompression: rows are the latent cache rows (stride 576 elements, first 512 used);
+  // column-major view: D (H*128 x rows) = W^T (H*128 x 512, from W [H*128][512]) x C^T
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  rocblas_handle hb = mha_blas_handle(dev);
+  if (!hb) return hipErrorNotInitialized;
+  if (rocblas_set_stream(hb, stream) != rocblas_status_success) return hipErrorNotInitialized;
+  const float one = 1.f, zero = 0.f;
+  for (int which = 0; which < 2; ++which) {
+    const rocblas_status st = rocblas_gemm_ex(
+        hb, rocblas_operation_transpose, rocblas_operation_none, H * 128, (rocblas_int)cache_rows,
+        512, &one, which ? w_uv : w_uk, rocblas_datatype_bf16_r, 512, kv, rocblas_datatype_bf16_r,
+        576, &zero, which ? (void *)vals : (void *)k_nope, rocblas_datatype_bf16_r, H * 128,
+        which ? (void *)vals : (void *)k_nope, rocblas_datatype_bf16_r, H * 128,
+        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    if (st != rocblas_status_success) return hipErrorLaunchFailure;
+  }
+  if (idx) {
+    const int64_t n = (int64_t)rh.num_rows * mask_words;
+    mha_mask_clear_kernel<<<(unsigned)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, stream>>>(
+        mask, n);
+    mha_mask_set_kernel<<<rh.num_rows, 256, 0, stream>>>(idx, k, rh.row_len, mask, mask_words);
+  }
+  const int n_row_tiles = (rh.num_rows + kMhaRows - 1) / kMhaRows;
+  const unsigned grid = (unsigned)n_row_tiles * (unsigned)H;
+  const float scale_log2 = scale * kLog2e;
+  const auto *qq = static_cast<const uint16_t *>(q);
+  const auto *kn = reinterpret_cast<const uint8_t *>(k_nope);
+  const auto *vv = reinterpret_cast<const uint8_t *>(vals);
+  const auto *kvb = static_cast<const uint8_t *>(kv);
+  auto *oo = static_cast<uint16_t *>(out);
+#define DSA_MHA_ARGS                                                                           \
+  rh.num_rows, H, n_row_tiles, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table,          \
+      rh.max_pages, scale_log2, qq, kn, vv, kvb, mask, mask_words, oo, lse
+  if (paged) {
+    if (idx) mha_prefill_kernel<true, true><<<grid, kMhaThreads, 0, stream>>>(DSA_MHA_ARGS);
+    else mha_prefill_kernel<true, false><<<grid, kMhaThreads, 0, stream>>>(DSA_MHA_ARGS);
+  } else {
+    if (idx) mha_prefill_kernel<false, true><<<grid, kMhaThreads, 0, stream>>>(DSA_MHA_ARGS);
+    else mha_prefill_kernel<false, false><<<grid, kMhaThreads, 0, stream>>>(DSA_MHA_ARGS);
+  }
+#undef DSA_MHA_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -228,3 +228,26 @@ def test_prep_validation(lib):
     assert both(dt=2, ks=FAKE) == INVALID and both(dt=2, qs=FAKE) == INVALID   # one scale missing
     assert both(dt=1, qs=FAKE) == INVALID
     assert both(dt=0) == UNSUPPORTED
+
+
+def test_mha_validation(lib):
+    def call(rows, n_cache=64, H=128, scale=0.07, idx=None, k=0, ws=None, ws_bytes=0, ptrs=True,
+             name="dsa_mha_prefill"):
+        p = FAKE if ptrs else None
+        return getattr(lib, name)(ctypes.byref(rows), n_cache, H, scale, p, p, p, p, idx, k, p,
+                                  None, ws, ws_bytes, None)
+    r = _rows()
+    assert call(r, n_cache=0) == INVALID
+    assert call(r, H=0) == INVALID
+    assert call(r, scale=0.0) == INVALID and call(r, scale=float("nan")) == INVALID
+    assert call(r, idx=FAKE, k=0) == INVALID and call(r, idx=FAKE, k=2049) == INVALID
+    assert call(r, ptrs=False) == INVALID
+    assert call(r, name="dsa_mha_prefill_paged") == INVALID            # layout mismatch
+    assert call(_rows(num_rows=0)) == OK
+    assert call(_rows(max_row_len=65537)) == UNSUPPORTED
+    need = lib.dsa_mha_prefill_workspace_size(64, 128, 2, 100, 0)
+    assert need >= 2 * 64 * 128 * 256
+    assert lib.dsa_mha_prefill_workspace_size(64, 128, 2, 100, 1) > need   # + the masks
+    assert call(r) == WORKSPACE and call(r, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    assert lib.dsa_prefill_dense_mode(2048, 2048) == 1 and lib.dsa_prefill_dense_mode(2049, 2048) == 0
+    assert lib.dsa_prefill_dense_mode(0, 2048) == 0

@@ -362,3 +362,31 @@ def prep_batch(lens, new, *, idx_dtype="fp8", paged=False, H=128, pad=0, seed=0,
                      rope_table(max(lens) + 1).to(device), k_idx_in, kv_in, k_cache, k_scale,
                      kv_cache, q_idx_in, q, None if start is None else start.to(device),
                      None if page_table is None else page_table.to(device))
+
+
+# --------------------------------------------------------------------------- masked MHA mode
+
+@dataclass
+class MhaBatch:
+    """A prefill batch for the MHA mode: the layout and latent cache of a prefill_batch plus
+    per-head 192-dim queries and the up-projections W_UK, W_UV."""
+    wl: Workload              # rows, cache layout and the latent cache kv
+    q: torch.Tensor           # bf16 [R, H, 192]
+    w_uk: torch.Tensor        # bf16 [H, 128, 512]
+    w_uv: torch.Tensor        # bf16 [H, 128, 512]
+    scale: float
+
+
+def mha_batch(lens, *, new=None, H=128, paged=False, seed=0, device="cpu") -> MhaBatch:
+    """Rows and latent cache as prefill_batch (tiny indexer inputs, unused here), then from the
+    same device generator stream: q ~ N(0,1), W_UK and W_UV ~ N(0, 1/512) (keys and values of
+    unit scale), all bf16."""
+    wl = prefill_batch(lens, new=new, paged=paged, H=H, H_I=4, D_I=128, seed=seed, device=device,
+                       name="mha_batch")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 1)
+    R = wl.num_rows
+    q = _normal((R, H, 192), gen, device).to(torch.bfloat16)
+    w_uk = (_normal((H, 128, 512), gen, device) / math.sqrt(512.0)).to(torch.bfloat16)
+    w_uv = (_normal((H, 128, 512), gen, device) / math.sqrt(512.0)).to(torch.bfloat16)
+    return MhaBatch(wl, q, w_uk, w_uv, 1.0 / math.sqrt(192.0))
