@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--prep", action="store_true",
                    help="time the indexer-input and cache-write prep of the workload's new tokens "
                         "(one per decode row; every token of a prefill) instead of the hot path")
+    p.add_argument("--mha", type=int, default=0, metavar="L",
+                   help="time the masked-MHA mode (dense causal) on an L-token prefill against the "
+                        "indexer + top-k + MQA path of the same length, instead of the hot path")
     p.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
                    help="no GPU work: 'trace NAME STATS_CSV CMD' writes profiles/NAME.md from a "
                         "rocprofv3 --kernel-trace --stats run; 'pmc KERNEL FETCH_CSV WRITE_CSV "
@@ -241,6 +244,82 @@ def prep_bench(args):
         "hbm_frac_of_step": (key_b + qry_b) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}))
 
 
+def mha_bench(args):
+    """One JSON line: the short-prefill MHA mode (dsa_mha_prefill, dense causal: latent
+    decompression + attention) on one L-token sequence, and the DSA path in MQA mode
+    (dsa_indexer_topk + dsa_sparse_mla_prefill) on a prefill of the same length, each captured
+    in a HIP graph and replayed after a cache flush."""
+    import torch
+
+    import sparse_attention_08_amd as dsa
+    import workloads
+
+    L = int(args.mha)
+    mb = workloads.mha_batch([L], seed=1000 + L, device="cuda")
+    wl = mb.wl
+    rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, seq_start=wl.seq_start)
+    H = int(mb.q.shape[1])
+    out = torch.empty((L, H, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dsa.mha_prefill_workspace_size(wl.kv.shape[0], H, L, L, False),
+                     dtype=torch.uint8, device="cuda")
+    w2 = workloads.prefill(L, seed=1000 + L, device="cuda")
+    rows2 = dsa.Rows(w2.row_seq, w2.row_len, w2.max_row_len, w2.num_seqs, seq_start=w2.seq_start)
+    logits = torch.empty((L, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, w2.topk), dtype=torch.int32, device="cuda")
+    o2 = torch.empty((L, w2.H, w2.D_v), dtype=torch.bfloat16, device="cuda")
+    tk_ws = torch.empty(max(dsa.indexer_topk_workspace_size(L, L, w2.q_idx.dtype, w2.topk), 1),
+                        dtype=torch.uint8, device="cuda")
+
+    def mha():
+        dsa.mha_prefill(rows, mb.q, wl.kv, mb.w_uk, mb.w_uv, mb.scale, out=out, ws=ws)
+
+    def mqa():
+        dsa.indexer_topk(rows2, w2.q_idx, w2.w, w2.k_idx, logits, w2.topk, idx=idx, ws=tk_ws)
+        dsa.sparse_mla_prefill(rows2, w2.q, w2.kv, idx, w2.scale, w2.D_v, out=o2)
+
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            if flush is not None:
+                flush.sum()
+            e[0].record(); graph.replay(); e[1].record()
+        torch.cuda.synchronize()
+        return statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+
+    ms_mha = timed(mha)
+    ms_mqa = timed(mqa)
+    pairs = L * (L + 1) // 2
+    dec_flops = 2 * L * 512 * H * 128 * 2
+    att_flops = pairs * H * (192 + 128) * 2
+    mqa_flops = sum(min(t + 1, w2.topk) for t in range(L)) * w2.H * (w2.D_qk + w2.D_v) * 2
+    achieved = (dec_flops + att_flops) / (ms_mha * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "short-prefill masked-MHA mode time per step", "value": ms_mha * 1e3,
+        "unit": "us", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic", "launch_mode": "hip_graph",
+        "config": {"workload": f"prefill of {L} tokens, dense causal", "heads": H,
+                   "cache_flushed_between_steps": flush is not None},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "flops": {"decompression": dec_flops, "attention": att_flops}},
+        "mqa_path": {"us": ms_mqa * 1e3, "calls": "indexer+top-k, sparse MLA prefill",
+                     "attention_flops": mqa_flops},
+        "speedup_vs_mqa_path": ms_mqa / ms_mha}))
+
+
 def cpu_baseline(wl_host, n_rows: int):
     """The fp64 oracle (as it stands) on the first n_rows rows of the same batch."""
     import numpy as np
@@ -288,6 +367,9 @@ def main():
         sys.exit(2)
     if args.prep:
         prep_bench(args)
+        return
+    if args.mha:
+        mha_bench(args)
         return
     import torch
 

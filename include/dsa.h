@@ -238,11 +238,11 @@ int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int i
  * 128] bf16.  ws: device scratch of dsa_mha_prefill_workspace_size(num_cache_rows, n_heads,
  * R, max_row_len, idx != NULL) bytes (the decompressed keys and values, 2 x 256 B per cache
  * row and head, and the top-k masks); calls sharing a workspace must not run concurrently.
- * max_row_len <= 65536.  dsa_prefill_dense_mode(max_row_len, topk) is 1 when every row has
+ * max_row_len <= 16384.  dsa_prefill_dense_mode(max_row_len, topk) is 1 when every row has
  * at most topk positions, i.e. when the dense mode (idx = NULL) equals DSA exactly.
  * Errors: DSA_ERR_INVALID_ARG for a bad row description, missing pointers, n_heads < 1,
  * num_cache_rows < 1, a non-finite or non-positive scale, k outside [1, 2048] with idx;
- * DSA_ERR_UNSUPPORTED for max_row_len > 65536; DSA_ERR_WORKSPACE for a missing or small ws;
+ * DSA_ERR_UNSUPPORTED for max_row_len > 16384; DSA_ERR_WORKSPACE for a missing or small ws;
  * DSA_ERR_HIP when the decompression GEMM (rocBLAS) or a launch fails. */
 int dsa_prefill_dense_mode(int max_row_len, int topk);
 size_t dsa_mha_prefill_workspace_size(int64_t num_cache_rows, int n_heads, int num_rows,

@@ -242,7 +242,7 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
   return status_of(e);
 }
 
-constexpr int kMhaMaxRowLen = 65536;   // the attended range's pages are staged in LDS
+constexpr int kMhaMaxRowLen = 16384;   // the attended range's pages are staged in LDS
 
 int mha_common(const dsa_rows *rows, bool paged, int64_t num_cache_rows, int n_heads,
                float softmax_scale, const void *q, const void *kv, const void *w_uk,

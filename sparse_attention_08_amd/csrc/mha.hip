@@ -8,11 +8,12 @@
 // head h, over its sequence's positions s (all s < row_len, or the set of its top-k entries):
 // z_s = scale [q_nope | q_rope] . [K_nope[s, h] | kr_s], out = softmax(z) V, lse = ln sum e^z.
 //
-// Attention kernel: a workgroup owns 64 consecutive query rows (4 waves x 16) of one head.
-// Key tiles of 32 positions (K_nope 8 KB + RoPE keys 4 KB + V 8 KB) go through a
-// double-buffered LDS ring with global->LDS loads, each 1 KB instruction filled by one wave.
-// Each wave computes the transposed score tile S^T = K . Q^T (keys as MFMA rows, its 16 rows
-// as columns, q in registers), an online softmax in the log2 domain, and O^T += V^T . P^T
+// Attention kernel: a workgroup owns 128 consecutive query rows (4 waves x 2 blocks of 16) of
+// one head.  Key tiles of 32 positions (K_nope 8 KB + RoPE keys 4 KB + V 8 KB) go through a
+// 3-stage LDS ring (two tiles in flight) with global->LDS loads, each 1 KB instruction filled
+// by one wave.  Each wave computes the transposed score tiles S^T = K . Q^T (keys as MFMA
+// rows, its rows as columns, q in registers, each key operand load serving both row blocks),
+// an online softmax in the log2 domain, and O^T += V^T . P^T
 // with V^T read through the transposing LDS read; key rows of the score blocks are permuted
 // (block kb, row 4g + i <-> key 8g + 4kb + i) so each lane's weights are the B operand of
 // the value product as they stand.  Rows of one workgroup that belong to different
@@ -28,16 +29,19 @@ namespace dsa {
 
 constexpr int kMhaWaves = 4;
 constexpr int kMhaThreads = kMhaWaves * kWave;
-constexpr int kMhaRows = 16 * kMhaWaves;       // query rows per workgroup
+constexpr int kRowBlocks = 2;                  // 16-row blocks per wave
+constexpr int kMhaRows = 16 * kRowBlocks * kMhaWaves;   // query rows per workgroup
+constexpr int kMhaRing = 3;                    // LDS stages (two tiles in flight)
 constexpr int kMhaKeys = 32;                   // keys per tile
 constexpr int kNopeBytes = kMhaKeys * 256;     // 32 x 128 dims bf16
 constexpr int kRopeBytes = kMhaKeys * 128;     // 32 x 64 dims bf16
 constexpr int kValBytes = kMhaKeys * 256;      // 32 x 128 dims bf16
-constexpr int kMhaStage = kNopeBytes + kRopeBytes + kValBytes;   // 20 KB
-constexpr int kMhaDma = kMhaStage / 1024;      // 20 instructions of 1 KB
+constexpr int kMaskOff = kNopeBytes + kRopeBytes + kValBytes;     // masked mode: the rows'
+constexpr int kMhaStage = kMaskOff + 4 * 128;  // mask words of the tile (4 B per row)
+constexpr int kMhaDma = kMaskOff / 1024;       // 20 key / value instructions of 1 KB
 static_assert(kMhaDma % kMhaWaves == 0, "the DMA instructions split evenly over the waves");
 constexpr int kMhaDmaPerWave = kMhaDma / kMhaWaves;   // 5
-constexpr int kMhaMaxPages = 1024;             // pages of one sequence held in LDS (64K tokens)
+constexpr int kMhaMaxPages = 256;              // pages of one sequence held in LDS (16K tokens)
 
 // Chunk swizzles (16-byte chunk x of key row j sits at x ^ swz(j)): the score operand reads
 // (16 permuted key rows, one chunk per lane group) then touch 32 distinct 16-byte slots per
@@ -48,6 +52,11 @@ __device__ __forceinline__ int rope_swz(int j) { return ((j >> 3) & 3) << 1; }
 // two lane groups) lands in 8 distinct 32-byte bank windows.
 __device__ __forceinline__ int val_swz(int j) { return ((j & 3) | (((j >> 3) & 1) << 2)) << 1; }
 
+__device__ __forceinline__ void mha_dma4(const void *src, const void *lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la)
+                   : "memory");
+}
 __device__ __forceinline__ void mha_dma16(const void *src, const void *lds) {
   const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la)
@@ -60,14 +69,17 @@ typedef bf16x4 __attribute__((address_space(3))) *mha_lds_bf16x4_ptr;
 constexpr int mha_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 struct MhaShared {
-  uint8_t stage[2][kMhaStage];
+  uint8_t stage[kMhaRing][kMhaStage];
   int32_t pages[kMhaMaxPages];
   int32_t seq[kMhaRows];
   int32_t len[kMhaRows];
 };
 
+// Two waves per SIMD (two workgroups per CU): up to 256 registers per lane for the two row
+// blocks' queries and accumulators.
 template <bool PAGED, bool MASKED>
-__global__ __launch_bounds__(kMhaThreads) void mha_prefill_kernel(
+__global__ __launch_bounds__(kMhaThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+mha_prefill_kernel(
     int R, int H, int n_row_tiles, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
     const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
@@ -83,33 +95,44 @@ __global__ __launch_bounds__(kMhaThreads) void mha_prefill_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int r0 = rt * kMhaRows;
-  const int my_r = r0 + 16 * wave + c;   // this lane's query row (column c of the wave's tiles)
-  const bool row_ok = my_r < R;
   if (threadIdx.x < kMhaRows) {
     const int rr = r0 + threadIdx.x;
     sh.seq[threadIdx.x] = rr < R ? row_seq[rr] : -1;
     sh.len[threadIdx.x] = rr < R ? row_len[rr] : 0;
   }
-  // q^T operand: row my_r, dims 32t + 8g .. + 8 (t < 4: nope, t = 4, 5: rope)
-  bf16x8 qf[6];
-  {
-    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-        q + ((int64_t)(row_ok ? my_r : 0) * H + h) * 192 + 8 * g);
+  // the wave's row blocks: rows r0 + 32 wave + 16 rb + c (column c of block rb's tiles);
+  // q^T operand of block rb: dims 32t + 8g .. + 8 (t < 4: nope, t = 4, 5: rope)
+  int my_r[kRowBlocks];
+  bf16x8 qf[kRowBlocks][6];
 #pragma unroll
-    for (int t = 0; t < 6; ++t) qf[t] = qp[4 * t];
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    my_r[rb] = r0 + 32 * wave + 16 * rb + c;
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+        q + ((int64_t)(my_r[rb] < R ? my_r[rb] : 0) * H + h) * 192 + 8 * g);
+#pragma unroll
+    for (int t = 0; t < 6; ++t) qf[rb][t] = qp[4 * t];
   }
   __syncthreads();
-  const int my_seq = sh.seq[16 * wave + c];
-  const int my_len = sh.len[16 * wave + c];
-
-  f32x4 oacc[8];
+  int my_seq[kRowBlocks], my_len[kRowBlocks];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    my_seq[rb] = sh.seq[32 * wave + 16 * rb + c];
+    my_len[rb] = sh.len[32 * wave + 16 * rb + c];
+  }
+
+  f32x4 oacc[kRowBlocks][8];
+  float m_run[kRowBlocks], l_part[kRowBlocks];
+#pragma unroll
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) oacc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rb] = -INFINITY;
+    l_part[rb] = 0.f;
+  }
 
   // score operand rows: block kb, lane row c <-> key 8 (c >> 2) + (c & 3) + 4 kb; lane group g
   // reads logical chunk 4t + g (nope: t < 4, 256-byte rows) or 4(t - 4) + g (rope, 128-byte
-  // rows), stored at chunk ^ swz(key)
+  // rows), stored at chunk ^ swz(key).  One operand load serves both row blocks.
   const int arow0 = 8 * (c >> 2) + (c & 3);
   int a_nope[2], a_rope[2], s_nope[2], s_rope[2];
 #pragma unroll
@@ -143,21 +166,23 @@ __global__ __launch_bounds__(kMhaThreads) void mha_prefill_kernel(
     }
   }
 
-  uint64_t done = 0;
+  uint64_t done[kMhaRows / 64] = {};
   for (;;) {
     // the next sequence among the workgroup's rows and its longest row
     int b = -1, kmax = 0;
     for (int i = 0; i < kMhaRows; ++i) {
       const int sq = sh.seq[i];
-      if (sq < 0 || ((done >> i) & 1ull)) continue;
+      if (sq < 0 || ((done[i >> 6] >> (i & 63)) & 1ull)) continue;
       if (b < 0) b = sq;
       if (sq == b) {
         kmax = max(kmax, sh.len[i]);
-        done |= 1ull << i;
+        done[i >> 6] |= 1ull << (i & 63);
       }
     }
     if (b < 0) break;
-    const bool mine = my_seq == b;
+    bool mine[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) mine[rb] = my_seq[rb] == b;
     const int n_tiles = (kmax + kMhaKeys - 1) / kMhaKeys;
     int64_t base = 0;
     // every wave is done with the previous sequence's tiles (the ring is reused from slot 0)
@@ -177,116 +202,156 @@ __global__ __launch_bounds__(kMhaThreads) void mha_prefill_kernel(
       else
         return base + s;
     };
+    // per-lane source bases of the wave's instructions (the key's cache row is added per tile)
+    const uint8_t *src_base[kMhaDmaPerWave];
+    int64_t src_stride[kMhaDmaPerWave];
+#pragma unroll
+    for (int u = 0; u < kMhaDmaPerWave; ++u) {
+      const int i = wave + kMhaWaves * u;
+      if (i < 8) {
+        src_base[u] = k_nope + (int64_t)h * 256 + d_src[u];
+        src_stride[u] = (int64_t)H * 256;
+      } else if (i < 12) {
+        src_base[u] = kv + 1024 + d_src[u];
+        src_stride[u] = 1152;
+      } else {
+        src_base[u] = vals + (int64_t)h * 256 + d_src[u];
+        src_stride[u] = (int64_t)H * 256;
+      }
+    }
     auto issue = [&](int tile) {
-      uint8_t *st = sh.stage[tile & 1];
+      uint8_t *st = sh.stage[tile % kMhaRing];
+      if constexpr (MASKED)
+        if (wave < kMhaRows / 64) {   // rows 64 wave .. + 63: their mask word of this tile
+          const int rr = min(r0 + 64 * wave + lane, R - 1);
+          mha_dma4(mask + (int64_t)rr * mask_words + tile, st + kMaskOff + 256 * wave);
+        }
 #pragma unroll
       for (int u = 0; u < kMhaDmaPerWave; ++u) {
         const int i = wave + kMhaWaves * u;
         const int s = min(tile * kMhaKeys + d_key[u], kmax - 1);   // tail keys re-read the last
-        const int64_t cr = cache_row(s);
-        const uint8_t *src;
-        if (i < 8) src = k_nope + (cr * H + h) * 256 + d_src[u];
-        else if (i < 12) src = kv + cr * 1152 + 1024 + d_src[u];
-        else src = vals + (cr * H + h) * 256 + d_src[u];
-        mha_dma16(src, st + 1024 * i);
+        mha_dma16(src_base[u] + cache_row(s) * src_stride[u], st + 1024 * i);
       }
     };
-    issue(0);
-    uint32_t mword = 0;
-    if constexpr (MASKED)
-      if (mine) mword = mask[(int64_t)my_r * mask_words];
+    for (int t0 = 0; t0 < kMhaRing - 1 && t0 < n_tiles; ++t0) issue(t0);
+    // loads per tile issued by this wave (the only vector-memory operations of the loop)
+    const int n_dma = kMhaDmaPerWave + ((MASKED && wave < kMhaRows / 64) ? 1 : 0);
     for (int j = 0; j < n_tiles; ++j) {
-      // this wave's part of tile j has landed (nothing younger in flight yet), and every
-      // wave is done with tile j - 1, whose slot the next load reuses
-      __builtin_amdgcn_s_waitcnt(mha_vmcnt(0));
+      // this wave's part of tile j has landed once at most the younger tiles' loads are in
+      // flight; every wave is done with tile j - 1, whose slot the next load reuses
+      if (min(kMhaRing - 2, n_tiles - 1 - j) >= 1) {
+        if (n_dma == kMhaDmaPerWave) __builtin_amdgcn_s_waitcnt(mha_vmcnt(kMhaDmaPerWave));
+        else __builtin_amdgcn_s_waitcnt(mha_vmcnt(kMhaDmaPerWave + 1));
+      } else {
+        __builtin_amdgcn_s_waitcnt(mha_vmcnt(0));
+      }
       lds_barrier();
-      if (j + 1 < n_tiles) issue(j + 1);
-      uint32_t mnext = 0;
+      if (j + kMhaRing - 1 < n_tiles) issue(j + kMhaRing - 1);
+      const uint8_t *st = sh.stage[j % kMhaRing];
+      uint32_t mword[kRowBlocks] = {};
       if constexpr (MASKED)
-        if (mine && j + 1 < n_tiles) mnext = mask[(int64_t)my_r * mask_words + j + 1];
-      const uint8_t *st = sh.stage[j & 1];
-      // ---- S^T for the tile's 32 keys (2 blocks of 16) x the wave's 16 rows
-      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+          mword[rb] = reinterpret_cast<const uint32_t *>(st + kMaskOff)[32 * wave + 16 * rb + c];
+      // ---- S^T for the tile's 32 keys (2 blocks of 16) x the wave's 2 x 16 rows
+      f32x4 sc[kRowBlocks][2];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb)
+        sc[rb][0] = sc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 6; ++t) {
-        bf16x8 x0, x1;
-        if (t < 4) {
-          x0 = *reinterpret_cast<const bf16x8 *>(st + a_nope[0] + 16 * ((4 * t + g) ^ s_nope[0]));
-          x1 = *reinterpret_cast<const bf16x8 *>(st + a_nope[1] + 16 * ((4 * t + g) ^ s_nope[1]));
-        } else {
-          x0 = *reinterpret_cast<const bf16x8 *>(st + a_rope[0] +
-                                                 16 * ((4 * (t - 4) + g) ^ s_rope[0]));
-          x1 = *reinterpret_cast<const bf16x8 *>(st + a_rope[1] +
-                                                 16 * ((4 * (t - 4) + g) ^ s_rope[1]));
-        }
-        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[t], sc0, 0, 0, 0);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[t], sc1, 0, 0, 0);
+        bf16x8 x[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          x[kb] = t < 4 ? *reinterpret_cast<const bf16x8 *>(st + a_nope[kb] +
+                                                            16 * ((4 * t + g) ^ s_nope[kb]))
+                        : *reinterpret_cast<const bf16x8 *>(st + a_rope[kb] +
+                                                            16 * ((4 * (t - 4) + g) ^ s_rope[kb]));
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            sc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[kb], qf[rb][t], sc[rb][kb],
+                                                                 0, 0, 0);
       }
-      // ---- mask: key s = 32 j + 8g + 4 kb + i is attended by row my_r iff the row belongs
-      // to this sequence, s < len, and (masked mode) bit s of the row's mask is set
-      float p[8];
-      {
-        const int s0 = j * kMhaKeys + 8 * g;
+      // ---- per row block: mask (key s = 32 j + 8g + 4 kb + i attended by the row iff the
+      // row belongs to this sequence, s < len, and, masked, bit s of its mask is set) and the
+      // online softmax in the log2 domain (the reference maximum moves only when the tile
+      // maximum exceeds it by more than 8: weights stay <= 2^8, rescales are rare)
+      bf16x8 pf[kRowBlocks];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        // raw scores; masked entries -inf (the scale is applied in the exponent, scale > 0)
+        float p[8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int sl = 8 * g + 4 * kb + i;
-            bool ok = mine && (s0 + 4 * kb + i) < my_len;
-            if constexpr (MASKED) ok = ok && ((mword >> sl) & 1u);
-            const float z = kb ? sc1[i] : sc0[i];
-            p[4 * kb + i] = ok ? z * scale_log2 : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) p[4 * kb + i] = sc[rb][kb][i];
+        // dense mode: a tile below every row's length needs no mask (all but the last tiles)
+        const bool full = !MASKED && __all(mine[rb] && (j + 1) * kMhaKeys <= my_len[rb]);
+        if (!full) {
+          const int s0 = j * kMhaKeys + 8 * g;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bool ok = mine[rb] && (s0 + 4 * kb + i) < my_len[rb];
+              if constexpr (MASKED) ok = ok && ((mword[rb] >> (8 * g + 4 * kb + i)) & 1u);
+              if (!ok) p[4 * kb + i] = -INFINITY;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
+                         fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+        mx = max_xor32(max_xor16(mx)) * scale_log2;
+        const bool move = mx > -INFINITY && (m_run[rb] == -INFINITY || mx > m_run[rb] + 8.f);
+        if (__ballot(move && m_run[rb] > -INFINITY)) {
+          const float alpha =
+              (move && m_run[rb] > -INFINITY) ? __builtin_amdgcn_exp2f(m_run[rb] - mx) : 1.f;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[rb][nb][i] *= alpha;
+          l_part[rb] *= alpha;
+        }
+        if (move) m_run[rb] = mx;
+        const float neg_m = m_run[rb] > -INFINITY ? -m_run[rb] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(p[i], scale_log2, neg_m));
+        l_part[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pf[rb] = __builtin_bit_cast(
+            bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
       }
-      // ---- online softmax (log2 domain): the reference maximum only moves when the tile
-      // maximum exceeds it by more than 8, so weights stay <= 2^8 and rescales are rare
-      float mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
-                       fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
-      mx = max_xor32(max_xor16(mx));
-      const bool any = mx > -INFINITY;
-      const bool move = any && (m_run == -INFINITY || mx > m_run + 8.f);
-      if (__ballot(move && m_run > -INFINITY)) {
-        const float alpha = (move && m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
-        l_part *= alpha;
-      }
-      if (move) m_run = mx;
-      const float neg_m = m_run > -INFINITY ? -m_run : 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(p[i] + neg_m);
-      l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      const bf16x8 pf = __builtin_bit_cast(
-          bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
-      // ---- O^T += V^T . P^T, value rows 16 nb + c
+      // ---- O^T += V^T . P^T, value rows 16 nb + c; one operand load serves both row blocks
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         const uint8_t *va = st + v_off + 32 * (nb ^ v_sw);
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)va);
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)(va + 4 * 256));
-        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), pf, oacc[nb], 0, 0, 0);
+        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+          oacc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], oacc[rb][nb], 0, 0, 0);
       }
-      mword = mnext;
     }
   }
 
-  // ---- epilogue: lane (g, c) holds row my_r, value dims 16 nb + 4g + i
-  const float l = sum_xor32(sum_xor16(l_part));
-  if (!row_ok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t *o = out + ((int64_t)my_r * H + h) * 128 + 4 * g;
+  // ---- epilogue: lane (g, c) holds row my_r[rb], value dims 16 nb + 4g + i
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const uint2 v = make_uint2(pack_bf16x2(oacc[nb][0] * inv, oacc[nb][1] * inv),
-                               pack_bf16x2(oacc[nb][2] * inv, oacc[nb][3] * inv));
-    *reinterpret_cast<uint2 *>(o + 16 * nb) = v;
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    const float l = sum_xor32(sum_xor16(l_part[rb]));
+    if (my_r[rb] >= R) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t *o = out + ((int64_t)my_r[rb] * H + h) * 128 + 4 * g;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint2 v = make_uint2(pack_bf16x2(oacc[rb][nb][0] * inv, oacc[rb][nb][1] * inv),
+                                 pack_bf16x2(oacc[rb][nb][2] * inv, oacc[rb][nb][3] * inv));
+      *reinterpret_cast<uint2 *>(o + 16 * nb) = v;
+    }
+    if (lse && g == 0)
+      lse[(int64_t)my_r[rb] * H + h] = l > 0.f ? (m_run[rb] + __log2f(l)) * kLn2 : -INFINITY;
   }
-  if (lse && g == 0)
-    lse[(int64_t)my_r * H + h] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 // Mask bits of the top-k sets: word w of row r holds positions 32 w .. 32 w + 31.

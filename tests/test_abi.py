@@ -244,7 +244,7 @@ def test_mha_validation(lib):
     assert call(r, ptrs=False) == INVALID
     assert call(r, name="dsa_mha_prefill_paged") == INVALID            # layout mismatch
     assert call(_rows(num_rows=0)) == OK
-    assert call(_rows(max_row_len=65537)) == UNSUPPORTED
+    assert call(_rows(max_row_len=16385)) == UNSUPPORTED
     need = lib.dsa_mha_prefill_workspace_size(64, 128, 2, 100, 0)
     assert need >= 2 * 64 * 128 * 256
     assert lib.dsa_mha_prefill_workspace_size(64, 128, 2, 100, 1) > need   # + the masks
