@@ -120,7 +120,9 @@ def _short_name(name: str) -> str:
 def summarize_trace(out_name: str, stats_csv: str, command: str):
     """profiles/<out_name>.md: the dsa kernels of a rocprofv3 --kernel-trace --stats run."""
     import csv
-    rows = [r for r in csv.DictReader(open(stats_csv)) if "dsa::" in r["Name"]]
+    # the library's kernels, and the rocBLAS GEMMs it calls (Tensile kernels are named Cijk_*)
+    rows = [r for r in csv.DictReader(open(stats_csv))
+            if "dsa::" in r["Name"] or r["Name"].startswith("Cijk_")]
     lines = [f"# {out_name}", "", "Command (from the repository root, on one MI355X):", "",
              "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | share of dsa time |",
