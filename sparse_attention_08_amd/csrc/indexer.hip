@@ -120,14 +120,17 @@ __device__ __forceinline__ int key_swz(int key) {
 #ifndef DSA_IDX_BLOCKS
 #define DSA_IDX_BLOCKS 256
 #endif
-#ifndef DSA_IDX_GROUP_BYTES
-#define DSA_IDX_GROUP_BYTES 4096
+#ifndef DSA_IDX_GROUP_BYTES_FP8
+#define DSA_IDX_GROUP_BYTES_FP8 4096
 #endif
-constexpr int kGroupBytes = DSA_IDX_GROUP_BYTES;   // keys streamed per wave per step
+#ifndef DSA_IDX_GROUP_BYTES_BF16
+#define DSA_IDX_GROUP_BYTES_BF16 4096
+#endif
 
 template <bool FP8>
 struct IdxCfg {
   static constexpr int kRowBytes = kIdxDim * (FP8 ? 1 : 2);   // 128 / 256
+  static constexpr int kGroupBytes = FP8 ? DSA_IDX_GROUP_BYTES_FP8 : DSA_IDX_GROUP_BYTES_BF16;
   static constexpr int kKeys = kGroupBytes / kRowBytes;        // keys per group (fp8: 32 at 4 KB)
   static constexpr int kTiles = kKeys / 16;                    // 16-key MFMA tiles per group
   static constexpr int kChunks = kRowBytes / 64;               // 16-byte chunks per lane per key
@@ -179,7 +182,7 @@ __device__ __forceinline__ void dma4(const void *g, void *lds) {
 // group this lane's 16 bytes belong to and the byte offset of its source chunk.
 template <bool FP8>
 struct DmaLane {
-  static constexpr int kJ = kGroupBytes / 1024;
+  static constexpr int kJ = IdxCfg<FP8>::kGroupBytes / 1024;
   int key[kJ];
   int byte[kJ];
   __device__ __forceinline__ void init(int lane) {
@@ -207,13 +210,13 @@ __device__ __forceinline__ void issue_group_loads(uint8_t *slot, const uint8_t *
   if (last == C::kKeys - 1) {            // the whole group lies inside the row
 #pragma unroll
     for (int j = 0; j < DmaLane<FP8>::kJ; ++j) dma16<NT>(gbase + dl.byte[j], slot + 1024 * j);
-    if constexpr (FP8) dma4(k_scale + row0 + min(lane, C::kKeys - 1), slot + kGroupBytes);
+    if constexpr (FP8) dma4(k_scale + row0 + min(lane, C::kKeys - 1), slot + C::kGroupBytes);
   } else {
 #pragma unroll
     for (int j = 0; j < DmaLane<FP8>::kJ; ++j)
       dma16<NT>(gbase + dl.byte[j] + (min(dl.key[j], last) - dl.key[j]) * C::kRowBytes,
                 slot + 1024 * j);
-    if constexpr (FP8) dma4(k_scale + row0 + min(lane, last), slot + kGroupBytes);
+    if constexpr (FP8) dma4(k_scale + row0 + min(lane, last), slot + C::kGroupBytes);
   }
 }
 template <bool FP8, bool PAGED>
@@ -266,7 +269,7 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
     const float v = head_sum(acc, hw);   // all 64 heads of key c, in every lane (., c)
     if (g == u) mine = v;
   }
-  if constexpr (FP8) mine *= reinterpret_cast<const float *>(slot + kGroupBytes)[lane];
+  if constexpr (FP8) mine *= reinterpret_cast<const float *>(slot + C::kGroupBytes)[lane];
   return mine;
 }
 
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kern
   int page_lane = 0;   // paged layout: lane j holds the page of the wave's j-th group
   DmaLane<FP8> dl;
   // loads per group: kGroupBytes/1024 key instructions (+1 scale instruction for fp8)
-  constexpr int kLoads = kGroupBytes / 1024 + (FP8 ? 1 : 0);
+  constexpr int kLoads = C::kGroupBytes / 1024 + (FP8 ? 1 : 0);
   auto group_start = [&](int j) { return (int64_t)(wr + j * waves_per_row) * C::kKeys; };
   auto group_page = [&](int j) {
     return PAGED ? __builtin_amdgcn_readlane(page_lane, j) : 0;
@@ -360,8 +363,11 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kern
         issue_group<FP8, PAGED>(ring + ((i + C::kDepth - 1) % C::kDepth) * C::kSlotBytes, k, k_scale,
                                 base_row, group_page(i + C::kDepth - 1), group_start(i + C::kDepth - 1),
                                 s_last, dl, lane, cached);
-        // group i is older than the C::kDepth-1 groups issued after it: loads complete in order
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (C::kDepth - 1)));
+        // group i is older than the C::kDepth-1 groups issued after it and than the score
+        // stores of the iterations since it was issued (one per iteration: every group holds a
+        // valid key); vector memory completes in order, and stores count too
+        if (i >= C::kDepth - 1) __builtin_amdgcn_s_waitcnt(vmcnt_only((kLoads + 1) * (C::kDepth - 1)));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoads * (C::kDepth - 1)));
       } else {
         // tail: nothing is issued past the wave's groups, so wait for every load in flight
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));

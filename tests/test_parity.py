@@ -191,6 +191,27 @@ def test_multi_token_decode(idx_dtype, paged):
     assert torch.equal(idx1, idx)
 
 
+def test_multi_token_decode_full_size():
+    """Two new tokens on each of 8 sequences of 131072 (fp8 indexer): the one-call decode
+    against the separate calls on every row, and the oracle on sampled rows."""
+    wl = workloads.prefill_batch([131072] * 8, new=[2] * 8, idx_dtype="fp8", seed=99, device=DEV,
+                                 name="mtp_full_128k_fp8")
+    wl = dataclasses.replace(wl, mode="decode")
+    say("one-call decode 8 x 128K x 2")
+    g, idx = _attention_decode_vs_separate(wl)
+    which = [0, 1, 9, 15]
+    g = g.cpu().numpy()
+    ref = oracle_indexer(wl, which=which)
+    lens = wl.row_len.cpu().numpy()
+    err = oracle.max_abs_rel(valid_logits(g[which], lens, which), valid_logits(ref, lens, which))
+    assert err <= TOL["fp8"], f"indexer err {err}"
+    exp = oracle.topk(np.nan_to_num(g[which], nan=0.0).astype(np.float32), lens[which], wl.topk)
+    assert np.array_equal(idx.cpu().numpy()[which], exp)
+    _check_mla(wl, idx, which, TOL["bf16"])
+    del wl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_multi_token_decode_shared_keys(paged):
     """16 rows per sequence over two sequences (bf16): the key-sharing indexer with fewer than 8
