@@ -6,11 +6,14 @@
 //
 // Decode-shaped work (few query rows, long contexts) is bound by the key stream from
 // HBM: every key byte is read once and meets 64 heads (64 flop/B in bf16, 128 flop/B
-// in fp8), far under the MFMA ridge.  The MFMA kernel therefore gives each wave a
-// contiguous span of keys, keeps the row's 64x128 query block resident in registers as
-// MFMA operands, streams keys straight from HBM into registers (no LDS round trip,
-// the next key group is in flight while the current one is multiplied), and fuses
+// in fp8), far under the MFMA ridge.  The MFMA kernel therefore deals each row's keys to
+// many waves in 4 KB groups, keeps the row's 64x128 query block resident in registers as
+// MFMA operands, streams the groups through a small private LDS ring per wave with
+// global->LDS loads (the next groups are in flight while one is multiplied), and fuses
 // ReLU, the head weights, the fp8 scales and the 64-head sum into the MFMA epilogue.
+// The same kernel serves every batch shape of fp8 keys and the bf16 batches with few rows
+// per sequence (decode, multi-token decode); indexer_prefill.hip shares key tiles between
+// rows for bf16 prefill.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
