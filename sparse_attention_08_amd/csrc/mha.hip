@@ -148,6 +148,24 @@ mha_prefill_kernel(
   const int vrow = 8 * g + (c >> 2);
   const int v_off = kNopeBytes + kRopeBytes + vrow * 256 + 8 * (c & 3);
   const int v_sw = val_swz(vrow) >> 1;
+  // LDS addresses of every operand read in ring slot 0 (a tile in slot i reads them plus
+  // i * kMhaStage: one add per read).  Opaque to the compiler, which would otherwise fold the
+  // shared block's address back in and spend two adds per read.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)sh.stage[0];
+  uint32_t qk_addr[6][2], pv_addr[8];
+#pragma unroll
+  for (int t = 0; t < 6; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      qk_addr[t][kb] = lds0 + (t < 4 ? a_nope[kb] + 16 * ((4 * t + g) ^ s_nope[kb])
+                                     : a_rope[kb] + 16 * ((4 * (t - 4) + g) ^ s_rope[kb]));
+      __asm__ volatile("" : "+v"(qk_addr[t][kb]));
+    }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    pv_addr[nb] = lds0 + v_off + 32 * (nb ^ v_sw);
+    __asm__ volatile("" : "+v"(pv_addr[nb]));
+  }
   // this wave's DMA instructions: i = wave + 4 u (u < 5); 0..7 nope (4 keys each), 8..11 rope
   // (8 keys each), 12..19 values (4 keys each)
   int d_key[kMhaDmaPerWave], d_src[kMhaDmaPerWave];
@@ -219,24 +237,43 @@ mha_prefill_kernel(
         src_stride[u] = (int64_t)H * 256;
       }
     }
-    auto issue = [&](int tile) {
-      uint8_t *st = sh.stage[tile % kMhaRing];
+    // per-lane source of each DMA instruction at key d_key[u] of a tile whose first key is
+    // cache row 0: a full tile adds its first key's cache row times the stride (uniform)
+    const uint8_t *lane_src[kMhaDmaPerWave];
+#pragma unroll
+    for (int u = 0; u < kMhaDmaPerWave; ++u)
+      lane_src[u] = src_base[u] + (int64_t)d_key[u] * src_stride[u];
+    auto issue = [&](int tile, uint8_t *st) {
       if constexpr (MASKED)
         if (wave < kMhaRows / 64) {   // rows 64 wave .. + 63: their mask word of this tile
           const int rr = min(r0 + 64 * wave + lane, R - 1);
           mha_dma4(mask + (int64_t)rr * mask_words + tile, st + kMaskOff + 256 * wave);
         }
+      if ((tile + 1) * kMhaKeys <= kmax) {
+        // every key of the tile exists: 32 consecutive cache rows (half of one page when paged)
+        int64_t row0;
+        if constexpr (PAGED)
+          row0 = (int64_t)__builtin_amdgcn_readfirstlane(sh.pages[tile >> 1]) * 64 +
+                 (tile & 1) * kMhaKeys;
+        else
+          row0 = base + (int64_t)tile * kMhaKeys;
 #pragma unroll
-      for (int u = 0; u < kMhaDmaPerWave; ++u) {
-        const int i = wave + kMhaWaves * u;
-        const int s = min(tile * kMhaKeys + d_key[u], kmax - 1);   // tail keys re-read the last
-        mha_dma16(src_base[u] + cache_row(s) * src_stride[u], st + 1024 * i);
+        for (int u = 0; u < kMhaDmaPerWave; ++u)
+          mha_dma16(lane_src[u] + row0 * src_stride[u], st + 1024 * (wave + kMhaWaves * u));
+      } else {
+#pragma unroll
+        for (int u = 0; u < kMhaDmaPerWave; ++u) {
+          const int s = min(tile * kMhaKeys + d_key[u], kmax - 1);   // tail keys re-read the last
+          mha_dma16(lane_src[u] + (cache_row(s) - d_key[u]) * src_stride[u],
+                    st + 1024 * (wave + kMhaWaves * u));
+        }
       }
     };
-    for (int t0 = 0; t0 < kMhaRing - 1 && t0 < n_tiles; ++t0) issue(t0);
+    for (int t0 = 0; t0 < kMhaRing - 1 && t0 < n_tiles; ++t0) issue(t0, sh.stage[t0]);
     // loads per tile issued by this wave (the only vector-memory operations of the loop)
     const int n_dma = kMhaDmaPerWave + ((MASKED && wave < kMhaRows / 64) ? 1 : 0);
-    for (int j = 0; j < n_tiles; ++j) {
+    // one tile in ring slot `slot`
+    auto step = [&](int j, int slot) {
       // this wave's part of tile j has landed once at most the younger tiles' loads are in
       // flight; every wave is done with tile j - 1, whose slot the next load reuses
       if (min(kMhaRing - 2, n_tiles - 1 - j) >= 1) {
@@ -246,8 +283,10 @@ mha_prefill_kernel(
         __builtin_amdgcn_s_waitcnt(mha_vmcnt(0));
       }
       lds_barrier();
-      if (j + kMhaRing - 1 < n_tiles) issue(j + kMhaRing - 1);
-      const uint8_t *st = sh.stage[j % kMhaRing];
+      if (j + kMhaRing - 1 < n_tiles)
+        issue(j + kMhaRing - 1, sh.stage[slot == 0 ? kMhaRing - 1 : slot - 1]);
+      const uint8_t *st = sh.stage[slot];
+      const uint32_t slot_off = (uint32_t)slot * kMhaStage;
       uint32_t mword[kRowBlocks] = {};
       if constexpr (MASKED)
 #pragma unroll
@@ -263,10 +302,8 @@ mha_prefill_kernel(
         bf16x8 x[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          x[kb] = t < 4 ? *reinterpret_cast<const bf16x8 *>(st + a_nope[kb] +
-                                                            16 * ((4 * t + g) ^ s_nope[kb]))
-                        : *reinterpret_cast<const bf16x8 *>(st + a_rope[kb] +
-                                                            16 * ((4 * (t - 4) + g) ^ s_rope[kb]));
+          x[kb] = *(const __attribute__((address_space(3))) bf16x8 *)(uintptr_t)(qk_addr[t][kb] +
+                                                                                 slot_off);
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
@@ -295,9 +332,11 @@ mha_prefill_kernel(
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              bool ok = mine[rb] && (s0 + 4 * kb + i) < my_len[rb];
-              if constexpr (MASKED) ok = ok && ((mword[rb] >> (8 * g + 4 * kb + i)) & 1u);
-              if (!ok) p[4 * kb + i] = -INFINITY;
+              // non-short-circuit tests and a select: one compare chain and a v_cndmask per
+              // score (short-circuit forms were compiled to a branch per score)
+              bool ok = mine[rb] & ((s0 + 4 * kb + i) < my_len[rb]);
+              if constexpr (MASKED) ok = ok & (((mword[rb] >> (8 * g + 4 * kb + i)) & 1u) != 0u);
+              p[4 * kb + i] = ok ? p[4 * kb + i] : -INFINITY;
             }
         }
         float mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
@@ -325,15 +364,18 @@ mha_prefill_kernel(
       // ---- O^T += V^T . P^T, value rows 16 nb + c; one operand load serves both row blocks
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const uint8_t *va = st + v_off + 32 * (nb ^ v_sw);
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)va);
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)(va + 4 * 256));
+        const uint32_t va = pv_addr[nb] + slot_off;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)(uintptr_t)va);
+        const bf16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((mha_lds_bf16x4_ptr)(uintptr_t)(va + 4 * 256));
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb)
           oacc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], oacc[rb][nb], 0, 0, 0);
       }
-    }
+    };
+    for (int j = 0, slot = 0; j < n_tiles; ++j, slot = slot == kMhaRing - 1 ? 0 : slot + 1)
+      step(j, slot);
   }
 
   // ---- epilogue: lane (g, c) holds row my_r[rb], value dims 16 nb + 4g + i
