@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
     DSA_OK = 0,
     DSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent layout */
-    DSA_ERR_UNSUPPORTED = 2,   /* valid request this build has no kernel for */
+    DSA_ERR_UNSUPPORTED = 2,   /* valid request the library has no kernel for */
     DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
     DSA_ERR_HIP = 4            /* a HIP launch failed */
 } dsa_status;
