@@ -337,19 +337,30 @@ def cpu_baseline(wl_host, n_rows: int):
     q_i, k_i, w = raw(wl_host.q_idx), raw(wl_host.k_idx), raw(wl_host.w)
     q_s, k_s = raw(wl_host.q_scale), raw(wl_host.k_scale)
     q, kv = raw(wl_host.q), raw(wl_host.kv)
-    t0 = time.perf_counter()
-    scores = oracle.indexer(wl_host.idx_dtype, q_i, w, k_i, rows, q_scale=q_s, k_scale=k_s,
-                            which=which, n_threads=threads)
     lens = h["row_len"][which]
-    sel = oracle.topk(np.nan_to_num(scores, nan=0.0), lens, wl_host.topk, n_threads=threads)
-    full_idx = np.full((wl_host.num_rows, wl_host.topk), -1, dtype=np.int32)
-    full_idx[which] = sel
-    oracle.sparse_mla(wl_host.mla_dtype, q, kv, full_idx, rows, wl_host.scale, wl_host.D_v,
-                      which=which, n_threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": n_rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+
+    def one_pass():
+        scores = oracle.indexer(wl_host.idx_dtype, q_i, w, k_i, rows, q_scale=q_s, k_scale=k_s,
+                                which=which, n_threads=threads)
+        sel = oracle.topk(np.nan_to_num(scores, nan=0.0), lens, wl_host.topk, n_threads=threads)
+        full_idx = np.full((wl_host.num_rows, wl_host.topk), -1, dtype=np.int32)
+        full_idx[which] = sel
+        oracle.sparse_mla(wl_host.mla_dtype, q, kv, full_idx, rows, wl_host.scale, wl_host.D_v,
+                          which=which, n_threads=threads)
+
+    # passes over the sample until about 12 core-seconds of oracle work (at most 20 passes)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        one_pass()
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt * threads >= 12.0 or passes >= 20:
+            break
+    return {"value": n_rows * passes / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_rows} of {wl_host.num_rows} decode rows of the same workload "
-                      f"(full context each), indexer + top-k + sparse MLA in fp64, {dt:.2f} s wall"}
+                      f"(full context each), indexer + top-k + sparse MLA in fp64, {passes} "
+                      f"passes, {dt:.2f} s wall on {threads} threads"}
 
 
 def main():
