@@ -3,10 +3,28 @@
 // grids and enqueue kernels, and return the launch status.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dsa {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per device (the
+// attribute belongs to the device; `done` holds one bit per device id).  Concurrent first
+// calls may both set it, which is harmless.
+template <class Kernel>
+inline hipError_t ensure_dynamic_lds(Kernel *kernel, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 struct RowsHost {
   int32_t num_rows;

@@ -429,14 +429,9 @@ static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const Ro
                              const uint8_t *q8, const float *q_scale, const uint8_t *k8,
                              const float *k_scale, const float *w, float *logits, int64_t ld,
                              uint32_t *hcnt, uint32_t *hlist, int hstride, int cached) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&indexer_mfma_kernel<FP8, PAGED, HIST>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = ensure_dynamic_lds(&indexer_mfma_kernel<FP8, PAGED, HIST>, (int)shm, lds_set);
+  if (e != hipSuccess) return e;
   indexer_mfma_kernel<FP8, PAGED, HIST><<<grid, IdxCfg<FP8>::kWaves * kWave, shm, stream>>>(
       rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
   return hipGetLastError();

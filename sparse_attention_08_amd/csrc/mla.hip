@@ -673,14 +673,10 @@ static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const Row
                                     int32_t *idx, int k, int per, int splits, uint16_t *o16,
                                     float *lse, uint16_t *part_o, float *part_lse,
                                     const MlaSel &sel) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mla_bf16_kernel<PAGED, SEL>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(MlaShared));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e =
+      ensure_dynamic_lds(&mla_bf16_kernel<PAGED, SEL>, (int)sizeof(MlaShared), lds_set);
+  if (e != hipSuccess) return e;
   mla_bf16_kernel<PAGED, SEL><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
       R, splits, k, per, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
       rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse, sel);

@@ -316,14 +316,10 @@ hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, 
     return hipGetLastError();
   }
   if (max_row_len <= kStageElems) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_row_kernel<true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)(sizeof(uint32_t) * kStageElems));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_dynamic_lds(&topk_row_kernel<true>,
+                                            (int)(sizeof(uint32_t) * kStageElems), lds_set);
+    if (e != hipSuccess) return e;
     topk_row_kernel<true><<<num_rows, kSmallThreads, sizeof(uint32_t) * max_row_len, stream>>>(
         logits, ld, row_len, k, idx);
   } else {
