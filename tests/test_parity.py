@@ -322,6 +322,28 @@ def test_attention_decode_matches_separate_calls(idx_dtype, paged):
     assert np.array_equal(idx.cpu().numpy(), exp)
 
 
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_attention_decode_all_scores_tied(idx_dtype):
+    """Zero head weights make every score +0: every position of a row ties, the rows' survivor
+    lists overflow the LDS selection (rows above 10240 positions), and both the fused top-k and
+    the attention that finishes its own selection take the select over the whole score row.
+    The selection is then the row's lowest min(len, k) positions, ascending."""
+    wl = workloads.decode(FUSED_LENS, idx_dtype=idx_dtype, seed=95, device=DEV,
+                          name=f"decode3_tied_{idx_dtype}")
+    wl.w.zero_()
+    say(f"fused decode all tied {idx_dtype}")
+    g, idx = _attention_decode_vs_separate(wl)
+    lens = wl.row_len.cpu().numpy()
+    exp = np.full((wl.num_rows, wl.topk), -1, dtype=np.int32)
+    for r, n in enumerate(lens):
+        exp[r, :min(n, wl.topk)] = np.arange(min(n, wl.topk))
+    assert np.array_equal(idx.cpu().numpy(), exp)
+    g_np = g.cpu().numpy()
+    for r, n in enumerate(lens):
+        assert np.all(g_np[r, :n] == 0.0)
+    _check_mla(wl, idx, [0, 5, 7], TOL["bf16"])
+
+
 def test_attention_decode_other_schedules_and_full_size():
     # short rows: the call runs the indexer+top-k call and the attention call in turn
     wl = workloads.decode(RAGGED, idx_dtype="bf16", seed=94, device=DEV, name="decode3_short")
