@@ -89,6 +89,20 @@ def test_c1_tiny_fp32_prefill_full():
     assert oracle.max_abs_rel(out.cpu().numpy()[short], dense) <= TOL["f32"]
 
 
+def test_f32_paged_prefill_batch():
+    """The f32 path (the tiny config's shapes: 4 x 32 indexer, 8 heads of 80 / 64) on a paged
+    cache: two sequences of 200 and 77 tokens prefilled together, pages permuted; indexer,
+    top-64 and attention against the oracle on every row."""
+    wl = workloads.prefill_batch([200, 77], idx_dtype="f32", mla_dtype="f32", paged=True, H_I=4,
+                                 D_I=32, H=8, D_qk=80, D_v=64, topk=64, seed=96, device=DEV,
+                                 name="f32_paged_prefill")
+    which = list(range(wl.num_rows))
+    g, ref, _ = _check_indexer(wl, which, TOL["f32"])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g)
+    _check_mla(wl, idx, which, TOL["f32"])
+
+
 # ------------------------------------------------------------------------ small ragged decode
 
 RAGGED = [1, 17, 100, 2047, 2048, 2049, 3000, 5001]

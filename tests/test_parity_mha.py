@@ -62,6 +62,19 @@ def test_masked_mode_topk_sets():
     _check(mb, list(range(0, R, 7)) + [R - 1], idx=torch.from_numpy(idx).to(DEV))
 
 
+def test_masked_mode_topk_sets_paged():
+    """The masked mode on a paged cache (pages permuted): a 700-token prefill with top-64 sets
+    (a random subset of each longer row's positions, -1 padded); 16 heads."""
+    mb = workloads.mha_batch([700], H=16, paged=True, seed=66, device=DEV)
+    R, k = mb.wl.num_rows, 64
+    g = np.random.default_rng(8)
+    idx = np.full((R, k), -1, np.int32)
+    for r in range(R):
+        pick = g.choice(r + 1, size=min(r + 1, k), replace=False)
+        idx[r, :len(pick)] = pick
+    _check(mb, list(range(0, R, 5)) + [R - 1], idx=torch.from_numpy(idx).to(DEV))
+
+
 def test_chunk_over_cached_prefix_paged():
     """A chunk of 96 new rows over a 1500-token prefix in a paged cache (rows start mid-tile),
     dense causal over the whole sequence."""
