@@ -26,7 +26,10 @@
 
 namespace dsa {
 
-constexpr int kSmallThreads = 1024;
+#ifndef DSA_TOPK_ROW_THREADS
+#define DSA_TOPK_ROW_THREADS 1024   // threads of the one-workgroup-per-row schedule
+#endif
+constexpr int kSmallThreads = DSA_TOPK_ROW_THREADS;
 #ifndef DSA_TOPK_FINAL_THREADS
 #define DSA_TOPK_FINAL_THREADS 1024
 #endif
