@@ -135,6 +135,47 @@ def _dev(t: torch.Tensor, name: str, dtypes=None):
     return t
 
 
+def _shape(t: Optional[torch.Tensor], name: str, shape):
+    """Checks t's shape against `shape` (None entries match any size); t None passes."""
+    if t is None:
+        return
+    ok = t.dim() == len(shape) and all(e is None or int(d) == int(e) for d, e in zip(t.shape, shape))
+    if not ok:
+        want = "[" + ", ".join("*" if e is None else str(int(e)) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _rows_of(rows: "Rows", t: torch.Tensor, name: str):
+    if int(t.shape[0]) != rows.num_rows:
+        raise ValueError(f"{name} has {int(t.shape[0])} rows, the batch has {rows.num_rows}")
+
+
+def _logits_shape(rows: "Rows", logits: torch.Tensor):
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, ld]")
+    _rows_of(rows, logits, "logits")
+    if int(logits.shape[1]) < rows.max_row_len:
+        raise ValueError(f"logits rows hold {int(logits.shape[1])} scores, max_row_len is "
+                         f"{rows.max_row_len}")
+
+
+def _key_cache_shape(rows: "Rows", k: torch.Tensor, D: int, k_scale):
+    """Key cache [N, D] (contiguous) or [P, 64, D] (paged), and its [N] / [P, 64] scales."""
+    if rows.paged:
+        _shape(k, "k", (None, rows.page_size, D))
+        _shape(k_scale, "k_scale", (int(k.shape[0]), rows.page_size))
+    else:
+        _shape(k, "k", (None, D))
+        _shape(k_scale, "k_scale", (int(k.shape[0]),))
+
+
+def _latent_cache_shape(rows: "Rows", kv: torch.Tensor, Dqk: int):
+    if rows.paged:
+        _shape(kv, "kv", (None, rows.page_size, Dqk))
+    else:
+        _shape(kv, "kv", (None, Dqk))
+
+
 def dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -180,6 +221,17 @@ class Rows:
 
 # --------------------------------------------------------------------------- stage 1
 
+def _indexer_shapes(rows: Rows, q, w, k, logits, q_scale, k_scale):
+    if q.dim() != 3:
+        raise ValueError("q must be [R, H, D]")
+    _rows_of(rows, q, "q")
+    R, H, D = (int(x) for x in q.shape)
+    _shape(w, "w", (R, H))
+    _shape(q_scale, "q_scale", (R, H))
+    _logits_shape(rows, logits)
+    _key_cache_shape(rows, k, D, k_scale)
+
+
 def _indexer(paged: bool, rows: Rows, q, w, k, logits, q_scale=None, k_scale=None):
     lib = load_library()
     _dev(q, "q")
@@ -190,8 +242,7 @@ def _indexer(paged: bool, rows: Rows, q, w, k, logits, q_scale=None, k_scale=Non
         _dev(q_scale, "q_scale", (torch.float32,))
     if k_scale is not None:
         _dev(k_scale, "k_scale", (torch.float32,))
-    if q.dim() != 3:
-        raise ValueError("q must be [R, H, D]")
+    _indexer_shapes(rows, q, w, k, logits, q_scale, k_scale)
     st = rows.struct()
     fn = lib.dsa_indexer_logits_paged if paged else lib.dsa_indexer_logits
     s = fn(ctypes.byref(st), dtype_code(q), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(q_scale),
@@ -221,10 +272,16 @@ def topk(logits, row_len, k: int, max_row_len: int, idx=None, ws=None):
     lib = load_library()
     _dev(logits, "logits", (torch.float32,))
     _dev(row_len, "row_len", (torch.int32,))
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, ld]")
     R = int(logits.shape[0])
+    _shape(row_len, "row_len", (R,))
+    if int(logits.shape[1]) < int(max_row_len):
+        raise ValueError(f"logits rows hold {int(logits.shape[1])} scores, max_row_len is {max_row_len}")
     if idx is None:
         idx = torch.empty((R, k), dtype=torch.int32, device=logits.device)
     _dev(idx, "idx", (torch.int32,))
+    _shape(idx, "idx", (R, k))
     need = topk_workspace_size(R, max_row_len, k)
     if ws is None and need > 0:
         ws = torch.zeros(need, dtype=torch.uint8, device=logits.device)   # zero before first use
@@ -244,7 +301,10 @@ def indexer_topk_workspace_size(num_rows: int, max_row_len: int, dtype, k: int) 
 
 def indexer_topk(rows: Rows, q, w, k, logits, topk_k: int, idx=None, q_scale=None, k_scale=None,
                  ws=None):
-    """Indexer scores into ``logits`` and their top-k positions into ``idx`` in one call."""
+    """Indexer scores into ``logits`` and their top-k positions into ``idx`` in one call.
+
+    A workspace ``ws`` passed in must be zero-filled before its first use; every call leaves
+    it ready for the next one."""
     lib = load_library()
     _dev(q, "q")
     _dev(k, "k")
@@ -254,15 +314,15 @@ def indexer_topk(rows: Rows, q, w, k, logits, topk_k: int, idx=None, q_scale=Non
         _dev(q_scale, "q_scale", (torch.float32,))
     if k_scale is not None:
         _dev(k_scale, "k_scale", (torch.float32,))
-    if q.dim() != 3:
-        raise ValueError("q must be [R, H, D]")
+    _indexer_shapes(rows, q, w, k, logits, q_scale, k_scale)
     R = rows.num_rows
     if idx is None:
         idx = torch.empty((R, topk_k), dtype=torch.int32, device=logits.device)
     _dev(idx, "idx", (torch.int32,))
+    _shape(idx, "idx", (R, topk_k))
     need = indexer_topk_workspace_size(R, rows.max_row_len, dtype_code(q), topk_k)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=logits.device)   # zero before first use
     st = rows.struct()
     fn = lib.dsa_indexer_topk_paged if rows.paged else lib.dsa_indexer_topk
     s = fn(ctypes.byref(st), dtype_code(q), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(q_scale),
@@ -286,13 +346,20 @@ def _mla(name: str, rows: Rows, q, kv, idx, scale: float, d_v: int, out=None, ls
     _dev(idx, "idx", (torch.int32,))
     if q.dim() != 3:
         raise ValueError("q must be [R, H, d_qk]")
+    _rows_of(rows, q, "q")
     R, H, Dqk = (int(x) for x in q.shape)
+    _latent_cache_shape(rows, kv, Dqk)
+    if idx.dim() != 2:
+        raise ValueError("idx must be [R, k]")
+    _shape(idx, "idx", (R, None))
     k = int(idx.shape[-1])
     if out is None:
         out = torch.empty((R, H, d_v), dtype=q.dtype, device=q.device)
     _dev(out, "out", (q.dtype,))
+    _shape(out, "out", (R, H, d_v))
     if lse is not None:
         _dev(lse, "lse", (torch.float32,))
+        _shape(lse, "lse", (R, H))
     if not name.startswith("dsa_sparse_mla_prefill"):
         need = sparse_mla_workspace_size(R, H, d_v, k)
         if ws is None and need > 0:
@@ -345,6 +412,8 @@ def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, k
 
     Fills ``logits`` and ``idx`` as :func:`indexer_topk` and returns ``out`` as
     :func:`sparse_mla_decode` (``_paged`` for a paged ``rows``) would on that ``idx``.
+    A workspace ``ws`` passed in must be zero-filled before its first use; every call leaves
+    it ready for the next one.
     """
     lib = load_library()
     for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (kv, "kv")):
@@ -358,18 +427,24 @@ def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, k
         _dev(k_scale, "k_scale", (torch.float32,))
     if q_idx.dim() != 3 or q.dim() != 3:
         raise ValueError("q_idx must be [R, H_I, D_I] and q [R, H, d_qk]")
+    _indexer_shapes(rows, q_idx, w, k_idx, logits, q_scale, k_scale)
+    _rows_of(rows, q, "q")
     R, H, Dqk = (int(x) for x in q.shape)
+    _latent_cache_shape(rows, kv, Dqk)
     if idx is None:
         idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
     _dev(idx, "idx", (torch.int32,))
+    _shape(idx, "idx", (R, topk))
     if out is None:
         out = torch.empty((R, H, d_v), dtype=q.dtype, device=q.device)
     _dev(out, "out", (q.dtype,))
+    _shape(out, "out", (R, H, d_v))
     if lse is not None:
         _dev(lse, "lse", (torch.float32,))
+        _shape(lse, "lse", (R, H))
     need = sparse_attention_decode_workspace_size(R, rows.max_row_len, dtype_code(q_idx), topk, H, d_v)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)   # zero before first use
     st = rows.struct()
     name = "dsa_sparse_attention_decode_paged" if rows.paged else "dsa_sparse_attention_decode"
     s = getattr(lib, name)(
@@ -494,19 +569,24 @@ def mha_prefill(rows: Rows, q, kv, w_uk, w_uv, scale: float, idx=None, out=None,
     _dev(w_uv, "w_uv", (torch.bfloat16,))
     if q.dim() != 3 or q.shape[2] != 192:
         raise ValueError("q must be [R, H, 192]")
+    _rows_of(rows, q, "q")
     R, H = int(q.shape[0]), int(q.shape[1])
+    _latent_cache_shape(rows, kv, 576)
     if w_uk.shape != (H, 128, 512) or w_uv.shape != (H, 128, 512) or kv.shape[-1] != 576:
         raise ValueError("w_uk / w_uv must be [H, 128, 512] and kv rows 576 wide")
     n_cache = kv.numel() // 576
     k = 0
     if idx is not None:
         _dev(idx, "idx", (torch.int32,))
+        _shape(idx, "idx", (R, None))
         k = int(idx.shape[1])
     if out is None:
         out = torch.empty((R, H, 128), dtype=torch.bfloat16, device=q.device)
     _dev(out, "out", (torch.bfloat16,))
+    _shape(out, "out", (R, H, 128))
     if lse is not None:
         _dev(lse, "lse", (torch.float32,))
+        _shape(lse, "lse", (R, H))
     need = mha_prefill_workspace_size(n_cache, H, R, rows.max_row_len, idx is not None)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

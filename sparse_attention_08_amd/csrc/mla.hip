@@ -21,7 +21,6 @@
 // writes a normalised bf16 partial and its log-sum-exp, and a combine kernel merges them.
 #include "dsa_device.h"
 #include "dsa_launch.h"
-#include "topk_select.h"
 
 namespace dsa {
 
@@ -153,7 +152,6 @@ __device__ __forceinline__ int swz(int row) {
 typedef bf16x4 __attribute__((address_space(3))) *lds_bf16x4_ptr;
 typedef void __attribute__((address_space(3))) *lds_void_ptr;
 
-constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 struct MlaShared {
   uint8_t tiles[kRing][kTileBytes];
@@ -249,22 +247,6 @@ __device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
   return c.r < R;
 }
 
-// Finishing the row's top-k inside the attention workgroups (see mla_bf16_kernel).
-struct MlaSel {
-  const float *logits;   // the score rows (fallback of degenerate rows)
-  int64_t ld;
-  MbWs ws;               // the chunked filter's survivors
-  int chunks;            // 4096-score chunks of the longest row
-};
-constexpr size_t kSelScratchBytes = (sizeof(BlockScratch<kMlaThreads>) + 15) & ~(size_t)15;
-constexpr size_t kSelKeyOff = kSelScratchBytes;
-constexpr size_t kSelPosOff = kSelKeyOff + sizeof(uint32_t) * kSurvivorCap;
-constexpr size_t kSelCoffOff = kSelPosOff + sizeof(int32_t) * kSurvivorCap;
-constexpr size_t kSelListOff =
-    (kSelCoffOff + sizeof(uint32_t) * (kMaxChunks + 1) + 15) & ~(size_t)15;
-static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing * kTileBytes,
-              "selection scratch fits the tile ring");
-
 // One workgroup: all 128 heads of query row r over one split of its top-k slots.
 // Wave w owns heads 16w .. 16w+15 over the full contractions.  Per tile of 32 entries it
 // forms S^T = C . Q^T (entries as MFMA rows, 2 blocks of 16 entries x its 16 heads, q in
@@ -272,20 +254,16 @@ static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing
 // value dims, V^T read from the same LDS tile with the transposing LDS read.  Entry rows
 // of the score blocks are permuted (block kb, row 4g + i <-> entry 8g + 4kb + i) so that
 // each lane's weights are exactly the B operand of the value product.
-// SEL: the row's top-k is not given but finished here, from the survivors of the chunked
-// top-k filter (every split of the row selects the row's k positions in its tile ring, which
-// is free until the first tile load, keeps its own slots and writes them to idx as well).
-//
 // The leading arguments are the ones the prologue needs first (scalars and pointers, so
 // the launch can preload them into registers).
-template <bool PAGED, bool SEL>
+template <bool PAGED>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
-    int R, int splits, int k, int slots_per_split, int32_t *__restrict__ idx,
+    int R, int splits, int k, int slots_per_split, const int32_t *__restrict__ idx,
     const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
     const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
     const uint8_t *__restrict__ kv, uint16_t *__restrict__ out, float *__restrict__ lse,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_lse, MlaSel sel) {
+    uint16_t *__restrict__ part_o, float *__restrict__ part_lse) {
   constexpr int H = kHeadsPerBlock;
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared &sh = *reinterpret_cast<MlaShared *>(mla_smem);
@@ -298,7 +276,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int h0 = wave * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
-  int32_t *idx_row = idx + (int64_t)r * k + slot_begin;   // read, or written when SEL
+  const int32_t *idx_row = idx + (int64_t)r * k + slot_begin;
 
   // cache rows of the valid slots, compacted in slot order
   int n_valid = 0;
@@ -313,41 +291,16 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < 18; ++t) qf[t] = qp[4 * t];
     };
-    if constexpr (SEL) {
-      // the row's k positions, ascending, into the tile ring; slot j of the row is the j-th.
-      // The query loads go out after the selection, whose loads they would hold up.
-      const SurvivorLoads<kMlaThreads> sl = issue_survivor_loads<kMlaThreads>(sel.ws, r, sel.chunks);
-      const int n = row_len[r];
-      int32_t *lst = reinterpret_cast<int32_t *>(sh.tiles[0] + kSelListOff);
-      if (n > k) {
-        select_from_survivors<kMlaThreads>(
-            sl, sel.logits, sel.ld, sel.ws, r, n, k, lst,
-            *reinterpret_cast<BlockScratch<kMlaThreads> *>(sh.tiles[0]),
-            reinterpret_cast<uint32_t *>(sh.tiles[0] + kSelKeyOff),
-            reinterpret_cast<int32_t *>(sh.tiles[0] + kSelPosOff),
-            reinterpret_cast<uint32_t *>(sh.tiles[0] + kSelCoffOff));
-        __syncthreads();
-      }
-      load_q();
+    // the slot loads go out first (they need only the launch arguments), then the query
+    // block, then the row's descriptor loads: waits on vector memory are in issue order,
+    // so resolving the slots does not wait for the query block
 #pragma unroll
-      for (int j = 0; j < kSlotRounds; ++j) {
-        const int t = j * kMlaThreads + threadIdx.x;
-        const int slot = slot_begin + t;
-        sv[j] = t < n_slots ? (n > k ? lst[slot] : (slot < n ? slot : -1)) : -1;
-        if (t < n_slots) idx_row[t] = sv[j];
-      }
-    } else {
-      // the slot loads go out first (they need only the launch arguments), then the query
-      // block, then the row's descriptor loads: waits on vector memory are in issue order,
-      // so resolving the slots does not wait for the query block
-#pragma unroll
-      for (int j = 0; j < kSlotRounds; ++j) {
-        const int t = j * kMlaThreads + threadIdx.x;
-        sv[j] = t < n_slots ? idx_row[t] : -1;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_q();
+    for (int j = 0; j < kSlotRounds; ++j) {
+      const int t = j * kMlaThreads + threadIdx.x;
+      sv[j] = t < n_slots ? idx_row[t] : -1;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_q();
     __builtin_amdgcn_sched_barrier(0);
     const RowsDev rows{row_seq, row_len, seq_start, page_table, max_pages};
     const int len = row_len[r], b = row_seq[r];
@@ -667,27 +620,24 @@ size_t mla_workspace_bytes(int num_rows, int n_heads, int d_v, int k) {
   return (size_t)num_rows * splits * n_heads * (sizeof(uint16_t) * (size_t)d_v + sizeof(float));
 }
 
-template <bool PAGED, bool SEL>
+template <bool PAGED>
 static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const RowsDev &rows, int R,
                                     float sl2, const uint16_t *q16, const uint8_t *kv8,
-                                    int32_t *idx, int k, int per, int splits, uint16_t *o16,
-                                    float *lse, uint16_t *part_o, float *part_lse,
-                                    const MlaSel &sel) {
+                                    const int32_t *idx, int k, int per, int splits, uint16_t *o16,
+                                    float *lse, uint16_t *part_o, float *part_lse) {
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e =
-      ensure_dynamic_lds(&mla_bf16_kernel<PAGED, SEL>, (int)sizeof(MlaShared), lds_set);
+      ensure_dynamic_lds(&mla_bf16_kernel<PAGED>, (int)sizeof(MlaShared), lds_set);
   if (e != hipSuccess) return e;
-  mla_bf16_kernel<PAGED, SEL><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
+  mla_bf16_kernel<PAGED><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
       R, splits, k, per, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
-      rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse, sel);
+      rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse);
   return hipGetLastError();
 }
 
-// idx is read (sel == nullptr) or written: with sel the kernel finishes the row's top-k from
-// the chunked filter's survivors.
-static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale, const void *q,
-                              const void *kv, int32_t *idx, int k, void *out, float *lse,
-                              int splits, void *ws, const MlaSel *sel, hipStream_t stream) {
+hipError_t launch_mla_bf16(const RowsHost &rh, bool paged, int H, float scale, const void *q,
+                           const void *kv, const int32_t *idx, int k, void *out, float *lse,
+                           int splits, void *ws, hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
   const int per = (((k + splits - 1) / splits) + kTile - 1) / kTile * kTile;
   uint16_t *part_o = nullptr;
@@ -702,41 +652,15 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
   const uint8_t *kv8 = static_cast<const uint8_t *>(kv);
   uint16_t *o16 = static_cast<uint16_t *>(out);
   const float sl2 = scale * kLog2e;
-  const MlaSel none{};
-  hipError_t e;
-  if (sel)
-    e = paged ? launch_mla_kernel<true, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                              splits, o16, lse, part_o, part_lse, *sel)
-              : launch_mla_kernel<false, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                               splits, o16, lse, part_o, part_lse, *sel);
-  else
-    e = paged ? launch_mla_kernel<true, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                               splits, o16, lse, part_o, part_lse, none)
-              : launch_mla_kernel<false, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                                splits, o16, lse, part_o, part_lse, none);
+  const hipError_t e =
+      paged ? launch_mla_kernel<true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per, splits,
+                                      o16, lse, part_o, part_lse)
+            : launch_mla_kernel<false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per, splits,
+                                       o16, lse, part_o, part_lse);
   if (e != hipSuccess || splits == 1) return e;
   mla_combine_kernel<<<8u * (unsigned)((R + 7) / 8) * (H / kCombHeads), 256, 0, stream>>>(
       R, H, splits, part_o, part_lse, o16, lse);
   return hipGetLastError();
-}
-
-hipError_t launch_mla_bf16(const RowsHost &rh, bool paged, int H, float scale, const void *q,
-                           const void *kv, const int32_t *idx, int k, void *out, float *lse,
-                           int splits, void *ws, hipStream_t stream) {
-  return launch_bf16(rh, paged, H, scale, q, kv, const_cast<int32_t *>(idx), k, out, lse, splits,
-                     ws, nullptr, stream);
-}
-
-hipError_t launch_mla_bf16_select(const RowsHost &rh, bool paged, int H, float scale,
-                                  const void *q, const void *kv, int32_t *idx, int k, void *out,
-                                  float *lse, int splits, void *ws, const float *logits,
-                                  int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream) {
-  MlaSel sel;
-  sel.logits = logits;
-  sel.ld = ld;
-  sel.ws = topk_chunk_ws(topk_ws, rh.num_rows, rh.max_row_len, hist_lists);
-  sel.chunks = (rh.max_row_len + kChunk - 1) / kChunk;
-  return launch_bf16(rh, paged, H, scale, q, kv, idx, k, out, lse, splits, ws, &sel, stream);
 }
 
 }  // namespace dsa
