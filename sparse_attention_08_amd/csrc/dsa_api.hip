@@ -167,12 +167,22 @@ int mla_common(const dsa_rows *rows, bool paged, MlaMode mode, int dtype, int n_
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Stages 1-3 of a decode batch: the indexer with its top-k (in one launch for decode-shaped
-// batches), then the sparse MLA over the selection.  The top-k workspace comes first, so its
-// arrival counters sit at the start of the caller's workspace.
+// Stages 1-3 of a decode batch: for decode-shaped batches with the bf16 attention one launch
+// runs them all (decode.hip); otherwise the indexer with its top-k, then the sparse MLA over
+// the selection.  Either way the workspace's counters sit at its start.
+bool onelaunch_shape(int num_rows, int max_row_len, int idx_dtype, int topk) {
+  if (idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3) return false;
+  return dsa::decode_onelaunch_ok(num_rows, max_row_len, idx_dtype == DSA_FP8_E4M3, topk);
+}
+
+// The size queries do not see the number of sequences (which decides between the one-launch
+// decode and the two calls), so the workspace covers both.
 size_t decode_ws(int num_rows, int max_row_len, int idx_dtype, int topk, int n_heads, int d_v) {
-  return align256(indexer_topk_ws(num_rows, max_row_len, idx_dtype, topk)) +
-         dsa::mla_workspace_bytes(num_rows, n_heads, d_v, topk);
+  const size_t two = align256(indexer_topk_ws(num_rows, max_row_len, idx_dtype, topk)) +
+                     dsa::mla_workspace_bytes(num_rows, n_heads, d_v, topk);
+  if (!onelaunch_shape(num_rows, max_row_len, idx_dtype, topk)) return two;
+  return std::max(two, dsa::decode_onelaunch_ws_bytes(num_rows, max_row_len,
+                                                      idx_dtype == DSA_FP8_E4M3, topk));
 }
 
 int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int idx_heads,
@@ -199,6 +209,11 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
   const size_t tk_bytes = align256(indexer_topk_ws(R, L, idx_dtype, topk));
   const size_t need = decode_ws(R, L, idx_dtype, topk, n_heads, d_v);
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (dtype == DSA_BF16 && !shares_keys(rows, idx_dtype) && onelaunch_shape(R, L, idx_dtype, topk))
+    return status_of(dsa::launch_decode_onelaunch(
+        to_host(rows), paged, idx_dtype == DSA_FP8_E4M3, q_idx, q_idx_scale, k_idx, k_idx_scale, w,
+        logits, ld_logits, topk, idx, softmax_scale, q, kv, out, lse, ws,
+        static_cast<hipStream_t>(stream)));
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   void *tk_ws = tk_bytes ? wsb : nullptr;
   void *ml_ws = need > tk_bytes ? wsb + tk_bytes : nullptr;

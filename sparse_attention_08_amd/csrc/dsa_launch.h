@@ -78,6 +78,19 @@ hipError_t launch_mla_bf16(const RowsHost &rows, bool paged, int H, float scale,
                            const void *kv, const int32_t *idx, int k, void *out, float *lse,
                            int splits, void *ws, hipStream_t stream);
 
+// ---- the whole decode step in one launch (decode.hip) ----
+// Indexer (bf16 or fp8 keys), top-k and bf16 sparse MLA (128 heads, 576 / 512) of a
+// decode-shaped batch (at most 256 rows of at most 1M positions): logits, idx, out and lse as
+// the separate calls give them.  ws: decode_onelaunch_ws_bytes bytes whose leading counters
+// are zero before the call and are left zero by it.
+bool decode_onelaunch_ok(int num_rows, int max_row_len, bool fp8, int k);
+size_t decode_onelaunch_ws_bytes(int num_rows, int max_row_len, bool fp8, int k);
+hipError_t launch_decode_onelaunch(const RowsHost &rows, bool paged, bool fp8, const void *q_idx,
+                                   const float *q_scale, const void *k_idx, const float *k_scale,
+                                   const float *w, float *logits, int64_t ld, int topk,
+                                   int32_t *idx, float scale, const void *q, const void *kv,
+                                   void *out, float *lse, void *ws, hipStream_t stream);
+
 // ---- masked MHA mode (short prefill) ----
 // Workspace: decompressed K_nope and V ([cache_rows, H, 128] bf16 each) and, with idx, the
 // rows' top-k sets as bit masks.

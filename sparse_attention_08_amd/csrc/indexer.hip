@@ -130,9 +130,11 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kThreads) void indexer_mfma_kernel(
     __syncthreads();   // the chunk's scores are in LDS; the query block and the rings are free
     PublishLds &pl = *reinterpret_cast<PublishLds *>(smem);
     if (!publish_chunk<C::kThreads>(sc, reinterpret_cast<uint32_t *>(smem + C::kQBytes), pl, sel.ws, r,
-                                    blockIdx.x, lo, hi, out, len > sel.k))
+                                    blockIdx.x, lo, hi, len, out, len > sel.k))
       return;
     __syncthreads();   // the publication scratch is reused by the selection
+    if (threadIdx.x == 0)   // every workgroup of the row has counted itself: ready for the next call
+      __hip_atomic_store(sel.ws.arrive + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     select_published<C::kThreads>(sel.ws, r, len, sel.k, span, out, sel.idx + (int64_t)r * sel.k,
                                   *reinterpret_cast<SelectLds<C::kThreads> *>(smem));
   } else {
@@ -201,16 +203,16 @@ int indexer_blocks_per_row(int num_rows, int max_row_len, bool fp8) {
 }
 
 // Candidates kept per chunk for the in-kernel selection: about four times a chunk's share of
-// k, at most 16 per selecting thread and at most 1024.
+// k (at least 256), at most kSelCandPerThread per selecting thread and at most 1024.
 int indexer_sel_cap(int num_rows, int max_row_len, bool fp8, int k) {
   const int C = blocks_per_row(num_rows, max_row_len, fp8, true);
   const int nt = fp8 ? IdxCfg<true>::kThreads : IdxCfg<false>::kThreads;
   int tpl = nt;
   while (tpl > 1 && tpl * C > nt) tpl >>= 1;
-  const int want = (4 * k + C - 1) / C;
+  const int want = max(256, (4 * k + C - 1) / C);
   int cap = 16;
   while (cap < want) cap <<= 1;
-  const int lim = 16 * tpl < 1024 ? 16 * tpl : 1024;
+  const int lim = kSelCandPerThread * tpl < 1024 ? kSelCandPerThread * tpl : 1024;
   if (cap > lim) cap = lim;
   if (cap < tpl) cap = tpl;
   return cap;
