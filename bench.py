@@ -269,7 +269,7 @@ def mha_bench(args):
     logits = torch.empty((L, L), dtype=torch.float32, device="cuda")
     idx = torch.empty((L, w2.topk), dtype=torch.int32, device="cuda")
     o2 = torch.empty((L, w2.H, w2.D_v), dtype=torch.bfloat16, device="cuda")
-    tk_ws = torch.zeros(max(dsa.indexer_topk_workspace_size(L, L, w2.q_idx.dtype, w2.topk), 1),
+    tk_ws = torch.empty(max(dsa.indexer_topk_workspace_size(L, L, w2.q_idx.dtype, w2.topk), 1),
                         dtype=torch.uint8, device="cuda")
 
     def mha():
@@ -419,7 +419,7 @@ def main():
         idx_fn(rows, wl.q_idx, wl.w, wl.k_idx, logits, q_scale=wl.q_scale, k_scale=wl.k_scale)
 
     fused_ws_n = dsa.indexer_topk_workspace_size(R, wl.max_row_len, wl.q_idx.dtype, wl.topk)
-    fused_ws = torch.zeros(max(fused_ws_n, 1), dtype=torch.uint8, device=dev)   # zeroed once
+    fused_ws = torch.empty(max(fused_ws_n, 1), dtype=torch.uint8, device=dev)
 
     def stage_indexer_topk():
         dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, idx=idx,
@@ -430,7 +430,7 @@ def main():
 
     dec_ws_n = 0 if prefill else dsa.sparse_attention_decode_workspace_size(
         R, wl.max_row_len, wl.q_idx.dtype, wl.topk, wl.H, wl.D_v)
-    dec_ws = torch.zeros(max(dec_ws_n, 1), dtype=torch.uint8, device=dev)   # zeroed once
+    dec_ws = torch.empty(max(dec_ws_n, 1), dtype=torch.uint8, device=dev)
 
     def stage_decode():
         dsa.sparse_attention_decode(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, wl.q, wl.kv,

@@ -301,10 +301,7 @@ def indexer_topk_workspace_size(num_rows: int, max_row_len: int, dtype, k: int) 
 
 def indexer_topk(rows: Rows, q, w, k, logits, topk_k: int, idx=None, q_scale=None, k_scale=None,
                  ws=None):
-    """Indexer scores into ``logits`` and their top-k positions into ``idx`` in one call.
-
-    A workspace ``ws`` passed in must be zero-filled before its first use; every call leaves
-    it ready for the next one."""
+    """Indexer scores into ``logits`` and their top-k positions into ``idx`` in one call."""
     lib = load_library()
     _dev(q, "q")
     _dev(k, "k")
@@ -322,7 +319,7 @@ def indexer_topk(rows: Rows, q, w, k, logits, topk_k: int, idx=None, q_scale=Non
     _shape(idx, "idx", (R, topk_k))
     need = indexer_topk_workspace_size(R, rows.max_row_len, dtype_code(q), topk_k)
     if ws is None and need > 0:
-        ws = torch.zeros(need, dtype=torch.uint8, device=logits.device)   # zero before first use
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
     st = rows.struct()
     fn = lib.dsa_indexer_topk_paged if rows.paged else lib.dsa_indexer_topk
     s = fn(ctypes.byref(st), dtype_code(q), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(q_scale),
@@ -412,8 +409,6 @@ def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, k
 
     Fills ``logits`` and ``idx`` as :func:`indexer_topk` and returns ``out`` as
     :func:`sparse_mla_decode` (``_paged`` for a paged ``rows``) would on that ``idx``.
-    A workspace ``ws`` passed in must be zero-filled before its first use; every call leaves
-    it ready for the next one.
     """
     lib = load_library()
     for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (kv, "kv")):
@@ -444,7 +439,7 @@ def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, k
         _shape(lse, "lse", (R, H))
     need = sparse_attention_decode_workspace_size(R, rows.max_row_len, dtype_code(q_idx), topk, H, d_v)
     if ws is None and need > 0:
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)   # zero before first use
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = rows.struct()
     name = "dsa_sparse_attention_decode_paged" if rows.paged else "dsa_sparse_attention_decode"
     s = getattr(lib, name)(

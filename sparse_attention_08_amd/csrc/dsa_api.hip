@@ -90,22 +90,25 @@ int indexer_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int
                                   logits, ld_logits, static_cast<hipStream_t>(stream)));
 }
 
-// Batches whose indexer workgroups also select each row's top-k in the same launch: the
-// one-row MFMA indexer (bf16 or fp8, not the key-sharing prefill indexer) on decode-shaped
-// batches.  The size queries do not see the number of sequences, so their answer covers
-// both this and the separate top-k.
-bool sel_shape(int num_rows, int max_row_len, int dtype) {
-  if (dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return false;
-  return dsa::indexer_sel_ok(num_rows, max_row_len, dtype == DSA_FP8_E4M3);
+// Histogram lists per row when the per-row indexer's workgroups feed the top-k directly, or 0
+// when the batch takes the separate path (f32 indexer, the one-workgroup-per-row top-k
+// schedule, or the shared-key indexer).
+int hist_lists_of_shape(int num_rows, int max_row_len, int dtype) {
+  if (dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return 0;
+  const int nh = dsa::indexer_blocks_per_row(num_rows, max_row_len, dtype == DSA_FP8_E4M3);
+  return dsa::topk_hist_fusable(num_rows, max_row_len, nh) ? nh : 0;
 }
-bool sel_fused(const dsa_rows *rows, int dtype) {
-  return !shares_keys(rows, dtype) && sel_shape(rows->num_rows, rows->max_row_len, dtype);
+int fused_hist_lists(const dsa_rows *rows, int dtype) {
+  if (shares_keys(rows, dtype)) return 0;
+  return hist_lists_of_shape(rows->num_rows, rows->max_row_len, dtype);
 }
 
+// Workspace of the indexer + top-k for any batch of this shape: the size queries do not see
+// the number of sequences, so this covers both the fused and the separate top-k.
 size_t indexer_topk_ws(int num_rows, int max_row_len, int dtype, int k) {
   const size_t sep = dsa::topk_workspace_bytes(num_rows, max_row_len, k);
-  if (!sel_shape(num_rows, max_row_len, dtype)) return sep;
-  return std::max(sep, dsa::indexer_sel_ws_bytes(num_rows, max_row_len, dtype == DSA_FP8_E4M3, k));
+  const int nh = hist_lists_of_shape(num_rows, max_row_len, dtype);
+  return nh ? std::max(sep, dsa::topk_fused_workspace_bytes(num_rows, max_row_len, nh)) : sep;
 }
 
 int indexer_topk_common(const dsa_rows *rows, bool paged, int dtype, int n_heads, int head_dim,
@@ -122,10 +125,15 @@ int indexer_topk_common(const dsa_rows *rows, bool paged, int dtype, int n_heads
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = rows->num_rows, L = rows->max_row_len;
-  if (sel_fused(rows, dtype))
-    return status_of(dsa::launch_indexer_select(to_host(rows), paged, dtype == DSA_FP8_E4M3, q,
-                                                q_scale, k, k_scale, w, logits, ld_logits, topk,
-                                                idx, ws, s));
+  const int nh = fused_hist_lists(rows, dtype);
+  if (nh) {
+    const dsa::TopkHistDest dest = dsa::topk_hist_dest(ws, R, L, nh);
+    hipError_t e = dsa::launch_indexer_mfma_hist(to_host(rows), paged, dtype == DSA_FP8_E4M3, q,
+                                                 q_scale, k, k_scale, w, logits, ld_logits, dest, s);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    return status_of(dsa::launch_topk_after_hist(logits, ld_logits, rows->row_len, R, L, topk, idx,
+                                                 ws, nh, s));
+  }
   hipError_t e = indexer_launch(rows, paged, dtype, n_heads, head_dim, q, q_scale, k, k_scale, w,
                                 logits, ld_logits, s);
   if (e != hipSuccess) return DSA_ERR_HIP;
@@ -165,24 +173,22 @@ int mla_common(const dsa_rows *rows, bool paged, MlaMode mode, int dtype, int n_
                                         splits, ws, s));
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Stages 1-3 of a decode batch: for decode-shaped batches with the bf16 attention one launch
-// runs them all (decode.hip); otherwise the indexer with its top-k, then the sparse MLA over
-// the selection.  Either way the workspace's counters sit at its start.
-bool onelaunch_shape(int num_rows, int max_row_len, int idx_dtype, int topk) {
-  if (idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3) return false;
-  return dsa::decode_onelaunch_ok(num_rows, max_row_len, idx_dtype == DSA_FP8_E4M3, topk);
+// Stages 1-3 of a decode batch.  Up to kSelectInAttentionRows long rows (batches whose
+// indexer feeds the top-k histograms) with the bf16 attention finish the selection inside
+// the attention workgroups; every other batch runs the two calls in turn.  Each split of a
+// row repeats the row's selection, which pays while the saved launch outweighs the longer
+// attention prologue (measured: 8 rows of 128K gain, 32 rows of up to 64K lose).
+constexpr int kSelectInAttentionRows = 16;
+bool decode_fusable(const dsa_rows *rows, int idx_dtype, int dtype) {
+  return dtype == DSA_BF16 && rows->num_rows <= kSelectInAttentionRows &&
+         fused_hist_lists(rows, idx_dtype) > 0;
 }
 
-// The size queries do not see the number of sequences (which decides between the one-launch
-// decode and the two calls), so the workspace covers both.
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t decode_ws(int num_rows, int max_row_len, int idx_dtype, int topk, int n_heads, int d_v) {
-  const size_t two = align256(indexer_topk_ws(num_rows, max_row_len, idx_dtype, topk)) +
-                     dsa::mla_workspace_bytes(num_rows, n_heads, d_v, topk);
-  if (!onelaunch_shape(num_rows, max_row_len, idx_dtype, topk)) return two;
-  return std::max(two, dsa::decode_onelaunch_ws_bytes(num_rows, max_row_len,
-                                                      idx_dtype == DSA_FP8_E4M3, topk));
+  return align256(indexer_topk_ws(num_rows, max_row_len, idx_dtype, topk)) +
+         dsa::mla_workspace_bytes(num_rows, n_heads, d_v, topk);
 }
 
 int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int idx_heads,
@@ -209,19 +215,31 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
   const size_t tk_bytes = align256(indexer_topk_ws(R, L, idx_dtype, topk));
   const size_t need = decode_ws(R, L, idx_dtype, topk, n_heads, d_v);
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
-  if (dtype == DSA_BF16 && !shares_keys(rows, idx_dtype) && onelaunch_shape(R, L, idx_dtype, topk))
-    return status_of(dsa::launch_decode_onelaunch(
-        to_host(rows), paged, idx_dtype == DSA_FP8_E4M3, q_idx, q_idx_scale, k_idx, k_idx_scale, w,
-        logits, ld_logits, topk, idx, softmax_scale, q, kv, out, lse, ws,
-        static_cast<hipStream_t>(stream)));
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   void *tk_ws = tk_bytes ? wsb : nullptr;
   void *ml_ws = need > tk_bytes ? wsb + tk_bytes : nullptr;
-  st = indexer_topk_common(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
-                           k_idx_scale, w, logits, ld_logits, topk, idx, tk_ws, tk_bytes, stream);
-  if (st != DSA_OK) return st;
-  return mla_common(rows, paged, MlaMode::kDecode, dtype, n_heads, d_qk, d_v, softmax_scale, q, kv,
-                    idx, topk, out, lse, ml_ws, need - tk_bytes, stream);
+  const size_t ml_bytes = need - tk_bytes;
+  if (!decode_fusable(rows, idx_dtype, dtype)) {
+    st = indexer_topk_common(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
+                             k_idx_scale, w, logits, ld_logits, topk, idx, tk_ws, tk_bytes, stream);
+    if (st != DSA_OK) return st;
+    return mla_common(rows, paged, MlaMode::kDecode, dtype, n_heads, d_qk, d_v, softmax_scale, q,
+                      kv, idx, topk, out, lse, ml_ws, ml_bytes, stream);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nh = fused_hist_lists(rows, idx_dtype);
+  const dsa::TopkHistDest dest = dsa::topk_hist_dest(tk_ws, R, L, nh);
+  hipError_t e = dsa::launch_indexer_mfma_hist(to_host(rows), paged, idx_dtype == DSA_FP8_E4M3,
+                                               q_idx, q_idx_scale, k_idx, k_idx_scale, w, logits,
+                                               ld_logits, dest, s);
+  if (e == hipSuccess)
+    e = dsa::launch_topk_filter_after_hist(logits, ld_logits, rows->row_len, R, L, topk, idx,
+                                           tk_ws, nh, s);
+  if (e == hipSuccess)
+    e = dsa::launch_mla_bf16_select(to_host(rows), paged, n_heads, softmax_scale, q, kv, idx, topk,
+                                    out, lse, dsa::mla_num_splits(R, n_heads, topk), ml_ws,
+                                    logits, ld_logits, tk_ws, nh, s);
+  return status_of(e);
 }
 
 constexpr int kMhaMaxRowLen = 16384;   // the attended range's pages are staged in LDS

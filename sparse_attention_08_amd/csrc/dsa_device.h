@@ -113,10 +113,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// s_waitcnt immediate that waits for at most n outstanding vector-memory operations and
-// leaves the export and LDS/scalar counters unconstrained (gfx9 field layout).
-constexpr int vmcnt_only(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
-
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every vector
 // memory operation of the wave (vmcnt(0)), which would drain global->LDS loads that are
 // meant to stay in flight across the barrier; here only LDS operations (lgkmcnt) are

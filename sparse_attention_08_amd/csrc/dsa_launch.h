@@ -51,19 +51,36 @@ hipError_t launch_indexer_prefill(const RowsHost &rows, bool paged, const void *
                                   const float *w, float *logits, int64_t ld, hipStream_t stream);
 // Workgroups per row of the MFMA indexer grid for this batch shape.
 int indexer_blocks_per_row(int num_rows, int max_row_len, bool fp8);
-// The indexer whose workgroups also select each row's top-k (decode-shaped batches: at most
-// 256 rows of at most 1M positions): logits as launch_indexer_mfma, idx [R, topk] as the
-// top-k of them.  ws: indexer_sel_ws_bytes bytes whose leading arrival counters are zero
-// before the call and are left zero by it.
-bool indexer_sel_ok(int num_rows, int max_row_len, bool fp8);
-size_t indexer_sel_ws_bytes(int num_rows, int max_row_len, bool fp8, int topk);
-hipError_t launch_indexer_select(const RowsHost &rows, bool paged, bool fp8, const void *q,
-                                 const float *q_scale, const void *k, const float *k_scale,
-                                 const float *w, float *logits, int64_t ld, int topk,
-                                 int32_t *idx, void *ws, hipStream_t stream);
+// Same, also depositing each workgroup's leading-digit histogram of its scores (the
+// first stage of the few-row top-k), indexer_blocks_per_row lists per row.
+struct TopkHistDest;
+hipError_t launch_indexer_mfma_hist(const RowsHost &rows, bool paged, bool fp8, const void *q,
+                                    const float *q_scale, const void *k, const float *k_scale,
+                                    const float *w, float *logits, int64_t ld,
+                                    const TopkHistDest &hist, hipStream_t stream);
 
 // ---- top-k ----
+// Where a producer of scores deposits per-workgroup compressed histograms of the 12-bit
+// leading digit of the order keys (list j of row r: count at hcnt[r*stride + j], entries
+// (digit << 16 | count) at hlist[(r*stride + j) * 4096 ...]).
+struct TopkHistDest {
+  uint32_t *hcnt;
+  uint32_t *hlist;
+  int stride;
+};
 size_t topk_workspace_bytes(int num_rows, int max_row_len, int k);
+// few long rows whose leading-digit histograms come from the score producer
+bool topk_hist_fusable(int num_rows, int max_row_len, int hist_lists);
+size_t topk_fused_workspace_bytes(int num_rows, int max_row_len, int hist_lists);
+TopkHistDest topk_hist_dest(void *ws, int num_rows, int max_row_len, int hist_lists);
+hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                  int num_rows, int max_row_len, int k, int32_t *idx, void *ws,
+                                  int hist_lists, hipStream_t stream);
+// Only the chunk filter of the above: its survivors are left in ws for the attention kernel
+// that finishes the selection (launch_mla_bf16_select); rows with row_len <= k are written.
+hipError_t launch_topk_filter_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                         int num_rows, int max_row_len, int k, int32_t *idx,
+                                         void *ws, int hist_lists, hipStream_t stream);
 hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,
                        int max_row_len, int k, int32_t *idx, void *ws, hipStream_t stream);
 
@@ -77,19 +94,12 @@ hipError_t launch_mla_f32(const RowsHost &rows, bool paged, int H, int Dqk, int 
 hipError_t launch_mla_bf16(const RowsHost &rows, bool paged, int H, float scale, const void *q,
                            const void *kv, const int32_t *idx, int k, void *out, float *lse,
                            int splits, void *ws, hipStream_t stream);
-
-// ---- the whole decode step in one launch (decode.hip) ----
-// Indexer (bf16 or fp8 keys), top-k and bf16 sparse MLA (128 heads, 576 / 512) of a
-// decode-shaped batch (at most 256 rows of at most 1M positions): logits, idx, out and lse as
-// the separate calls give them.  ws: decode_onelaunch_ws_bytes bytes whose leading counters
-// are zero before the call and are left zero by it.
-bool decode_onelaunch_ok(int num_rows, int max_row_len, bool fp8, int k);
-size_t decode_onelaunch_ws_bytes(int num_rows, int max_row_len, bool fp8, int k);
-hipError_t launch_decode_onelaunch(const RowsHost &rows, bool paged, bool fp8, const void *q_idx,
-                                   const float *q_scale, const void *k_idx, const float *k_scale,
-                                   const float *w, float *logits, int64_t ld, int topk,
-                                   int32_t *idx, float scale, const void *q, const void *kv,
-                                   void *out, float *lse, void *ws, hipStream_t stream);
+// Same, finishing each row's top-k from the survivors that launch_topk_filter_after_hist left
+// in topk_ws (hist_lists as given to it) and writing it to idx.
+hipError_t launch_mla_bf16_select(const RowsHost &rows, bool paged, int H, float scale,
+                                  const void *q, const void *kv, int32_t *idx, int k, void *out,
+                                  float *lse, int splits, void *ws, const float *logits,
+                                  int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream);
 
 // ---- masked MHA mode (short prefill) ----
 // Workspace: decompressed K_nope and V ([cache_rows, H, 128] bf16 each) and, with idx, the

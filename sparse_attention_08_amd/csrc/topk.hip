@@ -272,6 +272,41 @@ size_t topk_workspace_bytes(int num_rows, int max_row_len, int) {
   return mb_ws_bytes(num_rows, C);
 }
 
+bool topk_hist_fusable(int num_rows, int max_row_len, int hist_lists) {
+  return few_rows(num_rows, max_row_len) && hist_lists >= 1 && hist_lists <= kMaxChunks;
+}
+
+size_t topk_fused_workspace_bytes(int num_rows, int max_row_len, int hist_lists) {
+  const int C = (max_row_len + kChunk - 1) / kChunk;
+  return mb_ws_bytes(num_rows, C > hist_lists ? C : hist_lists);
+}
+
+TopkHistDest topk_hist_dest(void *ws, int num_rows, int max_row_len, int hist_lists) {
+  const int C = (max_row_len + kChunk - 1) / kChunk;
+  const MbWs w = carve_ws(ws, num_rows, C > hist_lists ? C : hist_lists);
+  return TopkHistDest{w.hcnt, w.hlist, w.C};
+}
+
+hipError_t launch_topk_filter_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                         int num_rows, int max_row_len, int k, int32_t *idx,
+                                         void *ws, int hist_lists, hipStream_t stream) {
+  const MbWs w = topk_chunk_ws(ws, num_rows, max_row_len, hist_lists);
+  dim3 grid((max_row_len + kChunk - 1) / kChunk, num_rows);
+  topk_filter_kernel<<<grid, kMbThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_after_hist(const float *logits, int64_t ld, const int32_t *row_len,
+                                  int num_rows, int max_row_len, int k, int32_t *idx, void *ws,
+                                  int hist_lists, hipStream_t stream) {
+  hipError_t e = launch_topk_filter_after_hist(logits, ld, row_len, num_rows, max_row_len, k, idx,
+                                               ws, hist_lists, stream);
+  if (e != hipSuccess) return e;
+  const MbWs w = topk_chunk_ws(ws, num_rows, max_row_len, hist_lists);
+  topk_final_kernel<kFinalThreads><<<num_rows, kFinalThreads, 0, stream>>>(logits, ld, row_len, k, idx, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float *logits, int64_t ld, const int32_t *row_len, int num_rows,
                        int max_row_len, int k, int32_t *idx, void *ws, hipStream_t stream) {
   if (few_rows(num_rows, max_row_len)) {

@@ -78,13 +78,3 @@ def valid_logits(x: np.ndarray, lens, which):
 def sorted_sets(idx: np.ndarray) -> np.ndarray:
     return np.sort(idx, axis=-1)
 
-
-def selects_in_indexer(wl) -> bool:
-    """Whether the library routes this batch's top-k into the indexer launch (the one-row
-    indexer on a decode-shaped batch): then the workspace starts with the per-row arrival
-    counters that every call leaves at zero.  Mirrors the routing rule of the C ABI."""
-    R, B, L = wl.num_rows, wl.num_seqs, wl.max_row_len
-    if wl.idx_dtype not in ("bf16", "fp8") or R > 256 or L > (1 << 20):
-        return False
-    shares_keys = wl.idx_dtype == "bf16" and (R >= 8 * B or (R >= 4 * B and L <= 32768))
-    return not shares_keys
