@@ -53,6 +53,8 @@ extern "C" {
 #define DSA_ABI_VERSION 1
 #define DSA_PAGE_SIZE 64     /* tokens per cache page in the paged layout */
 #define DSA_MAX_TOPK 2048    /* largest supported k (index_topk of the model) */
+/* scratch of dsa_sparse_attention_decode_noalloc, held per GPU for the process's lifetime */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum {
     DSA_OK = 0,
@@ -220,6 +222,25 @@ int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int i
                                       float softmax_scale, const void *q, const void *kv,
                                       void *out, float *lse, void *ws, size_t ws_bytes,
                                       void *stream);
+
+/* dsa_sparse_attention_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same call
+ * on the contiguous layout, with the same results bit for bit, but without a workspace
+ * argument.  Its scratch is a static device array of DSA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; the call allocates nothing
+ * (its first call on a device looks the array's address up).  Every call on one GPU uses
+ * that GPU's one array, so calls that overlap on a GPU (other streams, other host threads)
+ * race and must be serialised by the caller.  The scratch needs no initialisation.
+ * Errors: those of dsa_sparse_attention_decode, and DSA_ERR_WORKSPACE when
+ * dsa_sparse_attention_decode_workspace_size of the batch exceeds DSA_NOALLOC_SCRATCH_BYTES
+ * (nothing is enqueued then). */
+int dsa_sparse_attention_decode_noalloc(const dsa_rows *rows, int idx_dtype, int idx_heads,
+                                        int idx_dim, const void *q_idx, const float *q_idx_scale,
+                                        const void *k_idx, const float *k_idx_scale,
+                                        const float *w, float *logits, int64_t ld_logits, int topk,
+                                        int32_t *idx, int dtype, int n_heads, int d_qk, int d_v,
+                                        float softmax_scale, const void *q, const void *kv,
+                                        void *out, float *lse, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Masked MHA mode for short prefill ("DeepSeek-V3.2 技术报告摘要", section 1, "短序列优化":

@@ -83,6 +83,10 @@ def load_library() -> ctypes.CDLL:
         f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                       i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
         f.restype = i32
+    lib.dsa_sparse_attention_decode_noalloc.argtypes = [
+        rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i32, vp,
+        i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp]
+    lib.dsa_sparse_attention_decode_noalloc.restype = i32
     lib.dsa_prep_cache_write.argtypes = [i32, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.dsa_prep_cache_write.restype = i32
     lib.dsa_prep_queries.argtypes = [i32, vp, vp, i32, i32, vp, vp, vp, i32, vp, vp]
@@ -404,13 +408,17 @@ def sparse_attention_decode_workspace_size(num_rows: int, max_row_len: int, idx_
 
 def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, kv, scale: float,
                             d_v: int, idx=None, out=None, lse=None, q_scale=None, k_scale=None,
-                            ws=None):
+                            ws=None, noalloc: bool = False):
     """Indexer scores, their top-k and the sparse MLA over it, in one call (decode).
 
     Fills ``logits`` and ``idx`` as :func:`indexer_topk` and returns ``out`` as
     :func:`sparse_mla_decode` (``_paged`` for a paged ``rows``) would on that ``idx``.
+    ``noalloc``: call dsa_sparse_attention_decode_noalloc (contiguous rows, no ``ws``), whose
+    scratch is the library's static per-GPU array.
     """
     lib = load_library()
+    if noalloc and (rows.paged or ws is not None):
+        raise ValueError("noalloc takes contiguous rows and no workspace")
     for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (kv, "kv")):
         _dev(t, n)
     _dev(w, "w", (torch.float32,))
@@ -437,10 +445,18 @@ def sparse_attention_decode(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, k
     if lse is not None:
         _dev(lse, "lse", (torch.float32,))
         _shape(lse, "lse", (R, H))
+    st = rows.struct()
+    if noalloc:
+        s = lib.dsa_sparse_attention_decode_noalloc(
+            ctypes.byref(st), dtype_code(q_idx), int(q_idx.shape[1]), int(q_idx.shape[2]),
+            _ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), _ptr(logits),
+            int(logits.shape[-1]), int(topk), _ptr(idx), dtype_code(q), H, Dqk, int(d_v),
+            float(scale), _ptr(q), _ptr(kv), _ptr(out), _ptr(lse), _stream())
+        _check(s, "dsa_sparse_attention_decode_noalloc")
+        return out
     need = sparse_attention_decode_workspace_size(R, rows.max_row_len, dtype_code(q_idx), topk, H, d_v)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = rows.struct()
     name = "dsa_sparse_attention_decode_paged" if rows.paged else "dsa_sparse_attention_decode"
     s = getattr(lib, name)(
         ctypes.byref(st), dtype_code(q_idx), int(q_idx.shape[1]), int(q_idx.shape[2]), _ptr(q_idx),

@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "dsa_launch.h"
 
@@ -403,6 +404,56 @@ int dsa_sparse_attention_decode(const dsa_rows *rows, int idx_dtype, int idx_hea
                                  k_idx, k_idx_scale, w, logits, ld_logits, topk, idx, dtype,
                                  n_heads, d_qk, d_v, softmax_scale, q, kv, out, lse, ws, ws_bytes,
                                  stream);
+}
+
+// ---- the decode call without a workspace argument --------------------------------
+// Its scratch is this file-scope device array: every GPU the library runs on holds one copy
+// from the library's load until the process ends.  Host code never uses the array's name as
+// an address (on the host it only names the symbol): the device address is looked up once
+// per device, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];   // device address of `scratch` per device (null: not yet)
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
+int dsa_sparse_attention_decode_noalloc(const dsa_rows *rows, int idx_dtype, int idx_heads,
+                                        int idx_dim, const void *q_idx, const float *q_idx_scale,
+                                        const void *k_idx, const float *k_idx_scale,
+                                        const float *w, float *logits, int64_t ld_logits, int topk,
+                                        int32_t *idx, int dtype, int n_heads, int d_qk, int d_v,
+                                        float softmax_scale, const void *q, const void *kv,
+                                        void *out, float *lse, void *stream) {
+  if (!rows) return DSA_ERR_INVALID_ARG;
+  if (rows->num_rows > 0 &&
+      dsa_sparse_attention_decode_workspace_size(rows->num_rows, rows->max_row_len, idx_dtype, topk,
+                                                 n_heads, d_v) > DSA_NOALLOC_SCRATCH_BYTES)
+    return DSA_ERR_WORKSPACE;   // the batch needs more scratch than the static array holds
+  void *ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != DSA_OK) return st;
+  return attention_decode_common(rows, false, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale,
+                                 k_idx, k_idx_scale, w, logits, ld_logits, topk, idx, dtype,
+                                 n_heads, d_qk, d_v, softmax_scale, q, kv, out, lse, ws,
+                                 DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int dsa_sparse_attention_decode_paged(const dsa_rows *rows, int idx_dtype, int idx_heads,

@@ -251,3 +251,17 @@ def test_mha_validation(lib):
     assert call(r) == WORKSPACE and call(r, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
     assert lib.dsa_prefill_dense_mode(2048, 2048) == 1 and lib.dsa_prefill_dense_mode(2049, 2048) == 0
     assert lib.dsa_prefill_dense_mode(0, 2048) == 0
+
+
+def test_noalloc_decode_rejects_batches_beyond_its_scratch(lib):
+    # 64 rows of 1M scores need far more than the static scratch: refused before any HIP call
+    rows = _rows(num_rows=64, num_seqs=64, max_row_len=1 << 20)
+    need = lib.dsa_sparse_attention_decode_workspace_size(64, 1 << 20, 2, 2048, 128, 512)
+    assert need > (64 << 20)
+    s = lib.dsa_sparse_attention_decode_noalloc(
+        ctypes.byref(rows), 2, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 2048, FAKE,
+        1, 128, 576, 512, 0.1, FAKE, FAKE, FAKE, None, None)
+    assert s == WORKSPACE
+    assert lib.dsa_sparse_attention_decode_noalloc(None, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                   FAKE, 100, 64, FAKE, 1, 128, 576, 512, 0.1,
+                                                   FAKE, FAKE, FAKE, None, None) == INVALID
