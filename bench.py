@@ -12,7 +12,10 @@ bracket the step.  For decode the timed step is one dsa_sparse_attention_decode 
 call; the step is captured once in a HIP graph and replayed (--no-graph: eager launches;
 --separate: the indexer, the top-k and the attention as three calls).  An eager pass with
 events between separate stage calls gives the per-stage attribution and the indexer's
-roofline.  value = rows (tokens) / mean step time.
+roofline.  value = rows (tokens) / mean step time.  roofline.path_frac is the metric's own
+fraction: the whole path's algorithmic bytes (indexer inputs and keys, gathered latent
+entries, queries and outputs) over the step time, against 8 TB/s.  A decode run also times
+the 16K-token prefill workload (key prefill_c3: step time and bf16 MFMA fraction).
 
 Prints ONE JSON line.  --config selects another of the five workloads for diagnostics.
 """
@@ -57,6 +60,8 @@ def parse():
     p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the 16K-token prefill leg that a decode run also times")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows in the oracle sample")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
@@ -322,8 +327,86 @@ def mha_bench(args):
         "speedup_vs_mqa_path": ms_mqa / ms_mha}))
 
 
-def cpu_baseline(wl_host, n_rows: int):
-    """The fp64 oracle (as it stands) on the first n_rows rows of the same batch."""
+def host_cpu():
+    """The host's CPU model and core counts (logical CPUs, and those this process may use)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def prefill_leg(steps: int = 3, warmup: int = 1):
+    """The 16K-token causal prefill (one sequence, indexer + top-k call, then the sparse MLA
+    prefill call), eager, 1 GiB cache flush before each step; bf16 MFMA fraction of the
+    algorithmic flops (indexer scores + attention over each row's selected entries)."""
+    import torch
+
+    import sparse_attention_08_amd as dsa
+    import workloads
+    wl = workloads.config(3, device="cuda")
+    rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, seq_start=wl.seq_start,
+                    page_table=wl.page_table)
+    R = wl.num_rows
+    logits = torch.empty((R, wl.max_row_len), dtype=torch.float32, device="cuda")
+    idx = torch.empty((R, wl.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((R, wl.H, wl.D_v), dtype=wl.q.dtype, device="cuda")
+    lse = torch.empty((R, wl.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(dsa.indexer_topk_workspace_size(R, wl.max_row_len, wl.q_idx.dtype,
+                                                         wl.topk), 1), dtype=torch.uint8,
+                     device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, idx=idx,
+                         q_scale=wl.q_scale, k_scale=wl.k_scale, ws=ws)
+        if ev:
+            ev[1].record()
+        dsa.sparse_mla_prefill(rows, wl.q, wl.kv, idx, wl.scale, wl.D_v, out=out, lse=lse)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        flush.sum()
+        step(ev)
+    torch.cuda.synchronize()
+    ms = statistics.fmean(e[0].elapsed_time(e[2]) for e in evs)
+    idx_ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
+    mla_ms = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs)
+    lens = wl.row_len.cpu().tolist()
+    idx_f, mla_f = algorithmic_flops(wl, lens)
+    tflops = (idx_f + mla_f) / (ms * 1e-3) / 1e12
+    res = {"workload": wl.name, "ms_per_step": ms, "tokens_per_s": R / (ms * 1e-3),
+           "algorithmic_tflop_per_step": (idx_f + mla_f) / 1e12, "tflops": tflops,
+           "mfma_frac": tflops / BF16_PEAK_TFLOPS, "peak_tflops": BF16_PEAK_TFLOPS,
+           "indexer_topk_ms": idx_ms, "sparse_mla_ms": mla_ms,
+           "sparse_mla_mfma_frac": mla_f / (mla_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+           "steps": steps, "warmup": warmup, "launch_mode": "eager",
+           "cache_flushed_between_steps": True}
+    del logits, idx, out, lse, ws, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl_host, n_rows: int, gpu_idx=None):
+    """The fp64 oracle (as it stands) on the first n_rows rows of the same batch, on up to 16
+    threads, and one row on one thread.  With gpu_idx (the timed step's selection, [R, k]
+    host array) also the selection recall on those rows: the share of the oracle's top-k (on
+    its fp64 scores) that the GPU selection holds."""
     import numpy as np
 
     import oracle
@@ -337,9 +420,9 @@ def cpu_baseline(wl_host, n_rows: int):
     q_i, k_i, w = raw(wl_host.q_idx), raw(wl_host.k_idx), raw(wl_host.w)
     q_s, k_s = raw(wl_host.q_scale), raw(wl_host.k_scale)
     q, kv = raw(wl_host.q), raw(wl_host.kv)
-    lens = h["row_len"][which]
 
-    def one_pass():
+    def one_pass(which=which, threads=threads):
+        lens = h["row_len"][which]
         scores = oracle.indexer(wl_host.idx_dtype, q_i, w, k_i, rows, q_scale=q_s, k_scale=k_s,
                                 which=which, n_threads=threads)
         sel = oracle.topk(np.nan_to_num(scores, nan=0.0), lens, wl_host.topk, n_threads=threads)
@@ -347,20 +430,38 @@ def cpu_baseline(wl_host, n_rows: int):
         full_idx[which] = sel
         oracle.sparse_mla(wl_host.mla_dtype, q, kv, full_idx, rows, wl_host.scale, wl_host.D_v,
                           which=which, n_threads=threads)
+        return sel
+
+    # one row on one thread (the per-core rate)
+    t1 = time.perf_counter()
+    one_pass(which=[0], threads=1)
+    single = time.perf_counter() - t1
 
     # passes over the sample until about 12 core-seconds of oracle work (at most 20 passes)
     t0 = time.perf_counter()
     passes = 0
     while True:
-        one_pass()
+        sel = one_pass()
         passes += 1
         dt = time.perf_counter() - t0
         if dt * threads >= 12.0 or passes >= 20:
             break
-    return {"value": n_rows * passes / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_rows} of {wl_host.num_rows} decode rows of the same workload "
-                      f"(full context each), indexer + top-k + sparse MLA in fp64, {passes} "
-                      f"passes, {dt:.2f} s wall on {threads} threads"}
+    res = {"value": n_rows * passes / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_rows} of {wl_host.num_rows} decode rows of the same workload "
+                     f"(full context each), indexer + top-k + sparse MLA in fp64, {passes} "
+                     f"passes, {dt:.2f} s wall on {threads} threads",
+           "one_thread": {"value": 1.0 / single, "unit": "tokens/s",
+                          "sample": f"row 0 alone on 1 thread, {single:.2f} s"}}
+    res.update(host_cpu())
+    if gpu_idx is not None:
+        rec = []
+        for i, r in enumerate(which):
+            kk = min(wl_host.topk, int(h["row_len"][r]))
+            rec.append(len(set(gpu_idx[r, :kk].tolist()) & set(sel[i, :kk].tolist())) / kk)
+        res["selection_recall"] = {"rows": len(rec), "min": min(rec),
+                                   "mean": sum(rec) / len(rec),
+                                   "reference": "oracle top-k on its own fp64 scores"}
+    return res
 
 
 def main():
@@ -531,10 +632,17 @@ def main():
         roof["kernel"] = "whole path (indexer + top-k + sparse MLA), algorithmic flops"
     else:
         achieved = idx_b / (idx_mean * 1e-3) / 1e9
+        path_gbs = (idx_b + mla_b) / (mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic("indexer_mfma_kernel", args.config),
                 "kernel": "indexer_mfma_kernel",
-                "algorithmic_bytes_per_launch": idx_b}
+                "kernel_timed": "the scores-only launch (dsa_indexer_logits, event-bracketed "
+                                "eager call); the one-call decode step runs the instantiation "
+                                "that also builds the top-k's first-digit histograms",
+                "algorithmic_bytes_per_launch": idx_b,
+                # the metric itself: indexer + top-k + sparse-MLA bytes over the whole step
+                "path_achieved": path_gbs, "path_frac": path_gbs / HBM_PEAK_GBS,
+                "path_algorithmic_bytes": idx_b + mla_b}
     res = {
         "metric": METRIC,
         "value": R / (mean * 1e-3),
@@ -554,7 +662,10 @@ def main():
                    "cache_flushed_between_steps": flush is not None},
         "roofline": roof,
         "path": {"algorithmic_bytes_per_step": idx_b + mla_b,
-                 "hbm_frac_of_step": (idx_b + mla_b) / (mean * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 # prefill gathers its selected rows from L2 / Infinity Cache far more than
+                 # from HBM: there the ratio is bytes moved, not an HBM fraction
+                 ("gathered_bytes_over_hbm_peak" if prefill else "hbm_frac_of_step"):
+                     (idx_b + mla_b) / (mean * 1e-3) / (HBM_PEAK_GBS * 1e9),
                  "algorithmic_flops_per_step": idx_f + mla_f,
                  "launch_mode": mode,
                  "calls": ("indexer, top-k, attention" if args.separate else
@@ -568,13 +679,16 @@ def main():
                  "wall_s_timed_loop_incl_flushes": t_wall},
         "cpu_baseline": None,
     }
+    # the timed step's buffers and graph are released before the other legs
+    run = graph = None
+    del logits, out, lse, flush, run, graph
+    torch.cuda.empty_cache()
+    if not prefill and not args.no_prefill:
+        res["prefill_c3"] = prefill_leg()
     if not args.no_cpu:
-        del logits, out, lse, flush, run
-        if not args.no_graph:
-            del graph
-        torch.cuda.empty_cache()
         n_cpu = args.cpu_rows or min(R, 8)
-        res["cpu_baseline"] = cpu_baseline(wl, n_cpu)
+        res["cpu_baseline"] = cpu_baseline(wl, n_cpu, gpu_idx=idx.cpu().numpy())
+        res["selection_recall"] = res["cpu_baseline"].pop("selection_recall", None)
     print(json.dumps(res))
 
 

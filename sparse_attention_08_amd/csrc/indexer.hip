@@ -57,6 +57,13 @@ hipError_t launch_indexer_f32(const RowsHost &rh, bool paged, int H, int D, cons
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
   dim3 grid((rh.max_row_len + 255) / 256, rh.num_rows);
   size_t shm = sizeof(float) * ((size_t)H * D + H);
+  // the query block and weights of the largest supported shape (64 heads x 256 dims: 65,792
+  // bytes) exceed the default 64 KB of dynamic LDS
+  constexpr int kMaxShm = (int)sizeof(float) * (64 * 256 + 64);
+  static std::atomic<uint64_t> lds_set[2];
+  hipError_t e = paged ? ensure_dynamic_lds(&indexer_f32_kernel<true>, kMaxShm, lds_set[1])
+                       : ensure_dynamic_lds(&indexer_f32_kernel<false>, kMaxShm, lds_set[0]);
+  if (e != hipSuccess) return e;
   if (paged)
     indexer_f32_kernel<true><<<grid, 256, shm, stream>>>(rows, H, D, q, k, w, logits, ld);
   else
