@@ -252,37 +252,32 @@ def prep_bench(args):
 
 
 def mha_bench(args):
-    """One JSON line: the short-prefill MHA mode (dsa_mha_prefill, dense causal: latent
-    decompression + attention) on one L-token sequence, and the DSA path in MQA mode
-    (dsa_indexer_topk + dsa_sparse_mla_prefill) on a prefill of the same length, each captured
-    in a HIP graph and replayed after a cache flush."""
+    """One JSON line: the prefill dispatch (dsa_sparse_attention_prefill) on one L-token
+    sequence in its two forms on the same inputs: the masked-MHA mode (dense_threshold = L:
+    latent decompression of the reached positions + dense causal MHA when L <= 2048, else
+    indexer + top-k + masked MHA) and the MQA path (dense_threshold = 0: indexer + top-k,
+    query absorption, sparse MLA, output projection), each captured in a HIP graph and
+    replayed after a cache flush."""
     import torch
 
     import sparse_attention_08_amd as dsa
     import workloads
 
     L = int(args.mha)
-    mb = workloads.mha_batch([L], seed=1000 + L, device="cuda")
+    mb = workloads.mha_batch([L], H_I=64, seed=1000 + L, device="cuda")
     wl = mb.wl
     rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, seq_start=wl.seq_start)
-    H = int(mb.q.shape[1])
+    H, k = int(mb.q.shape[1]), wl.topk
     out = torch.empty((L, H, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(dsa.mha_prefill_workspace_size(wl.kv.shape[0], H, L, L, False),
-                     dtype=torch.uint8, device="cuda")
-    w2 = workloads.prefill(L, seed=1000 + L, device="cuda")
-    rows2 = dsa.Rows(w2.row_seq, w2.row_len, w2.max_row_len, w2.num_seqs, seq_start=w2.seq_start)
     logits = torch.empty((L, L), dtype=torch.float32, device="cuda")
-    idx = torch.empty((L, w2.topk), dtype=torch.int32, device="cuda")
-    o2 = torch.empty((L, w2.H, w2.D_v), dtype=torch.bfloat16, device="cuda")
-    tk_ws = torch.empty(max(dsa.indexer_topk_workspace_size(L, L, w2.q_idx.dtype, w2.topk), 1),
-                        dtype=torch.uint8, device="cuda")
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    ws = {t: torch.empty(max(dsa.sparse_attention_prefill_workspace_size(
+        L, 1, L, wl.q_idx.dtype, k, H, t), 1), dtype=torch.uint8, device="cuda") for t in (0, L)}
 
-    def mha():
-        dsa.mha_prefill(rows, mb.q, wl.kv, mb.w_uk, mb.w_uv, mb.scale, out=out, ws=ws)
-
-    def mqa():
-        dsa.indexer_topk(rows2, w2.q_idx, w2.w, w2.k_idx, logits, w2.topk, idx=idx, ws=tk_ws)
-        dsa.sparse_mla_prefill(rows2, w2.q, w2.kv, idx, w2.scale, w2.D_v, out=o2)
+    def run(threshold):
+        return lambda: dsa.sparse_attention_prefill(
+            rows, wl.q_idx, wl.w, wl.k_idx, logits, k, mb.q, wl.kv, mb.w_uk, mb.w_uv, mb.scale,
+            threshold, idx=idx, out=out, ws=ws[threshold])
 
     flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
@@ -306,24 +301,26 @@ def mha_bench(args):
         torch.cuda.synchronize()
         return statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
 
-    ms_mha = timed(mha)
-    ms_mqa = timed(mqa)
+    ms_mha = timed(run(L))
+    ms_mqa = timed(run(0))
     pairs = L * (L + 1) // 2
+    sel_pairs = sum(min(t + 1, k) for t in range(L))
     dec_flops = 2 * L * 512 * H * 128 * 2
-    att_flops = pairs * H * (192 + 128) * 2
-    mqa_flops = sum(min(t + 1, w2.topk) for t in range(L)) * w2.H * (w2.D_qk + w2.D_v) * 2
+    att_flops = (pairs if L <= k else sel_pairs) * H * (192 + 128) * 2
+    mqa_flops = sel_pairs * H * (576 + 512) * 2 + 2 * L * H * 128 * 512 * 2
     achieved = (dec_flops + att_flops) / (ms_mha * 1e-3) / 1e12
     print(json.dumps({
         "metric": "short-prefill masked-MHA mode time per step", "value": ms_mha * 1e3,
         "unit": "us", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
         "dtype": "bf16", "data": "synthetic", "launch_mode": "hip_graph",
-        "config": {"workload": f"prefill of {L} tokens, dense causal", "heads": H,
+        "config": {"workload": f"prefill of {L} tokens, one sequence, top-{k}", "heads": H,
                    "cache_flushed_between_steps": flush is not None},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
                      "flops": {"decompression": dec_flops, "attention": att_flops}},
-        "mqa_path": {"us": ms_mqa * 1e3, "calls": "indexer+top-k, sparse MLA prefill",
-                     "attention_flops": mqa_flops},
+        "mqa_path": {"us": ms_mqa * 1e3,
+                     "calls": "indexer+top-k, query absorption, sparse MLA, output projection",
+                     "attention_and_projection_flops": mqa_flops},
         "speedup_vs_mqa_path": ms_mqa / ms_mha}))
 
 

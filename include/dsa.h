@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 #define DSA_PAGE_SIZE 64     /* tokens per cache page in the paged layout */
 #define DSA_MAX_TOPK 2048    /* largest supported k (index_topk of the model) */
 /* scratch of dsa_sparse_attention_decode_noalloc, held per GPU for the process's lifetime */
@@ -246,36 +246,75 @@ int dsa_sparse_attention_decode_noalloc(const dsa_rows *rows, int idx_dtype, int
  * Masked MHA mode for short prefill ("DeepSeek-V3.2 技术报告摘要", section 1, "短序列优化":
  * short prefill runs DSA as masked MHA; "DeepSeek-V3.2 -- Model techniques map",
  * "Multi-head latent attention": 128 nope + 64 rope query/key dims, 128 value dims per head).
- * Every latent cache row n ([c_n (512) | kr_n (64)], the layout of the MLA calls) is first
- * decompressed per head h: K[n,h] = [W_UK[h] c_n | kr_n] (192 dims), V[n,h] = W_UV[h] c_n
- * (128 dims), rounded to bf16.  Row r, head h then attends over the set of its valid idx
+ * The latent entries the batch reaches ([c (512) | kr (64)], the layout of the MLA calls: for
+ * each sequence, its positions below the longest row_len of its rows) are first decompressed
+ * per head h: K[s,h] = [W_UK[h] c_s | kr_s] (192 dims), V[s,h] = W_UV[h] c_s (128 dims), rounded
+ * to bf16; no other cache row is read.  Row r, head h then attends over the set of its valid idx
  * entries (idx [R, k] int32), or, with idx = NULL, over every position below row_len[r]
  * (dense causal: what the top-k selects when the row has at most k positions):
  *   z_s = softmax_scale * q[r,h,:] . K[row(s),h,:];  out[r,h,:] = softmax(z) . V;
  *   lse[r,h] = ln sum_s exp(z_s) (-inf for an empty set; lse may be NULL).
- * q: [R, n_heads, 192] bf16 (nope 128 | rope 64); kv: [num_cache_rows, 576] bf16 (contiguous
- * [N, 576] or paged [P, 64, 576], num_cache_rows = N or 64 P); w_uk, w_uv: [n_heads, 128, 512]
- * bf16 (row d of head h is the 512-vector producing key / value dim d); out: [R, n_heads,
- * 128] bf16.  ws: device scratch of dsa_mha_prefill_workspace_size(num_cache_rows, n_heads,
- * R, max_row_len, idx != NULL) bytes (the decompressed keys and values, 2 x 256 B per cache
- * row and head, and the top-k masks); calls sharing a workspace must not run concurrently.
+ * q: [R, n_heads, 192] bf16 (nope 128 | rope 64); kv: the latent cache, bf16 (contiguous
+ * [N, 576] or paged [P, 64, 576]); w_uk, w_uv: [n_heads, 128, 512] bf16 (row d of head h is
+ * the 512-vector producing key / value dim d); out: [R, n_heads, 128] bf16.  ws: device
+ * scratch of dsa_mha_prefill_workspace_size(num_seqs, n_heads, R, max_row_len, idx != NULL)
+ * bytes (the decompressed keys and values, 2 x 256 B per head for max_row_len positions of
+ * each sequence, and the top-k masks), independent of the cache's size; needs no
+ * initialisation; calls sharing a workspace must not run concurrently.
  * max_row_len <= 16384.  dsa_prefill_dense_mode(max_row_len, topk) is 1 when every row has
  * at most topk positions, i.e. when the dense mode (idx = NULL) equals DSA exactly.
  * Errors: DSA_ERR_INVALID_ARG for a bad row description, missing pointers, n_heads < 1,
- * num_cache_rows < 1, a non-finite or non-positive scale, k outside [1, 2048] with idx;
- * DSA_ERR_UNSUPPORTED for max_row_len > 16384; DSA_ERR_WORKSPACE for a missing or small ws;
- * DSA_ERR_HIP when the decompression GEMM (rocBLAS) or a launch fails. */
+ * a non-finite or non-positive scale, k outside [1, 2048] with idx; DSA_ERR_UNSUPPORTED for
+ * max_row_len > 16384; DSA_ERR_WORKSPACE for a missing or small ws; DSA_ERR_HIP when a
+ * launch fails. */
 int dsa_prefill_dense_mode(int max_row_len, int topk);
-size_t dsa_mha_prefill_workspace_size(int64_t num_cache_rows, int n_heads, int num_rows,
-                                      int max_row_len, int masked);
-int dsa_mha_prefill(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
-                    float softmax_scale, const void *q, const void *kv, const void *w_uk,
-                    const void *w_uv, const int32_t *idx, int k, void *out, float *lse, void *ws,
-                    size_t ws_bytes, void *stream);
-int dsa_mha_prefill_paged(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
-                          float softmax_scale, const void *q, const void *kv, const void *w_uk,
-                          const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
-                          void *ws, size_t ws_bytes, void *stream);
+size_t dsa_mha_prefill_workspace_size(int num_seqs, int n_heads, int num_rows, int max_row_len,
+                                      int masked);
+int dsa_mha_prefill(const dsa_rows *rows, int n_heads, float softmax_scale, const void *q,
+                    const void *kv, const void *w_uk, const void *w_uv, const int32_t *idx, int k,
+                    void *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+int dsa_mha_prefill_paged(const dsa_rows *rows, int n_heads, float softmax_scale, const void *q,
+                          const void *kv, const void *w_uk, const void *w_uv, const int32_t *idx,
+                          int k, void *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Prefill attention with the dispatch between its two forms ("DeepSeek-V3.2 技术报告摘要",
+ * section 1: MLA in MQA mode over the top-k entries, and "短序列优化": short prefill as
+ * masked MHA; the switch is the serving knob of "DeepSeek-V3.2" model docs, section 5.3,
+ * SGLANG_NSA_PREFILL_DENSE_ATTN_KV_LEN_THRESHOLD, which the pages set to 0 there).
+ * Inputs are those of dsa_indexer_topk(_paged) (idx_dtype .. topk, idx) and of
+ * dsa_mha_prefill(_paged) (n_heads, softmax_scale, q [R, H, 192], kv, w_uk, w_uv, out
+ * [R, H, 128], lse).  With max_row_len <= dense_threshold (and <= 16384) it runs the masked
+ * MHA mode: dense causal when max_row_len <= topk (DSA selects every position; the indexer
+ * does not run and logits / idx are not written), else over the top-k sets the indexer and
+ * top-k write to logits / idx.  Otherwise (dense_threshold 0: always) it runs the MQA path:
+ * indexer and top-k into logits / idx, the query absorbed through W_UK, q_abs[r,h] =
+ * [W_UK[h]^T q_nope (512) | q_rope (64)] (bf16), dsa_sparse_mla_prefill(_paged) over idx with
+ * d_qk 576 and d_v 512 (the latent, bf16), and out[r,h] = W_UV[h] o[r,h] (bf16); lse is the
+ * attention's.  The two forms agree up to their bf16 roundings.
+ * ws / ws_bytes: device scratch of dsa_sparse_attention_prefill_workspace_size(R, num_seqs,
+ * max_row_len, idx_dtype, topk, n_heads, dense_threshold) bytes; needs no initialisation.
+ * Errors: those of the calls it makes; DSA_ERR_UNSUPPORTED for the MQA path with
+ * n_heads != 128. */
+size_t dsa_sparse_attention_prefill_workspace_size(int num_rows, int num_seqs, int max_row_len,
+                                                   int idx_dtype, int topk, int n_heads,
+                                                   int dense_threshold);
+int dsa_sparse_attention_prefill(const dsa_rows *rows, int idx_dtype, int idx_heads, int idx_dim,
+                                 const void *q_idx, const float *q_idx_scale, const void *k_idx,
+                                 const float *k_idx_scale, const float *w, float *logits,
+                                 int64_t ld_logits, int topk, int32_t *idx, int n_heads,
+                                 float softmax_scale, const void *q, const void *kv,
+                                 const void *w_uk, const void *w_uv, void *out, float *lse,
+                                 int dense_threshold, void *ws, size_t ws_bytes, void *stream);
+int dsa_sparse_attention_prefill_paged(const dsa_rows *rows, int idx_dtype, int idx_heads,
+                                       int idx_dim, const void *q_idx, const float *q_idx_scale,
+                                       const void *k_idx, const float *k_idx_scale,
+                                       const float *w, float *logits, int64_t ld_logits, int topk,
+                                       int32_t *idx, int n_heads, float softmax_scale,
+                                       const void *q, const void *kv, const void *w_uk,
+                                       const void *w_uv, void *out, float *lse,
+                                       int dense_threshold, void *ws, size_t ws_bytes,
+                                       void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Indexer-input and cache-write prep: the step in front of the indexer for every new token

@@ -96,11 +96,18 @@ def load_library() -> ctypes.CDLL:
     lib.dsa_prep.restype = i32
     lib.dsa_prefill_dense_mode.argtypes = [i32, i32]
     lib.dsa_prefill_dense_mode.restype = i32
-    lib.dsa_mha_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    lib.dsa_mha_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.dsa_mha_prefill_workspace_size.restype = sz
     for name in ("dsa_mha_prefill", "dsa_mha_prefill_paged"):
         f = getattr(lib, name)
-        f.argtypes = [rows_p, i64, i32, ctypes.c_float, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        f.argtypes = [rows_p, i32, ctypes.c_float, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        f.restype = i32
+    lib.dsa_sparse_attention_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.dsa_sparse_attention_prefill_workspace_size.restype = sz
+    for name in ("dsa_sparse_attention_prefill", "dsa_sparse_attention_prefill_paged"):
+        f = getattr(lib, name)
+        f.argtypes = [rows_p, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32,
+                      ctypes.c_float, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         f.restype = i32
     _lib = lib
     return lib
@@ -562,10 +569,10 @@ def prefill_dense_mode(max_row_len: int, topk: int) -> bool:
     return bool(load_library().dsa_prefill_dense_mode(int(max_row_len), int(topk)))
 
 
-def mha_prefill_workspace_size(num_cache_rows: int, n_heads: int, num_rows: int,
-                               max_row_len: int, masked: bool) -> int:
+def mha_prefill_workspace_size(num_seqs: int, n_heads: int, num_rows: int, max_row_len: int,
+                               masked: bool) -> int:
     return int(load_library().dsa_mha_prefill_workspace_size(
-        int(num_cache_rows), int(n_heads), int(num_rows), int(max_row_len), int(bool(masked))))
+        int(num_seqs), int(n_heads), int(num_rows), int(max_row_len), int(bool(masked))))
 
 
 def mha_prefill(rows: Rows, q, kv, w_uk, w_uv, scale: float, idx=None, out=None, lse=None,
@@ -585,7 +592,6 @@ def mha_prefill(rows: Rows, q, kv, w_uk, w_uv, scale: float, idx=None, out=None,
     _latent_cache_shape(rows, kv, 576)
     if w_uk.shape != (H, 128, 512) or w_uv.shape != (H, 128, 512) or kv.shape[-1] != 576:
         raise ValueError("w_uk / w_uv must be [H, 128, 512] and kv rows 576 wide")
-    n_cache = kv.numel() // 576
     k = 0
     if idx is not None:
         _dev(idx, "idx", (torch.int32,))
@@ -598,13 +604,79 @@ def mha_prefill(rows: Rows, q, kv, w_uk, w_uv, scale: float, idx=None, out=None,
     if lse is not None:
         _dev(lse, "lse", (torch.float32,))
         _shape(lse, "lse", (R, H))
-    need = mha_prefill_workspace_size(n_cache, H, R, rows.max_row_len, idx is not None)
+    need = mha_prefill_workspace_size(rows.num_seqs, H, R, rows.max_row_len, idx is not None)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = rows.struct()
     name = "dsa_mha_prefill_paged" if rows.paged else "dsa_mha_prefill"
-    s = getattr(lib, name)(ctypes.byref(st), n_cache, H, float(scale), _ptr(q), _ptr(kv),
-                           _ptr(w_uk), _ptr(w_uv), _ptr(idx), k, _ptr(out), _ptr(lse), _ptr(ws),
+    s = getattr(lib, name)(ctypes.byref(st), H, float(scale), _ptr(q), _ptr(kv), _ptr(w_uk),
+                           _ptr(w_uv), _ptr(idx), k, _ptr(out), _ptr(lse), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream())
+    _check(s, name)
+    return out
+
+
+def sparse_attention_prefill_workspace_size(num_rows: int, num_seqs: int, max_row_len: int,
+                                            idx_dtype, topk: int, n_heads: int,
+                                            dense_threshold: int) -> int:
+    code = idx_dtype if isinstance(idx_dtype, int) else dtype_code(torch.empty(0, dtype=idx_dtype))
+    return int(load_library().dsa_sparse_attention_prefill_workspace_size(
+        int(num_rows), int(num_seqs), int(max_row_len), code, int(topk), int(n_heads),
+        int(dense_threshold)))
+
+
+def sparse_attention_prefill(rows: Rows, q_idx, w, k_idx, logits, topk: int, q, kv, w_uk, w_uv,
+                             scale: float, dense_threshold: int, idx=None, out=None, lse=None,
+                             q_scale=None, k_scale=None, ws=None):
+    """Prefill attention with the masked-MHA / MQA dispatch: q [R, H, 192] bf16 (nope | rope),
+    the latent cache ``kv`` and ``w_uk`` / ``w_uv`` [H, 128, 512]; the indexer inputs as for
+    :func:`indexer_topk`.  The masked MHA mode when ``rows.max_row_len <= dense_threshold``,
+    else the MQA path (query absorbed through W_UK, sparse MLA, output through W_UV).
+    Returns out [R, H, 128] bf16; ``logits`` / ``idx`` are written whenever the selection
+    runs (always, except the dense MHA mode of rows no longer than ``topk``)."""
+    lib = load_library()
+    for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx")):
+        _dev(t, n)
+    _dev(w, "w", (torch.float32,))
+    _dev(logits, "logits", (torch.float32,))
+    _dev(q, "q", (torch.bfloat16,))
+    _dev(kv, "kv", (torch.bfloat16,))
+    _dev(w_uk, "w_uk", (torch.bfloat16,))
+    _dev(w_uv, "w_uv", (torch.bfloat16,))
+    if q_scale is not None:
+        _dev(q_scale, "q_scale", (torch.float32,))
+    if k_scale is not None:
+        _dev(k_scale, "k_scale", (torch.float32,))
+    if q.dim() != 3 or q.shape[2] != 192 or q_idx.dim() != 3:
+        raise ValueError("q must be [R, H, 192] and q_idx [R, H_I, D_I]")
+    _indexer_shapes(rows, q_idx, w, k_idx, logits, q_scale, k_scale)
+    _rows_of(rows, q, "q")
+    R, H = int(q.shape[0]), int(q.shape[1])
+    _latent_cache_shape(rows, kv, 576)
+    if w_uk.shape != (H, 128, 512) or w_uv.shape != (H, 128, 512):
+        raise ValueError("w_uk / w_uv must be [H, 128, 512]")
+    if idx is None:
+        idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    _dev(idx, "idx", (torch.int32,))
+    _shape(idx, "idx", (R, topk))
+    if out is None:
+        out = torch.empty((R, H, 128), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", (torch.bfloat16,))
+    _shape(out, "out", (R, H, 128))
+    if lse is not None:
+        _dev(lse, "lse", (torch.float32,))
+        _shape(lse, "lse", (R, H))
+    need = sparse_attention_prefill_workspace_size(R, rows.num_seqs, rows.max_row_len,
+                                                   dtype_code(q_idx), topk, H, dense_threshold)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = rows.struct()
+    name = "dsa_sparse_attention_prefill_paged" if rows.paged else "dsa_sparse_attention_prefill"
+    s = getattr(lib, name)(
+        ctypes.byref(st), dtype_code(q_idx), int(q_idx.shape[1]), int(q_idx.shape[2]), _ptr(q_idx),
+        _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), _ptr(logits), int(logits.shape[-1]),
+        int(topk), _ptr(idx), H, float(scale), _ptr(q), _ptr(kv), _ptr(w_uk), _ptr(w_uv),
+        _ptr(out), _ptr(lse), int(dense_threshold), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream())
     _check(s, name)
     return out

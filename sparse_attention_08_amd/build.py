@@ -49,7 +49,7 @@ def build(verbose: bool = True) -> str:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
-           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+           "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     os.replace(tmp, LIB)
     if verbose:

@@ -245,23 +245,82 @@ int attention_decode_common(const dsa_rows *rows, bool paged, int idx_dtype, int
 
 constexpr int kMhaMaxRowLen = 16384;   // the attended range's pages are staged in LDS
 
-int mha_common(const dsa_rows *rows, bool paged, int64_t num_cache_rows, int n_heads,
-               float softmax_scale, const void *q, const void *kv, const void *w_uk,
-               const void *w_uv, const int32_t *idx, int k, void *out, float *lse, void *ws,
-               size_t ws_bytes, void *stream) {
+int mha_common(const dsa_rows *rows, bool paged, int n_heads, float softmax_scale, const void *q,
+               const void *kv, const void *w_uk, const void *w_uv, const int32_t *idx, int k,
+               void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
   if (!rows_ok(rows, paged)) return DSA_ERR_INVALID_ARG;
-  if (num_cache_rows < 1 || n_heads < 1) return DSA_ERR_INVALID_ARG;
+  if (n_heads < 1) return DSA_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DSA_ERR_INVALID_ARG;
   if (idx && (k < 1 || k > DSA_MAX_TOPK)) return DSA_ERR_INVALID_ARG;
   if (rows->num_rows == 0) return DSA_OK;
   if (!q || !kv || !w_uk || !w_uv || !out) return DSA_ERR_INVALID_ARG;
   if (rows->max_row_len > kMhaMaxRowLen) return DSA_ERR_UNSUPPORTED;
-  const size_t need = dsa::mha_workspace_bytes(num_cache_rows, n_heads, rows->num_rows,
+  const size_t need = dsa::mha_workspace_bytes(rows->num_seqs, n_heads, rows->num_rows,
                                                rows->max_row_len, idx != nullptr);
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
-  return status_of(dsa::launch_mha_prefill(to_host(rows), paged, num_cache_rows, n_heads,
-                                           softmax_scale, q, kv, w_uk, w_uv, idx, k, out, lse, ws,
+  return status_of(dsa::launch_mha_prefill(to_host(rows), paged, n_heads, softmax_scale, q, kv,
+                                           w_uk, w_uv, idx, k, out, lse, ws,
                                            static_cast<hipStream_t>(stream)));
+}
+
+// The prefill dispatch: the masked MHA mode when the batch's longest row reaches at most
+// dense_threshold positions (and the mode's 16384 limit), else the MQA path.  The MHA mode
+// needs the selection only for rows longer than topk.
+bool prefill_uses_mha(int max_row_len, int dense_threshold) {
+  return max_row_len <= dense_threshold && max_row_len <= kMhaMaxRowLen;
+}
+
+size_t prefill_ws(int R, int B, int L, int idx_dtype, int topk, int H, int dense_threshold) {
+  const bool mha = prefill_uses_mha(L, dense_threshold);
+  const size_t sel = (mha && L <= topk) ? 0 : align256(indexer_topk_ws(R, L, idx_dtype, topk));
+  return sel + (mha ? dsa::mha_workspace_bytes(B, H, R, L, L > topk)
+                    : dsa::absorb_workspace_bytes(R, H));
+}
+
+int prefill_common(const dsa_rows *rows, bool paged, int idx_dtype, int idx_heads, int idx_dim,
+                   const void *q_idx, const float *q_idx_scale, const void *k_idx,
+                   const float *k_idx_scale, const float *w, float *logits, int64_t ld_logits,
+                   int topk, int32_t *idx, int n_heads, float softmax_scale, const void *q,
+                   const void *kv, const void *w_uk, const void *w_uv, void *out, float *lse,
+                   int dense_threshold, void *ws, size_t ws_bytes, void *stream) {
+  if (!rows_ok(rows, paged)) return DSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > DSA_MAX_TOPK || n_heads < 1) return DSA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DSA_ERR_INVALID_ARG;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !kv || !w_uk || !w_uv || !out) return DSA_ERR_INVALID_ARG;
+  const int R = rows->num_rows, L = rows->max_row_len;
+  const bool mha = prefill_uses_mha(L, dense_threshold);
+  const bool select = !mha || L > topk;
+  if (select) {
+    const int st = indexer_check(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale,
+                                 k_idx, k_idx_scale, w, logits, ld_logits);
+    if (st != DSA_OK) return st;
+    if (!idx) return DSA_ERR_INVALID_ARG;
+  }
+  if (!mha && n_heads != 128) return DSA_ERR_UNSUPPORTED;   // the bf16 MQA attention's heads
+  const size_t need = prefill_ws(R, rows->num_seqs, L, idx_dtype, topk, n_heads, dense_threshold);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  const size_t sel_bytes = select ? align256(indexer_topk_ws(R, L, idx_dtype, topk)) : 0;
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  if (select) {
+    const int st = indexer_topk_common(rows, paged, idx_dtype, idx_heads, idx_dim, q_idx,
+                                       q_idx_scale, k_idx, k_idx_scale, w, logits, ld_logits,
+                                       topk, idx, sel_bytes ? wsb : nullptr, sel_bytes, stream);
+    if (st != DSA_OK) return st;
+  }
+  if (mha)
+    return mha_common(rows, paged, n_heads, softmax_scale, q, kv, w_uk, w_uv,
+                      select ? idx : nullptr, topk, out, lse, wsb + sel_bytes, need - sel_bytes,
+                      stream);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dsa::AbsorbBuffers ab = dsa::carve_absorb(wsb + sel_bytes, R, n_heads);
+  hipError_t e = dsa::launch_absorb_query(R, n_heads, q, w_uk, ab, s);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  const int st = mla_common(rows, paged, MlaMode::kPrefill, DSA_BF16, n_heads, 576, 512,
+                            softmax_scale, ab.q_abs, kv, idx, topk, ab.o_lat, lse, nullptr, 0,
+                            stream);
+  if (st != DSA_OK) return st;
+  return status_of(dsa::launch_expand_output(R, n_heads, ab.o_lat, w_uv, out, s));
 }
 
 int prep_keys_check(const dsa::PrepKeys &k, bool fp8) {
@@ -493,26 +552,60 @@ int dsa_prefill_dense_mode(int max_row_len, int topk) {
   return (max_row_len >= 1 && topk >= 1 && max_row_len <= topk) ? 1 : 0;
 }
 
-size_t dsa_mha_prefill_workspace_size(int64_t num_cache_rows, int n_heads, int num_rows,
-                                      int max_row_len, int masked) {
-  if (num_cache_rows < 1 || n_heads < 1 || num_rows < 0 || max_row_len < 1) return 0;
-  return dsa::mha_workspace_bytes(num_cache_rows, n_heads, num_rows, max_row_len, masked != 0);
+size_t dsa_mha_prefill_workspace_size(int num_seqs, int n_heads, int num_rows, int max_row_len,
+                                      int masked) {
+  if (num_seqs < 1 || n_heads < 1 || num_rows < 0 || max_row_len < 1) return 0;
+  return dsa::mha_workspace_bytes(num_seqs, n_heads, num_rows, max_row_len, masked != 0);
 }
 
-int dsa_mha_prefill(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
-                    float softmax_scale, const void *q, const void *kv, const void *w_uk,
-                    const void *w_uv, const int32_t *idx, int k, void *out, float *lse, void *ws,
-                    size_t ws_bytes, void *stream) {
-  return mha_common(rows, false, num_cache_rows, n_heads, softmax_scale, q, kv, w_uk, w_uv, idx,
-                    k, out, lse, ws, ws_bytes, stream);
+int dsa_mha_prefill(const dsa_rows *rows, int n_heads, float softmax_scale, const void *q,
+                    const void *kv, const void *w_uk, const void *w_uv, const int32_t *idx, int k,
+                    void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  return mha_common(rows, false, n_heads, softmax_scale, q, kv, w_uk, w_uv, idx, k, out, lse, ws,
+                    ws_bytes, stream);
 }
 
-int dsa_mha_prefill_paged(const dsa_rows *rows, int64_t num_cache_rows, int n_heads,
-                          float softmax_scale, const void *q, const void *kv, const void *w_uk,
-                          const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
-                          void *ws, size_t ws_bytes, void *stream) {
-  return mha_common(rows, true, num_cache_rows, n_heads, softmax_scale, q, kv, w_uk, w_uv, idx,
-                    k, out, lse, ws, ws_bytes, stream);
+int dsa_mha_prefill_paged(const dsa_rows *rows, int n_heads, float softmax_scale, const void *q,
+                          const void *kv, const void *w_uk, const void *w_uv, const int32_t *idx,
+                          int k, void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  return mha_common(rows, true, n_heads, softmax_scale, q, kv, w_uk, w_uv, idx, k, out, lse, ws,
+                    ws_bytes, stream);
+}
+
+size_t dsa_sparse_attention_prefill_workspace_size(int num_rows, int num_seqs, int max_row_len,
+                                                   int idx_dtype, int topk, int n_heads,
+                                                   int dense_threshold) {
+  if (num_rows < 0 || num_seqs < 1 || max_row_len < 1 || topk < 1 || topk > DSA_MAX_TOPK ||
+      n_heads < 1)
+    return 0;
+  if (idx_dtype != DSA_F32 && idx_dtype != DSA_BF16 && idx_dtype != DSA_FP8_E4M3) return 0;
+  return prefill_ws(num_rows, num_seqs, max_row_len, idx_dtype, topk, n_heads, dense_threshold);
+}
+
+int dsa_sparse_attention_prefill(const dsa_rows *rows, int idx_dtype, int idx_heads, int idx_dim,
+                                 const void *q_idx, const float *q_idx_scale, const void *k_idx,
+                                 const float *k_idx_scale, const float *w, float *logits,
+                                 int64_t ld_logits, int topk, int32_t *idx, int n_heads,
+                                 float softmax_scale, const void *q, const void *kv,
+                                 const void *w_uk, const void *w_uv, void *out, float *lse,
+                                 int dense_threshold, void *ws, size_t ws_bytes, void *stream) {
+  return prefill_common(rows, false, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
+                        k_idx_scale, w, logits, ld_logits, topk, idx, n_heads, softmax_scale, q,
+                        kv, w_uk, w_uv, out, lse, dense_threshold, ws, ws_bytes, stream);
+}
+
+int dsa_sparse_attention_prefill_paged(const dsa_rows *rows, int idx_dtype, int idx_heads,
+                                       int idx_dim, const void *q_idx, const float *q_idx_scale,
+                                       const void *k_idx, const float *k_idx_scale,
+                                       const float *w, float *logits, int64_t ld_logits, int topk,
+                                       int32_t *idx, int n_heads, float softmax_scale,
+                                       const void *q, const void *kv, const void *w_uk,
+                                       const void *w_uv, void *out, float *lse,
+                                       int dense_threshold, void *ws, size_t ws_bytes,
+                                       void *stream) {
+  return prefill_common(rows, true, idx_dtype, idx_heads, idx_dim, q_idx, q_idx_scale, k_idx,
+                        k_idx_scale, w, logits, ld_logits, topk, idx, n_heads, softmax_scale, q,
+                        kv, w_uk, w_uv, out, lse, dense_threshold, ws, ws_bytes, stream);
 }
 
 int dsa_prep_cache_write(int num_tokens, const int32_t *positions, const int64_t *cache_rows,

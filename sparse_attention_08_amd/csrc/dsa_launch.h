@@ -102,15 +102,31 @@ hipError_t launch_mla_bf16_select(const RowsHost &rows, bool paged, int H, float
                                   int64_t ld, void *topk_ws, int hist_lists, hipStream_t stream);
 
 // ---- masked MHA mode (short prefill) ----
-// Workspace: decompressed K_nope and V ([cache_rows, H, 128] bf16 each) and, with idx, the
-// rows' top-k sets as bit masks.
-size_t mha_workspace_bytes(int64_t cache_rows, int H, int R, int max_row_len, bool masked);
-// q [R, H, 192] bf16; kv latent cache rows [cache_rows, 576] bf16; W_UK, W_UV [H, 128, 512]
-// bf16; idx [R, k] or nullptr (dense causal); out [R, H, 128] bf16, lse [R, H] (optional).
-hipError_t launch_mha_prefill(const RowsHost &rows, bool paged, int64_t cache_rows, int H,
-                              float scale, const void *q, const void *kv, const void *w_uk,
-                              const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
-                              void *ws, hipStream_t stream);
+// Workspace: each sequence's reach, its decompressed K_nope and V ([B, max_row_len, H, 128]
+// bf16 each) and, with idx, the rows' top-k sets as bit masks.
+size_t mha_workspace_bytes(int num_seqs, int H, int R, int max_row_len, bool masked);
+// q [R, H, 192] bf16; kv latent cache rows [.., 576] bf16 (only rows the batch reaches are
+// read); W_UK, W_UV [H, 128, 512] bf16; idx [R, k] or nullptr (dense causal); out [R, H, 128]
+// bf16, lse [R, H] (optional).
+// ---- the MQA way of the prefill dispatch (prefill.hip) ----
+// q_abs [R, H, 576] = [W_UK[h]^T q_nope | q_rope]; the attention's latent output o_lat
+// [R, H, 512] maps back to out [R, H, 128] = W_UV[h] o_lat.
+struct AbsorbBuffers {
+  uint16_t *wuk_t;   // [H, 512, 128] W_UK transposed
+  uint16_t *q_abs;   // [R, H, 576]
+  uint16_t *o_lat;   // [R, H, 512]
+};
+size_t absorb_workspace_bytes(int R, int H);
+AbsorbBuffers carve_absorb(void *ws, int R, int H);
+hipError_t launch_absorb_query(int R, int H, const void *q, const void *w_uk,
+                               const AbsorbBuffers &b, hipStream_t stream);
+hipError_t launch_expand_output(int R, int H, const uint16_t *o_lat, const void *w_uv, void *out,
+                                hipStream_t stream);
+
+hipError_t launch_mha_prefill(const RowsHost &rows, bool paged, int H, float scale,
+                              const void *q, const void *kv, const void *w_uk, const void *w_uv,
+                              const int32_t *idx, int k, void *out, float *lse, void *ws,
+                              hipStream_t stream);
 
 // ---- indexer-input and cache-write prep ----
 // Query rows (R of them, R may be 0): 64 indexer heads rotated to bf16 or e4m3 (+ per-head

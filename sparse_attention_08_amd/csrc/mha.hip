@@ -3,9 +3,12 @@
 // techniques map", "Multi-head latent attention": per head 128 nope + 64 rope query/key dims
 // and 128 value dims, decompressed from the 512-dim latent).
 //
-// Step 1 decompresses every latent cache row n: K_nope[n, h] = W_UK[h] c_n and V[n, h] =
-// W_UV[h] c_n (128 dims each, bf16), two plain GEMMs on rocBLAS.  Step 2 attends: row r,
-// head h, over its sequence's positions s (all s < row_len, or the set of its top-k entries):
+// Step 1 decompresses the latent entries the batch can reach: for each sequence b, its
+// positions s below the longest row_len of its rows (its reach), K_nope[b, s, h] = W_UK[h] c
+// and V[b, s, h] = W_UV[h] c of the latent c at the cache row of (b, s), 128 dims each, bf16,
+// into a compact [B, max_row_len, H, 128] layout (a gather GEMM, gemm_nt.h); cache rows no
+// sequence reaches are never read.  Step 2 attends: row r, head h, over its sequence's
+// positions s (all s < row_len, or the set of its top-k entries):
 // z_s = scale [q_nope | q_rope] . [K_nope[s, h] | kr_s], out = softmax(z) V, lse = ln sum e^z.
 //
 // Attention kernel: a workgroup owns 128 consecutive query rows (4 waves x 2 blocks of 16) of
@@ -18,12 +21,9 @@
 // (block kb, row 4g + i <-> key 8g + 4kb + i) so each lane's weights are the B operand of
 // the value product as they stand.  Rows of one workgroup that belong to different
 // sequences are handled one sequence at a time.
-#include <mutex>
-
-#include <rocblas/rocblas.h>
-
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "gemm_nt.h"
 
 namespace dsa {
 
@@ -86,7 +86,7 @@ mha_prefill_kernel(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ k_nope,
     const uint8_t *__restrict__ vals, const uint8_t *__restrict__ kv,
     const uint32_t *__restrict__ mask, int mask_words, uint16_t *__restrict__ out,
-    float *__restrict__ lse) {
+    float *__restrict__ lse, int lmax) {
   __shared__ __attribute__((aligned(16))) MhaShared sh;
   // longest row tiles (most keys) first; the heads of one row tile are consecutive workgroups
   const int rt = n_row_tiles - 1 - (int)(blockIdx.x / H);
@@ -220,12 +220,17 @@ mha_prefill_kernel(
       else
         return base + s;
     };
-    // per-lane source bases of the wave's instructions (the key's cache row is added per tile)
+    // per-lane source bases of the wave's instructions (per tile, the key's row is added: its
+    // compact row b * lmax + s for the decompressed keys and values, its cache row for the
+    // RoPE keys, which come from the latent cache)
+    const int64_t cbase = (int64_t)b * lmax;
     const uint8_t *src_base[kMhaDmaPerWave];
     int64_t src_stride[kMhaDmaPerWave];
+    bool dec[kMhaDmaPerWave];
 #pragma unroll
     for (int u = 0; u < kMhaDmaPerWave; ++u) {
       const int i = wave + kMhaWaves * u;
+      dec[u] = i < 8 || i >= 12;
       if (i < 8) {
         src_base[u] = k_nope + (int64_t)h * 256 + d_src[u];
         src_stride[u] = (int64_t)H * 256;
@@ -251,20 +256,23 @@ mha_prefill_kernel(
         }
       if ((tile + 1) * kMhaKeys <= kmax) {
         // every key of the tile exists: 32 consecutive cache rows (half of one page when paged)
+        // and 32 consecutive compact rows
         int64_t row0;
         if constexpr (PAGED)
           row0 = (int64_t)__builtin_amdgcn_readfirstlane(sh.pages[tile >> 1]) * 64 +
                  (tile & 1) * kMhaKeys;
         else
           row0 = base + (int64_t)tile * kMhaKeys;
+        const int64_t crow0 = cbase + (int64_t)tile * kMhaKeys;
 #pragma unroll
         for (int u = 0; u < kMhaDmaPerWave; ++u)
-          mha_dma16(lane_src[u] + row0 * src_stride[u], st + 1024 * (wave + kMhaWaves * u));
+          mha_dma16(lane_src[u] + (dec[u] ? crow0 : row0) * src_stride[u],
+                    st + 1024 * (wave + kMhaWaves * u));
       } else {
 #pragma unroll
         for (int u = 0; u < kMhaDmaPerWave; ++u) {
           const int s = min(tile * kMhaKeys + d_key[u], kmax - 1);   // tail keys re-read the last
-          mha_dma16(lane_src[u] + (cache_row(s) - d_key[u]) * src_stride[u],
+          mha_dma16(lane_src[u] + ((dec[u] ? cbase + s : cache_row(s)) - d_key[u]) * src_stride[u],
                     st + 1024 * (wave + kMhaWaves * u));
         }
       }
@@ -414,50 +422,88 @@ __global__ __launch_bounds__(256) void mha_mask_set_kernel(const int32_t *__rest
   }
 }
 
-// One rocBLAS handle per device, created on first use.
-static rocblas_handle mha_blas_handle(int device) {
-  static std::mutex mu;
-  static rocblas_handle handles[64] = {};
-  std::lock_guard<std::mutex> lock(mu);
-  if (device < 0 || device >= 64) return nullptr;
-  if (!handles[device] && rocblas_create_handle(&handles[device]) != rocblas_status_success)
-    handles[device] = nullptr;
-  return handles[device];
+// Reach of each sequence: the longest row_len among its rows (0 without rows).
+__global__ __launch_bounds__(256) void mha_reach_kernel(const int32_t *__restrict__ row_seq,
+                                                        const int32_t *__restrict__ row_len, int R,
+                                                        int32_t *__restrict__ reach) {
+  __shared__ int32_t wmax[256 / kWave];
+  const int b = blockIdx.x;
+  int m = 0;
+  for (int r = threadIdx.x; r < R; r += 256)
+    if (row_seq[r] == b) m = max(m, row_len[r]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 256 / kWave; ++w) m = max(m, wmax[w]);
+    reach[b] = max(m, wmax[0]);
+  }
 }
 
-size_t mha_workspace_bytes(int64_t cache_rows, int H, int R, int max_row_len, bool masked) {
-  const size_t kv = (size_t)cache_rows * H * 128 * 2;   // K_nope and V, bf16 each
+// The decompression as a gather GEMM: C row m = compact row (b = m / lmax, s = m % lmax),
+// live while s < reach[b]; its A row is the latent c (first 512 of 576) at the cache row of
+// (b, s); B row n = row n of W_UK (z = 0) or W_UV (z = 1) viewed as [H * 128, 512]; C row m
+// of K_nope (z = 0) or V (z = 1), [B * lmax, H * 128].
+template <bool PAGED>
+struct MhaDecompress {
+  int M, N, K;
+  const uint16_t *kv;
+  const int64_t *seq_start;
+  const int32_t *page_table;
+  int max_pages, lmax;
+  const int32_t *reach;
+  const uint16_t *w[2];
+  uint16_t *dst[2];
+  __device__ bool live(int m, int) const { return m % lmax < reach[m / lmax]; }
+  __device__ const uint16_t *a(int m, int) const {
+    const int b = m / lmax, s = m % lmax;
+    int64_t row;
+    if constexpr (PAGED)
+      row = (int64_t)page_table[(int64_t)b * max_pages + (s >> 6)] * 64 + (s & 63);
+    else
+      row = seq_start[b] + s;
+    return kv + row * 576;
+  }
+  __device__ const uint16_t *b(int n, int z) const { return w[z] + (int64_t)n * 512; }
+  __device__ uint16_t *c(int m, int z) const { return dst[z] + (int64_t)m * N; }
+};
+
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// [B] reaches, then K_nope and V ([B, max_row_len, H, 128] bf16 each), then the masks
+size_t mha_workspace_bytes(int num_seqs, int H, int R, int max_row_len, bool masked) {
+  const size_t dec = (size_t)num_seqs * max_row_len * H * 128 * 2;
   const size_t m = masked ? (size_t)R * ((max_row_len + 31) / 32) * 4 : 0;
-  return 2 * ((kv + 255) & ~(size_t)255) + m;
+  return a256(4 * (size_t)num_seqs) + 2 * a256(dec) + m;
 }
 
-hipError_t launch_mha_prefill(const RowsHost &rh, bool paged, int64_t cache_rows, int H,
-                              float scale, const void *q, const void *kv, const void *w_uk,
-                              const void *w_uv, const int32_t *idx, int k, void *out, float *lse,
-                              void *ws, hipStream_t stream) {
-  const size_t kv_bytes = (((size_t)cache_rows * H * 128 * 2) + 255) & ~(size_t)255;
+hipError_t launch_mha_prefill(const RowsHost &rh, bool paged, int H, float scale, const void *q,
+                              const void *kv, const void *w_uk, const void *w_uv,
+                              const int32_t *idx, int k, void *out, float *lse, void *ws,
+                              hipStream_t stream) {
+  const int B = rh.num_seqs, L = rh.max_row_len;
+  const size_t dec_bytes = a256((size_t)B * L * H * 128 * 2), reach_bytes = a256(4 * (size_t)B);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
-  uint16_t *k_nope = reinterpret_cast<uint16_t *>(wsb);
-  uint16_t *vals = reinterpret_cast<uint16_t *>(wsb + kv_bytes);
-  uint32_t *mask = idx ? reinterpret_cast<uint32_t *>(wsb + 2 * kv_bytes) : nullptr;
-  const int mask_words = (rh.max_row_len + 31) / 32;
-  // decompression: rows are the latent cache rows (stride 576 elements, first 512 used);
-  // column-major view: D (H*128 x rows) = W^T (H*128 x 512, from W [H*128][512]) x C^T
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  rocblas_handle hb = mha_blas_handle(dev);
-  if (!hb) return hipErrorNotInitialized;
-  if (rocblas_set_stream(hb, stream) != rocblas_status_success) return hipErrorNotInitialized;
-  const float one = 1.f, zero = 0.f;
-  for (int which = 0; which < 2; ++which) {
-    const rocblas_status st = rocblas_gemm_ex(
-        hb, rocblas_operation_transpose, rocblas_operation_none, H * 128, (rocblas_int)cache_rows,
-        512, &one, which ? w_uv : w_uk, rocblas_datatype_bf16_r, 512, kv, rocblas_datatype_bf16_r,
-        576, &zero, which ? (void *)vals : (void *)k_nope, rocblas_datatype_bf16_r, H * 128,
-        which ? (void *)vals : (void *)k_nope, rocblas_datatype_bf16_r, H * 128,
-        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    if (st != rocblas_status_success) return hipErrorLaunchFailure;
+  int32_t *reach = reinterpret_cast<int32_t *>(wsb);
+  uint16_t *k_nope = reinterpret_cast<uint16_t *>(wsb + reach_bytes);
+  uint16_t *vals = reinterpret_cast<uint16_t *>(wsb + reach_bytes + dec_bytes);
+  uint32_t *mask =
+      idx ? reinterpret_cast<uint32_t *>(wsb + reach_bytes + 2 * dec_bytes) : nullptr;
+  const int mask_words = (L + 31) / 32;
+  mha_reach_kernel<<<B, 256, 0, stream>>>(rh.row_seq, rh.row_len, rh.num_rows, reach);
+  const dim3 dgrid((unsigned)H, (unsigned)(((int64_t)B * L + kGemmTile - 1) / kGemmTile), 2);
+  const auto *kv16 = static_cast<const uint16_t *>(kv);
+  const auto *wk = static_cast<const uint16_t *>(w_uk);
+  const auto *wv = static_cast<const uint16_t *>(w_uv);
+  if (paged) {
+    const MhaDecompress<true> pr{B * L, H * 128, 512, kv16, rh.seq_start, rh.page_table,
+                                 rh.max_pages, L, reach, {wk, wv}, {k_nope, vals}};
+    gemm_nt_kernel<<<dgrid, kGemmThreads, 0, stream>>>(pr);
+  } else {
+    const MhaDecompress<false> pr{B * L, H * 128, 512, kv16, rh.seq_start, rh.page_table,
+                                  rh.max_pages, L, reach, {wk, wv}, {k_nope, vals}};
+    gemm_nt_kernel<<<dgrid, kGemmThreads, 0, stream>>>(pr);
   }
   if (idx) {
     const int64_t n = (int64_t)rh.num_rows * mask_words;
@@ -475,7 +521,7 @@ hipError_t launch_mha_prefill(const RowsHost &rh, bool paged, int64_t cache_rows
   auto *oo = static_cast<uint16_t *>(out);
 #define DSA_MHA_ARGS                                                                           \
   rh.num_rows, H, n_row_tiles, rh.row_seq, rh.row_len, rh.seq_start, rh.page_table,          \
-      rh.max_pages, scale_log2, qq, kn, vv, kvb, mask, mask_words, oo, lse
+      rh.max_pages, scale_log2, qq, kn, vv, kvb, mask, mask_words, oo, lse, L
   if (paged) {
     if (idx) mha_prefill_kernel<true, true><<<grid, kMhaThreads, 0, stream>>>(DSA_MHA_ARGS);
     else mha_prefill_kernel<true, false><<<grid, kMhaThreads, 0, stream>>>(DSA_MHA_ARGS);

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert dsa.abi_version() == 1
+    assert dsa.abi_version() == 2
     assert dsa.status_string(0) == "DSA_OK"
     for s in (1, 2, 3, 4):
         assert dsa.status_string(s).startswith(dsa.STATUS[s])
@@ -231,13 +231,12 @@ def test_prep_validation(lib):
 
 
 def test_mha_validation(lib):
-    def call(rows, n_cache=64, H=128, scale=0.07, idx=None, k=0, ws=None, ws_bytes=0, ptrs=True,
+    def call(rows, H=128, scale=0.07, idx=None, k=0, ws=None, ws_bytes=0, ptrs=True,
              name="dsa_mha_prefill"):
         p = FAKE if ptrs else None
-        return getattr(lib, name)(ctypes.byref(rows), n_cache, H, scale, p, p, p, p, idx, k, p,
-                                  None, ws, ws_bytes, None)
+        return getattr(lib, name)(ctypes.byref(rows), H, scale, p, p, p, p, idx, k, p, None, ws,
+                                  ws_bytes, None)
     r = _rows()
-    assert call(r, n_cache=0) == INVALID
     assert call(r, H=0) == INVALID
     assert call(r, scale=0.0) == INVALID and call(r, scale=float("nan")) == INVALID
     assert call(r, idx=FAKE, k=0) == INVALID and call(r, idx=FAKE, k=2049) == INVALID
@@ -245,12 +244,42 @@ def test_mha_validation(lib):
     assert call(r, name="dsa_mha_prefill_paged") == INVALID            # layout mismatch
     assert call(_rows(num_rows=0)) == OK
     assert call(_rows(max_row_len=16385)) == UNSUPPORTED
-    need = lib.dsa_mha_prefill_workspace_size(64, 128, 2, 100, 0)
-    assert need >= 2 * 64 * 128 * 256
-    assert lib.dsa_mha_prefill_workspace_size(64, 128, 2, 100, 1) > need   # + the masks
+    # the decompressed keys and values cover max_row_len positions of each sequence, whatever
+    # the cache's size
+    need = lib.dsa_mha_prefill_workspace_size(2, 128, 2, 100, 0)
+    assert need >= 2 * 2 * 100 * 128 * 256
+    assert lib.dsa_mha_prefill_workspace_size(2, 128, 2, 100, 1) > need   # + the masks
+    assert lib.dsa_mha_prefill_workspace_size(0, 128, 2, 100, 0) == 0
     assert call(r) == WORKSPACE and call(r, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
     assert lib.dsa_prefill_dense_mode(2048, 2048) == 1 and lib.dsa_prefill_dense_mode(2049, 2048) == 0
     assert lib.dsa_prefill_dense_mode(0, 2048) == 0
+
+
+def test_prefill_dispatch_validation_and_sizes(lib):
+    def call(rows, threshold, H=128, topk=2048, ws=None, ws_bytes=0, idx=FAKE, ptrs=True,
+             name="dsa_sparse_attention_prefill"):
+        p = FAKE if ptrs else None
+        return getattr(lib, name)(ctypes.byref(rows), 1, 64, 128, p, None, p, None, p, p, 100,
+                                  topk, idx, H, 0.07, p, p, p, p, p, None, threshold, ws,
+                                  ws_bytes, None)
+    r = _rows()
+    size = lambda R, L, t, H=128, topk=2048: lib.dsa_sparse_attention_prefill_workspace_size(
+        R, 2, L, 1, topk, H, t)
+    # short batch under the threshold: the dense MHA mode (no selection, no absorption buffers)
+    assert size(2, 100, 100) == lib.dsa_mha_prefill_workspace_size(2, 128, 2, 100, 0)
+    # rows longer than topk under the threshold: selection + masked MHA
+    assert size(2, 100, 100, topk=64) >= lib.dsa_mha_prefill_workspace_size(2, 128, 2, 100, 1)
+    # over the threshold (0: always): the MQA path with its absorbed query and latent output
+    assert size(2, 100, 0) >= 2 * 128 * (576 + 512) * 2 + 128 * 512 * 128 * 2
+    assert size(2, 100, 99) == size(2, 100, 0)
+    assert size(2, 100, 0, topk=0) == 0
+    assert call(r, 0, ptrs=False) == INVALID
+    assert call(r, 0, topk=0) == INVALID
+    assert call(r, 0, H=64) == UNSUPPORTED or call(r, 0, H=64) == WORKSPACE
+    assert call(r, 0) == WORKSPACE
+    assert call(r, 0, idx=None) == INVALID                           # the selection needs idx
+    assert call(r, 0, name="dsa_sparse_attention_prefill_paged") == INVALID
+    assert call(_rows(num_rows=0), 0) == OK
 
 
 def test_noalloc_decode_rejects_batches_beyond_its_scratch(lib):

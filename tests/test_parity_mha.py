@@ -93,3 +93,134 @@ def test_dense_equals_masked_with_every_position():
     a = dsa.mha_prefill(dev_rows(mb.wl), mb.q, mb.wl.kv, mb.w_uk, mb.w_uv, mb.scale)
     b = dsa.mha_prefill(dev_rows(mb.wl), mb.q, mb.wl.kv, mb.w_uk, mb.w_uv, mb.scale, idx=idx)
     assert torch.equal(a, b)
+
+
+def _outputs(mb, idx=None, kv=None, rows=None):
+    wl = mb.wl
+    R, H = mb.q.shape[0], mb.q.shape[1]
+    out = torch.full((R, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((R, H), float("nan"), dtype=torch.float32, device=DEV)
+    dsa.mha_prefill(rows or dev_rows(wl), mb.q, wl.kv if kv is None else kv, mb.w_uk, mb.w_uv,
+                    mb.scale, idx=idx, out=out, lse=lse)
+    return out, lse
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_foreign_cache_rows_are_never_read(paged):
+    """The cache also holds rows no sequence of the batch reaches, filled with NaN: the pages
+    the page table lists past each sequence's end (paged), or rows in front of and between
+    the sequences (contiguous).  The results equal those on the plain cache bit for bit, and
+    the workspace does not grow with the cache."""
+    mb = workloads.mha_batch([300, 77], H=16, paged=paged, seed=67, device=DEV)
+    wl = mb.wl
+    say(f"mha foreign rows {'paged' if paged else 'contiguous'}")
+    ref_o, ref_l = _outputs(mb)
+    if paged:
+        P = wl.kv.shape[0]
+        F = 5
+        kv2 = torch.cat([wl.kv, torch.full((F, 64, 576), float("nan"), dtype=wl.kv.dtype,
+                                           device=DEV)])
+        pt = wl.page_table.clone()
+        tail = pt < 0
+        pt[tail] = P + torch.arange(int(tail.sum()), device=DEV, dtype=torch.int32) % F
+        rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, page_table=pt)
+    else:
+        pad = 1000
+        kv2 = torch.cat([torch.full((pad, 576), float("nan"), dtype=wl.kv.dtype, device=DEV),
+                         wl.kv[:300], torch.full((pad, 576), float("nan"), dtype=wl.kv.dtype,
+                                                 device=DEV), wl.kv[300:]])
+        ss = torch.tensor([pad, 2 * pad + 300], dtype=torch.int64, device=DEV)
+        rows = dsa.Rows(wl.row_seq, wl.row_len, wl.max_row_len, wl.num_seqs, seq_start=ss)
+    o, l = _outputs(mb, kv=kv2, rows=rows)
+    assert torch.isfinite(o.float()).all()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    assert dsa.mha_prefill_workspace_size(2, 16, wl.num_rows, wl.max_row_len, False) < \
+        kv2.numel() // 576 * 16 * 512
+
+
+def test_hip_graph_replays_match_eager_mha_and_dispatch():
+    """The MHA mode (dense and masked) and the prefill dispatch in both forms, captured once in
+    a HIP graph and replayed three times with eager work in between: every replay equals the
+    eager call bit for bit."""
+    mb = workloads.mha_batch([600], H=128, H_I=64, seed=68, device=DEV)
+    wl = mb.wl
+    R, H, k = wl.num_rows, 128, 256
+    logits = torch.empty((R, wl.max_row_len), dtype=torch.float32, device=DEV)
+    idx = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    dsa.indexer_topk(dev_rows(wl), wl.q_idx, wl.w, wl.k_idx, logits, k, idx=idx)
+    cases = {}
+    for name in ("dense", "masked", "dispatch_mha", "dispatch_mqa"):
+        out = torch.empty((R, H, 128), dtype=torch.bfloat16, device=DEV)
+        lg = torch.empty_like(logits)
+        ix = torch.empty_like(idx)
+        if name == "dense":
+            ws = torch.empty(dsa.mha_prefill_workspace_size(1, H, R, R, False), dtype=torch.uint8,
+                             device=DEV)
+            fn = lambda out=out, ws=ws: dsa.mha_prefill(dev_rows(wl), mb.q, wl.kv, mb.w_uk,
+                                                        mb.w_uv, mb.scale, out=out, ws=ws)
+        elif name == "masked":
+            ws = torch.empty(dsa.mha_prefill_workspace_size(1, H, R, R, True), dtype=torch.uint8,
+                             device=DEV)
+            fn = lambda out=out, ws=ws: dsa.mha_prefill(dev_rows(wl), mb.q, wl.kv, mb.w_uk,
+                                                        mb.w_uv, mb.scale, idx=idx, out=out, ws=ws)
+        else:
+            t = R if name == "dispatch_mha" else 0
+            ws = torch.empty(dsa.sparse_attention_prefill_workspace_size(
+                R, 1, R, wl.q_idx.dtype, k, H, t), dtype=torch.uint8, device=DEV)
+            fn = lambda out=out, ws=ws, t=t, lg=lg, ix=ix: dsa.sparse_attention_prefill(
+                dev_rows(wl), wl.q_idx, wl.w, wl.k_idx, lg, k, mb.q, wl.kv, mb.w_uk, mb.w_uv,
+                mb.scale, t, idx=ix, out=out, ws=ws)
+        cases[name] = (fn, out)
+    for name, (fn, out) in cases.items():
+        say(f"graph replay {name}")
+        fn()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for rep in range(3):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"{name}: replay {rep} differs"
+            junk = torch.randn(1 << 20, device=DEV)   # eager work between the replays
+            junk.sum().item()
+        del graph
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_dispatch_both_forms_against_the_oracle(paged):
+    """dsa_sparse_attention_prefill on one 300-token sequence with top-96 selection, in both
+    forms: the masked MHA mode (threshold 300) and the MQA path (threshold 0: absorbed query,
+    sparse MLA over the latent, output through W_UV).  Both select the same idx (the indexer
+    and top-k calls), and both match the oracle's MHA over that set (decompression in fp64)
+    on sampled rows; the short rows (at most 96 positions) are dense."""
+    mb = workloads.mha_batch([300], H=128, H_I=64, paged=paged, seed=69, device=DEV)
+    wl = mb.wl
+    R, H, k = wl.num_rows, 128, 96
+    which = list(range(0, R, 13)) + [R - 1]
+    K, V = oracle.mha_decompress(raw(wl.kv), raw(mb.w_uk), raw(mb.w_uv))
+    outs = {}
+    for t in (R, 0):
+        say(f"prefill dispatch threshold {t} {'paged' if paged else 'contiguous'}")
+        logits = torch.empty((R, wl.max_row_len), dtype=torch.float32, device=DEV)
+        idx = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
+        out = torch.full((R, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((R, H), float("nan"), dtype=torch.float32, device=DEV)
+        dsa.sparse_attention_prefill(dev_rows(wl), wl.q_idx, wl.w, wl.k_idx, logits, k, mb.q,
+                                     wl.kv, mb.w_uk, mb.w_uv, mb.scale, t, idx=idx, out=out,
+                                     lse=lse)
+        ref_o, ref_l = oracle.mha(raw(mb.q), K, V, oracle_rows(wl), mb.scale, idx=raw(idx),
+                                  which=which)
+        err = oracle.max_abs_rel(out.float().cpu().numpy()[which], ref_o)
+        lerr = oracle.max_abs_rel(lse.cpu().numpy()[which], ref_l)
+        assert err <= TOL["bf16"] and lerr <= TOL["bf16"], f"threshold {t}: {err} {lerr}"
+        outs[t] = (idx, out)
+    assert torch.equal(outs[R][0], outs[0][0])   # one selection

@@ -377,12 +377,13 @@ class MhaBatch:
     scale: float
 
 
-def mha_batch(lens, *, new=None, H=128, paged=False, seed=0, device="cpu") -> MhaBatch:
-    """Rows and latent cache as prefill_batch (tiny indexer inputs, unused here), then from the
-    same device generator stream: q ~ N(0,1), W_UK and W_UV ~ N(0, 1/512) (keys and values of
-    unit scale), all bf16."""
-    wl = prefill_batch(lens, new=new, paged=paged, H=H, H_I=4, D_I=128, seed=seed, device=device,
-                       name="mha_batch")
+def mha_batch(lens, *, new=None, H=128, H_I=4, paged=False, seed=0, device="cpu") -> MhaBatch:
+    """Rows, latent cache and bf16 indexer inputs (H_I heads of 128 dims: the model's 64 where
+    the indexer runs, else a tiny unused set) as prefill_batch, then from the same device
+    generator stream: q ~ N(0,1), W_UK and W_UV ~ N(0, 1/512) (keys and values of unit scale),
+    all bf16."""
+    wl = prefill_batch(lens, new=new, paged=paged, H=H, H_I=H_I, D_I=128, seed=seed,
+                       device=device, name="mha_batch")
     gen = torch.Generator(device=device)
     gen.manual_seed(seed + 1)
     R = wl.num_rows
