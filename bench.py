@@ -80,7 +80,8 @@ def parse():
                    help="no GPU work: 'trace NAME STATS_CSV CMD' writes profiles/NAME.md from a "
                         "rocprofv3 --kernel-trace --stats run; 'pmc KERNEL FETCH_CSV WRITE_CSV "
                         "COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB CONFIG CMD...' writes "
-                        "profiles/KERNEL_pmc.{json,md} (HBM bytes per launch)")
+                        "profiles/KERNEL_pmc.{json,md} (HBM bytes per launch); 'mfma NAME CSV "
+                        "CMD' writes profiles/NAME.md from a run with the MFMA counters")
     return p.parse_args()
 
 
@@ -125,9 +126,7 @@ def _short_name(name: str) -> str:
 def summarize_trace(out_name: str, stats_csv: str, command: str):
     """profiles/<out_name>.md: the dsa kernels of a rocprofv3 --kernel-trace --stats run."""
     import csv
-    # the library's kernels, and the rocBLAS GEMMs it calls (Tensile kernels are named Cijk_*)
-    rows = [r for r in csv.DictReader(open(stats_csv))
-            if "dsa::" in r["Name"] or r["Name"].startswith("Cijk_")]
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "dsa::" in r["Name"]]
     lines = [f"# {out_name}", "", "Command (from the repository root, on one MI355X):", "",
              "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | share of dsa time |",
@@ -137,6 +136,53 @@ def summarize_trace(out_name: str, stats_csv: str, command: str):
         lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / total:.1%} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, out_name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+SIMDS = 1024   # 256 CUs x 4 SIMDs
+XCDS = 8       # GRBM_GUI_ACTIVE of a dispatch is the sum over the XCDs
+
+
+def summarize_mfma(out_name: str, csv_path: str, command: str):
+    """profiles/<out_name>.md: per dsa kernel of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+    GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 run, medians per dispatch: the MFMA busy
+    share (busy SIMD cycles / (active cycles of one XCD x SIMDs): utilisation at the clock the
+    chip ran), the clock that implies (active cycles of one XCD / duration), and the bf16
+    MFMA flops (MOPS x 512) and rate over the dispatch's own duration against the 2.5 PF/s
+    figure (2.4 GHz)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if "dsa::" not in r["Kernel_Name"]:
+            continue
+        key = (_short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+        d = per.setdefault(key, {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    kernels = {}
+    for (name, _), d in per.items():
+        kernels.setdefault(name, []).append(d)
+    lines = [f"# {out_name}", "", "Command (from the repository root, on one MI355X):", "",
+             "```", command, "```", "",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), "
+             "i.e. MFMA utilisation at the clock the chip ran; clock = GRBM_GUI_ACTIVE / 8 / "
+             "duration; bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; medians over the "
+             "dispatches.", "",
+             "| kernel | dispatches | MFMA busy | clock GHz | bf16 MFMA GFLOP | duration us | TFLOP/s | of 2.5 PF |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, ds in sorted(kernels.items()):
+        busy = statistics.median(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds)
+        gui = statistics.median(d.get("GRBM_GUI_ACTIVE", 0.0) for d in ds)
+        flop = statistics.median(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in ds) * 512
+        ns = statistics.median(d.get("ns", 0.0) for d in ds)
+        util = busy / (gui / XCDS * SIMDS) if gui else 0.0
+        ghz = gui / XCDS / ns if ns else 0.0
+        rate = flop / ns / 1e3 if ns else 0.0
+        lines.append(f"| `{name}` | {len(ds)} | {util:.1%} | {ghz:.2f} | {flop / 1e9:,.1f} | "
+                     f"{ns / 1e3:,.1f} | {rate:,.0f} | {rate / BF16_PEAK_TFLOPS:.1%} |")
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, out_name + ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -469,8 +515,11 @@ def main():
             summarize_trace(a[1], a[2], " ".join(a[3:]))
         elif a[0] == "pmc" and len(a) >= 9:
             summarize_pmc(a[1], a[2], a[3], a[4], a[5], a[6], a[7], " ".join(a[8:]))
+        elif a[0] == "mfma" and len(a) >= 4:
+            summarize_mfma(a[1], a[2], " ".join(a[3:]))
         else:
-            raise SystemExit("--summarize trace NAME CSV CMD... | pmc KERNEL F W CF CW MIB CONFIG CMD...")
+            raise SystemExit("--summarize trace NAME CSV CMD... | pmc KERNEL F W CF CW MIB CONFIG "
+                             "CMD... | mfma NAME CSV CMD...")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is a single-GPU "
