@@ -62,9 +62,15 @@ __device__ void radix_digit(const Acc &acc, int n, int shift, BlockScratch<NT> &
   for (int i = threadIdx.x; i < NB; i += NT) sh.hist[i] = 0;
   __syncthreads();
   const uint32_t prefix = sh.prefix, mask = sh.mask;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t u = acc.key(i);
-    if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & (NB - 1)], 1u);
+  // four keys a thread per round, their reads issued together
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+    uint32_t u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = i0 + q * NT < n ? acc.key(i0 + q * NT) : 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (i0 + q * NT < n && (u[q] & mask) == prefix)
+        atomicAdd(&sh.hist[(u[q] >> shift) & (NB - 1)], 1u);
   }
   __syncthreads();
   // thread t owns bins NB-1-PER*t-j (j < PER): descending digit order across threads
@@ -120,16 +126,26 @@ __device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__
   radix_digit<NT, kD2Bits>(acc, n, 0, sh);
   const uint32_t T = sh.prefix;
   const int32_t need_eq = sh.need;
-  // ordered write: wave w owns a contiguous span; counts, wave offsets, then ballots
+  // ordered write: wave w owns a contiguous span; counts, wave offsets, then ballots (four
+  // keys a lane per round, their reads issued together)
   constexpr int NW = NT / kWave;
+  constexpr int kU = 4;
   const int span = (((n + NW - 1) / NW) + 63) & ~63;
   const int lo = wave * span, hi = min(n, lo + span);
   uint32_t gt_cnt = 0, eq_cnt = 0;
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const uint32_t u = i < hi ? acc.key(i) : 0u;
-    gt_cnt += __popcll(__ballot(i < hi && u > T));
-    eq_cnt += __popcll(__ballot(i < hi && u == T));
+  for (int base = lo; base < hi; base += kU * kWave) {
+    uint32_t u[kU];
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int i = base + q * kWave + lane;
+      u[q] = i < hi ? acc.key(i) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const bool in = base + q * kWave + lane < hi;
+      gt_cnt += __popcll(__ballot(in && u[q] > T));
+      eq_cnt += __popcll(__ballot(in && u[q] == T));
+    }
   }
   if (lane == 0) {
     sh.wcnt[0][wave] = gt_cnt;
@@ -143,18 +159,26 @@ __device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__
     eq_before += sh.wcnt[1][w];
   }
   const uint64_t lt = lanemask_lt();
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const uint32_t u = i < hi ? acc.key(i) : 0u;
-    const bool gt = i < hi && u > T;
-    const bool eq = i < hi && u == T;
-    const uint64_t eq_mask = __ballot(eq);
-    const uint32_t eq_rank = eq_before + __popcll(eq_mask & lt);
-    const bool sel = gt || (eq && eq_rank < (uint32_t)need_eq);
-    const uint64_t sel_mask = __ballot(sel);
-    if (sel) out[sel_before + __popcll(sel_mask & lt)] = acc.pos(i);
-    eq_before += __popcll(eq_mask);
-    sel_before += __popcll(sel_mask);
+  for (int base = lo; base < hi; base += kU * kWave) {
+    uint32_t u[kU];
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int i = base + q * kWave + lane;
+      u[q] = i < hi ? acc.key(i) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int i = base + q * kWave + lane;
+      const bool gt = i < hi && u[q] > T;
+      const bool eq = i < hi && u[q] == T;
+      const uint64_t eq_mask = __ballot(eq);
+      const uint32_t eq_rank = eq_before + __popcll(eq_mask & lt);
+      const bool sel = gt || (eq && eq_rank < (uint32_t)need_eq);
+      const uint64_t sel_mask = __ballot(sel);
+      if (sel) out[sel_before + __popcll(sel_mask & lt)] = acc.pos(i);
+      eq_before += __popcll(eq_mask);
+      sel_before += __popcll(sel_mask);
+    }
   }
 }
 
