@@ -541,6 +541,37 @@ def test_mla_skips_invalid_and_empty_selections():
     assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_many_row_attention_edges(paged):
+    """The no-split attention (one workgroup per row): a short row whose valid slots are
+    compacted, duplicate and out-of-range slots, k = 1000 (a ragged last tile), a row with
+    no valid slot, and cache values that grow across the cache so that the running maximum
+    of the softmax moves by more than its lazy threshold between tiles (rescales)."""
+    lens = [40, 700, 3000, 5000]
+    wl = workloads.decode(lens, paged=paged, seed=21, device=DEV, name="many_row_edges")
+    kv = wl.kv.reshape(-1, wl.kv.shape[-1])
+    grow = 1.0 + 7.0 * torch.arange(kv.shape[0], device=DEV, dtype=torch.float32) / kv.shape[0]
+    kv.copy_((kv.float() * grow[:, None]).to(kv.dtype))
+    k = 1000
+    rng = np.random.default_rng(5)
+    idx = np.full((4, k), -1, dtype=np.int32)
+    idx[0, :40] = np.arange(40)
+    idx[1] = rng.integers(-20, 760, size=k)                       # dups, < 0 and >= len
+    idx[2] = np.sort(rng.choice(3000, size=k, replace=False))
+    idx_dev = torch.from_numpy(idx).to(DEV)
+    rows = dev_rows(wl)
+    out = torch.empty((4, wl.H, wl.D_v), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((4, wl.H), dtype=torch.float32, device=DEV)
+    say(f"many-row attention edges paged={paged}")
+    fn = dsa.sparse_mla_prefill_paged if paged else dsa.sparse_mla_prefill
+    fn(rows, wl.q, wl.kv, idx_dev, wl.scale, wl.D_v, out=out, lse=lse)
+    ref_o, ref_l = oracle_mla(wl, idx, which=[0, 1, 2])
+    o = out.float().cpu().numpy()
+    assert oracle.max_abs_rel(o[:3], ref_o) <= TOL["bf16"]
+    assert oracle.max_abs_rel(lse.cpu().numpy()[:3], ref_l) <= TOL["bf16"]
+    assert np.all(o[3] == 0) and np.all(np.isneginf(lse.cpu().numpy()[3]))
+
+
 def test_prefill_and_decode_entry_points_agree():
     """Many-row (no split) and few-row (split + combine) attention give the same answer."""
     wl = workloads.decode([2500, 4000, 9000], seed=12, device=DEV, name="agree")
