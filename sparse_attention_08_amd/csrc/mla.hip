@@ -241,12 +241,16 @@ __device__ __forceinline__ void wait_younger(int younger) {
 
 // Workgroup -> (row, split).  Workgroups are dealt to the 8 XCDs round-robin by id, so
 // all splits of a row land on one XCD: their query block and partials share its L2.
+// Without a split (many rows, one workgroup each) the rows are taken from the last to the
+// first: in a prefill batch later positions select more entries, so the longest rows start
+// first and the short ones fill the end of the grid.
 struct MlaCoord { int r, split; };
 __device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
   const int x = bid & 7, j = bid >> 3;
   c.r = (j / S) * 8 + x;
   c.split = j % S;
-  return c.r < R;
+  if (S == 1) c.r = R - 1 - c.r;   // the grid holds 8 * ceil(R / 8) >= R workgroups
+  return c.r >= 0 && c.r < R;
 }
 
 // Finishing the row's top-k inside the attention workgroups (see mla_bf16_kernel).
