@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured copy / GEMM ceilings reported beside the peaks")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the 16K-token prefill leg that a decode run also times")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows in the oracle sample")
@@ -94,6 +96,44 @@ def algorithmic_bytes(wl, lens):
     idx_b = sum(per_row_idx + key_b * n for n in lens)
     mla_b = sum(min(n, wl.topk) * wl.D_qk * elt_m + wl.H * (wl.D_qk + wl.D_v) * elt_m for n in lens)
     return idx_b, mla_b
+
+
+def implementation_bytes(wl, lens, mla_ws_bytes: int) -> dict:
+    """Bytes the path moves beyond the algorithmic ones: the score rows (written by the
+    indexer, read by the top-k) and the split partials (written by the attention, read by
+    the merge).  Reported beside the algorithmic bytes, never added to them."""
+    logits = sum(4 * n for n in lens)
+    return {"logits_write_and_read": 2 * logits, "split_partials_write_and_read": 2 * mla_ws_bytes}
+
+
+def device_ceilings(torch, dev) -> dict:
+    """Measured beside the spec peaks (diagnostics only): a 1 GiB device-to-device copy
+    (read + write bytes over its time) and a bf16 8192^3 torch.matmul (library GEMM)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        dst.copy_(src)
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(10):
+        dst.copy_(src)
+    e[1].record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e[2].record()
+    torch.cuda.synchronize()
+    copy_s = e[0].elapsed_time(e[1]) * 1e-3 / 10
+    gemm_s = e[1].elapsed_time(e[2]) * 1e-3 / 10
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return {"copy_1gib_read_plus_write_gbs": 2 * n / copy_s / 1e9,
+            "gemm_bf16_8192_tflops": 2 * 8192 ** 3 / gemm_s / 1e12,
+            "note": "measured ceilings for context; fractions are against the spec peaks"}
 
 
 def algorithmic_flops(wl, lens):
@@ -721,6 +761,9 @@ def main():
                  "stage_ms": {"indexer": idx_mean, "topk": statistics.fmean(topk_ms),
                               "sparse_mla": statistics.fmean(mla_ms)},
                  "step_ms_median": statistics.median(step_ms), "step_ms_min": min(step_ms),
+                 "step_ms_p90": sorted(step_ms)[min(len(step_ms) - 1, int(0.9 * len(step_ms)))],
+                 "implementation_bytes_per_step": implementation_bytes(
+                     wl, lens, 0 if prefill else dsa.sparse_mla_workspace_size(R, wl.H, wl.D_v, wl.topk)),
                  "warm_back_to_back_ms_per_step": warm_ms,
                  "wall_s_timed_loop_incl_flushes": t_wall},
         "cpu_baseline": None,
@@ -729,6 +772,8 @@ def main():
     run = graph = None
     del logits, out, lse, flush, run, graph
     torch.cuda.empty_cache()
+    if not args.no_ceilings:
+        res["device_ceilings"] = device_ceilings(torch, dev)
     if not prefill and not args.no_prefill:
         res["prefill_c3"] = prefill_leg()
     if not args.no_cpu:

@@ -60,3 +60,11 @@ def test_committed_counter_profile_matches_the_kernel_source():
     """The HBM counters under profiles/ were taken on the indexer as it is in the tree (after a
     change to the kernel or the device header, they must be taken again)."""
     assert bench.pmc_traffic("indexer_mfma_kernel", 4) is not None
+
+
+def test_implementation_bytes_are_reported_beside_the_algorithmic_ones():
+    """Score rows are written once and read once (4 bytes a score); split partials likewise."""
+    import types
+    wl = types.SimpleNamespace()
+    d = bench.implementation_bytes(wl, [10, 20], 1000)
+    assert d == {"logits_write_and_read": 2 * 4 * 30, "split_partials_write_and_read": 2000}
