@@ -17,6 +17,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Where query rows find their cache: contiguous (seq_start) or 64-token pages.
+// Grids with one row per block index: the y dimension of a grid holds at most 65535 blocks,
+// so rows beyond it continue in z (grid (x, min(R, 65535), ceil(R / 65535)), launched by
+// row_grid); blocks past the last row return at once.
+__device__ __forceinline__ int grid_row() { return (int)(blockIdx.y + gridDim.y * blockIdx.z); }
+
 struct RowsDev {
   const int32_t *row_seq;
   const int32_t *row_len;

@@ -26,6 +26,14 @@ inline hipError_t ensure_dynamic_lds(Kernel *kernel, int bytes, std::atomic<uint
   return e;
 }
 
+// Grid of x blocks per row for R rows, rows past the 65535 a grid's y dimension holds
+// continuing in z (the kernels recover the row with grid_row()).
+constexpr int kMaxGridY = 65535;
+inline dim3 row_grid(unsigned x, int R) {
+  const unsigned y = R < 1 ? 1u : (R < kMaxGridY ? (unsigned)R : (unsigned)kMaxGridY);
+  return dim3(x, y, R < 1 ? 1u : ((unsigned)R + y - 1) / y);
+}
+
 struct RowsHost {
   int32_t num_rows;
   int32_t num_seqs;

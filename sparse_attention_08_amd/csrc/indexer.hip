@@ -24,13 +24,14 @@ namespace dsa {
 // exactness path (checked at 1e-5 relative) and is not tuned.
 // ------------------------------------------------------------------------------------
 template <bool PAGED>
-__global__ __launch_bounds__(256) void indexer_f32_kernel(RowsDev rows, int H, int D,
+__global__ __launch_bounds__(256) void indexer_f32_kernel(RowsDev rows, int R, int H, int D,
                                                           const float *__restrict__ q,
                                                           const float *__restrict__ k,
                                                           const float *__restrict__ w,
                                                           float *__restrict__ logits, int64_t ld) {
   extern __shared__ float smem[];   // q row [H*D] then w row [H]
-  const int r = blockIdx.y;
+  const int r = grid_row();
+  if (r >= R) return;
   const int len = rows.row_len[r];
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if ((int64_t)blockIdx.x * blockDim.x >= len) return;
@@ -55,7 +56,7 @@ hipError_t launch_indexer_f32(const RowsHost &rh, bool paged, int H, int D, cons
                               const float *k, const float *w, float *logits, int64_t ld,
                               hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
-  dim3 grid((rh.max_row_len + 255) / 256, rh.num_rows);
+  const dim3 grid = row_grid((rh.max_row_len + 255) / 256, rh.num_rows);
   size_t shm = sizeof(float) * ((size_t)H * D + H);
   // the query block and weights of the largest supported shape (64 heads x 256 dims: 65,792
   // bytes) exceed the default 64 KB of dynamic LDS
@@ -65,9 +66,9 @@ hipError_t launch_indexer_f32(const RowsHost &rh, bool paged, int H, int D, cons
                        : ensure_dynamic_lds(&indexer_f32_kernel<false>, kMaxShm, lds_set[0]);
   if (e != hipSuccess) return e;
   if (paged)
-    indexer_f32_kernel<true><<<grid, 256, shm, stream>>>(rows, H, D, q, k, w, logits, ld);
+    indexer_f32_kernel<true><<<grid, 256, shm, stream>>>(rows, rh.num_rows, H, D, q, k, w, logits, ld);
   else
-    indexer_f32_kernel<false><<<grid, 256, shm, stream>>>(rows, H, D, q, k, w, logits, ld);
+    indexer_f32_kernel<false><<<grid, 256, shm, stream>>>(rows, rh.num_rows, H, D, q, k, w, logits, ld);
   return hipGetLastError();
 }
 
@@ -288,7 +289,7 @@ __device__ __forceinline__ float consume_group(const uint8_t *slot,
 // list blockIdx.x of row r.
 template <bool FP8, bool PAGED, bool HIST>
 __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kernel(
-    RowsDev rows, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    RowsDev rows, int R, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, const float *__restrict__ w,
     float *__restrict__ logits, int64_t ld, uint32_t *__restrict__ hcnt,
     uint32_t *__restrict__ hlist, int hstride, int cached) {
@@ -299,7 +300,8 @@ __global__ __launch_bounds__(IdxCfg<FP8>::kWaves * kWave) void indexer_mfma_kern
   uint8_t *smem = idx_smem;
   i32x4 *q_lds = reinterpret_cast<i32x4 *>(smem);
   uint32_t *hist = reinterpret_cast<uint32_t *>(smem + kQChunks * 16 + C::kWaves * C::kDepth * C::kSlotBytes);
-  const int r = blockIdx.y;
+  const int r = grid_row();
+  if (r >= R) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
@@ -433,14 +435,14 @@ size_t indexer_lds_bytes(bool fp8, bool hist) {
 
 template <bool FP8, bool PAGED, bool HIST>
 static hipError_t launch_one(dim3 grid, size_t shm, hipStream_t stream, const RowsDev &rows,
-                             const uint8_t *q8, const float *q_scale, const uint8_t *k8,
+                             int R, const uint8_t *q8, const float *q_scale, const uint8_t *k8,
                              const float *k_scale, const float *w, float *logits, int64_t ld,
                              uint32_t *hcnt, uint32_t *hlist, int hstride, int cached) {
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = ensure_dynamic_lds(&indexer_mfma_kernel<FP8, PAGED, HIST>, (int)shm, lds_set);
   if (e != hipSuccess) return e;
   indexer_mfma_kernel<FP8, PAGED, HIST><<<grid, IdxCfg<FP8>::kWaves * kWave, shm, stream>>>(
-      rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
+      rows, R, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
   return hipGetLastError();
 }
 
@@ -470,16 +472,17 @@ static hipError_t launch_indexer(const RowsHost &rh, bool paged, bool fp8, const
                                  const float *w, float *logits, int64_t ld, uint32_t *hcnt,
                                  uint32_t *hlist, int hstride, hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
-  dim3 grid((unsigned)indexer_blocks_per_row(rh.num_rows, rh.max_row_len, fp8), rh.num_rows);
+  const dim3 grid = row_grid((unsigned)indexer_blocks_per_row(rh.num_rows, rh.max_row_len, fp8),
+                             rh.num_rows);
   const size_t shm = indexer_lds_bytes(fp8, HIST);
   const uint8_t *q8 = static_cast<const uint8_t *>(q);
   const uint8_t *k8 = static_cast<const uint8_t *>(k);
   const int cached = rh.num_rows > rh.num_seqs;   // rows share sequences: keep keys in cache
   if (fp8)
-    return paged ? launch_one<true, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached)
-                 : launch_one<true, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
-  return paged ? launch_one<false, true, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached)
-               : launch_one<false, false, HIST>(grid, shm, stream, rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
+    return paged ? launch_one<true, true, HIST>(grid, shm, stream, rows, rh.num_rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached)
+                 : launch_one<true, false, HIST>(grid, shm, stream, rows, rh.num_rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
+  return paged ? launch_one<false, true, HIST>(grid, shm, stream, rows, rh.num_rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached)
+               : launch_one<false, false, HIST>(grid, shm, stream, rows, rh.num_rows, q8, q_scale, k8, k_scale, w, logits, ld, hcnt, hlist, hstride, cached);
 }
 
 hipError_t launch_indexer_mfma(const RowsHost &rh, bool paged, bool fp8, const void *q,

@@ -29,7 +29,7 @@ namespace dsa {
 // fp32 path: one workgroup per (row, head), two passes over the selected entries.
 // ------------------------------------------------------------------------------------
 template <bool PAGED>
-__global__ __launch_bounds__(256) void mla_f32_kernel(RowsDev rows, int H, int Dqk, int Dv,
+__global__ __launch_bounds__(256) void mla_f32_kernel(RowsDev rows, int R, int H, int Dqk, int Dv,
                                                       float scale, const float *__restrict__ q,
                                                       const float *__restrict__ kv,
                                                       const int32_t *__restrict__ idx, int k,
@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(RowsDev rows, int H, int D
   float *qs = reinterpret_cast<float *>(crow + k);        // [Dqk]
   __shared__ float red[256 / kWave];
   __shared__ float bcast;
-  const int h = blockIdx.x, r = blockIdx.y;
+  const int h = blockIdx.x, r = grid_row();
+  if (r >= R) return;
   const int len = rows.row_len[r], b = rows.row_seq[r];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int d = threadIdx.x; d < Dqk; d += blockDim.x) qs[d] = q[((int64_t)r * H + h) * Dqk + d];
@@ -104,13 +105,13 @@ hipError_t launch_mla_f32(const RowsHost &rh, bool paged, int H, int Dqk, int Dv
                           const float *q, const float *kv, const int32_t *idx, int k, float *out,
                           float *lse, hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
-  dim3 grid(H, rh.num_rows);
+  const dim3 grid = row_grid(H, rh.num_rows);
   const size_t shm = sizeof(float) * ((k + 1) & ~1) + sizeof(int64_t) * k + sizeof(float) * Dqk;
   if (paged)
-    mla_f32_kernel<true><<<grid, 256, shm, stream>>>(rows, H, Dqk, Dv, scale, q, kv, idx, k, out,
+    mla_f32_kernel<true><<<grid, 256, shm, stream>>>(rows, rh.num_rows, H, Dqk, Dv, scale, q, kv, idx, k, out,
                                                      lse);
   else
-    mla_f32_kernel<false><<<grid, 256, shm, stream>>>(rows, H, Dqk, Dv, scale, q, kv, idx, k, out,
+    mla_f32_kernel<false><<<grid, 256, shm, stream>>>(rows, rh.num_rows, H, Dqk, Dv, scale, q, kv, idx, k, out,
                                                       lse);
   return hipGetLastError();
 }

@@ -541,6 +541,63 @@ def test_mla_skips_invalid_and_empty_selections():
     assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
 
 
+def test_rows_beyond_the_grid_y_limit():
+    """More query rows (70,000) than one grid dimension holds (65,535 blocks): the indexer
+    that gives every row its own blocks (fp8 and f32) and the f32 attention continue the rows
+    in the grid's third dimension.  Rows share one 256-token sequence, row r sees
+    1 + (r % 256) positions; rows on both sides of the limit are checked."""
+    R, L = 70000, 256
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77)
+    row_seq = torch.zeros(R, dtype=torch.int32, device=DEV)
+    row_len = (torch.arange(R, device=DEV, dtype=torch.int32) % L) + 1
+    seq_start = torch.zeros(1, dtype=torch.int64, device=DEV)
+    rows = dsa.Rows(row_seq, row_len, L, 1, seq_start=seq_start)
+    lens = row_len.cpu().numpy()
+    orows = oracle.Rows(np.zeros(R, np.int32), lens, seq_start=np.zeros(1, np.int64))
+    which = [0, 1, 65534, 65535, 65536, 69999]
+
+    say("fp8 indexer, 70000 rows")
+    q8, qs = workloads.quantize_e4m3(torch.randn((R, 64, 128), generator=gen, device=DEV), 1)
+    qs = qs[:, None].expand(R, 64).contiguous()
+    k8, ks = workloads.quantize_e4m3(torch.randn((L, 128), generator=gen, device=DEV), 1)
+    w = torch.rand((R, 64), generator=gen, device=DEV) / 8
+    logits = torch.full((R, L), float("nan"), device=DEV)
+    dsa.indexer_logits(rows, q8, w, k8, logits, q_scale=qs, k_scale=ks)
+    ref = oracle.indexer("fp8", raw(q8), raw(w), raw(k8), orows, q_scale=raw(qs),
+                         k_scale=raw(ks), which=which, ld=L)
+    got = logits.cpu().numpy()[which]
+    assert oracle.max_abs_rel(valid_logits(got, lens, which),
+                              valid_logits(ref, lens, which)) <= TOL["fp8"]
+    del q8, qs, logits
+
+    say("f32 indexer, 70000 rows")
+    qf = torch.randn((R, 4, 32), generator=gen, device=DEV)
+    kf = torch.randn((L, 32), generator=gen, device=DEV)
+    wf = torch.rand((R, 4), generator=gen, device=DEV)
+    logits = torch.full((R, L), float("nan"), device=DEV)
+    dsa.indexer_logits(rows, qf, wf, kf, logits)
+    ref = oracle.indexer("f32", raw(qf), raw(wf), raw(kf), orows, which=which, ld=L)
+    got = logits.cpu().numpy()[which]
+    assert oracle.max_abs_rel(valid_logits(got, lens, which),
+                              valid_logits(ref, lens, which)) <= TOL["f32"]
+
+    say("f32 attention, 70000 rows")
+    k = 16
+    q = torch.randn((R, 8, 80), generator=gen, device=DEV)
+    kv = torch.randn((L, 80), generator=gen, device=DEV)
+    j = torch.arange(k, device=DEV, dtype=torch.int32)
+    idx = torch.where(j[None, :] < row_len[:, None], (row_len[:, None] - 1 - j[None, :]) % L,
+                      torch.full_like(j[None, :], -1)).to(torch.int32).contiguous()
+    out = torch.empty((R, 8, 64), device=DEV)
+    lse = torch.empty((R, 8), device=DEV)
+    dsa.sparse_mla_decode(rows, q, kv, idx, 80 ** -0.5, 64, out=out, lse=lse)
+    ref_o, ref_l = oracle.sparse_mla("f32", raw(q), raw(kv), idx.cpu().numpy(), orows,
+                                     80 ** -0.5, 64, which=which)
+    assert oracle.max_abs_rel(out.cpu().numpy()[which], ref_o) <= TOL["f32"]
+    assert oracle.max_abs_rel(lse.cpu().numpy()[which], ref_l) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_many_row_attention_edges(paged):
     """The no-split attention (one workgroup per row): a short row whose valid slots are
