@@ -167,13 +167,27 @@ def summarize_trace(out_name: str, stats_csv: str, command: str):
     """profiles/<out_name>.md: the dsa kernels of a rocprofv3 --kernel-trace --stats run."""
     import csv
     rows = [r for r in csv.DictReader(open(stats_csv)) if "dsa::" in r["Name"]]
+    # medians per kernel from the per-dispatch trace beside the stats file, when it is there
+    # (a kernel's first launch can take several times its steady-state duration)
+    med = {}
+    trace_csv = os.path.join(os.path.dirname(stats_csv),
+                             os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    if trace_csv != stats_csv and os.path.exists(trace_csv):
+        durs = {}
+        for t in csv.DictReader(open(trace_csv)):
+            if "dsa::" in t["Kernel_Name"]:
+                durs.setdefault(t["Kernel_Name"], []).append(
+                    (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3)
+        med = {k: statistics.median(v) for k, v in durs.items()}
     lines = [f"# {out_name}", "", "Command (from the repository root, on one MI355X):", "",
              "```", command, "```", "",
-             "| kernel | calls | avg us | min us | max us | share of dsa time |",
-             "|---|---:|---:|---:|---:|---:|"]
+             "| kernel | calls | avg us | median us | min us | max us | share of dsa time |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        m = med.get(r["Name"])
         lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{'-' if m is None else f'{m:.2f}'} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / total:.1%} |")
     os.makedirs(PROFILES, exist_ok=True)
