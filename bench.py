@@ -108,7 +108,18 @@ def implementation_bytes(wl, lens, mla_ws_bytes: int) -> dict:
 
 def device_ceilings(torch, dev) -> dict:
     """Measured beside the spec peaks (diagnostics only): a 1 GiB device-to-device copy
-    (read + write bytes over its time) and a bf16 8192^3 torch.matmul (library GEMM)."""
+    (read + write bytes over its time), a bf16 8192^3 torch.matmul (library GEMM) and the
+    library's MFMA-loop probe (back-to-back independent bf16 MFMAs on every SIMD: the matrix
+    cores' rate at the clock the chip holds under that load)."""
+    import sparse_attention_08_amd as dsa
+    iters = 20000
+    probe = dsa.mfma_rate_probe(1000)
+    p0 = torch.cuda.Event(enable_timing=True); p1 = torch.cuda.Event(enable_timing=True)
+    p0.record()
+    dsa.mfma_rate_probe(iters, probe)
+    p1.record()
+    torch.cuda.synchronize()
+    mfma_tflops = dsa.MFMA_PROBE_WAVES * iters * 8 * 16384 / (p0.elapsed_time(p1) * 1e-3) / 1e12
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -133,6 +144,7 @@ def device_ceilings(torch, dev) -> dict:
     torch.cuda.empty_cache()
     return {"copy_1gib_read_plus_write_gbs": 2 * n / copy_s / 1e9,
             "gemm_bf16_8192_tflops": 2 * 8192 ** 3 / gemm_s / 1e12,
+            "mfma_loop_bf16_tflops": mfma_tflops,
             "note": "measured ceilings for context; fractions are against the spec peaks"}
 
 

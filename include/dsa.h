@@ -364,6 +364,17 @@ int dsa_prep(int num_tokens, const int32_t *positions, const int64_t *cache_rows
              void *kv_cache, const void *q_idx_in, void *q_idx, float *q_idx_scale, int n_heads,
              void *q, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Measurement aid (not a step of the method): the bf16 matrix-core rate the GPU sustains.
+ * 512 workgroups of 4 waves (two per SIMD on every CU) each run `iters` rounds of 8
+ * independent v_mfma_f32_16x16x32_bf16 on register operands; each wave writes one sum to
+ * out[wave] so the work is kept.  Useful work: 2048 waves x iters x 8 x 16,384 flops; time
+ * it with events on `stream` for the achievable bf16 MFMA rate at the clock the chip holds
+ * under that load, to set beside the published peak.
+ * out: device, DSA_MFMA_PROBE_WAVES floats.  iters: 1 .. 1,000,000, else DSA_ERR_INVALID_ARG. */
+#define DSA_MFMA_PROBE_WAVES 2048
+int dsa_mfma_rate_probe(int iters, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 PAGE_SIZE = 64
 MAX_TOPK = 2048
+MFMA_PROBE_WAVES = 2048      # DSA_MFMA_PROBE_WAVES
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
           4: "DSA_ERR_HIP"}
 
@@ -53,6 +54,8 @@ def load_library() -> ctypes.CDLL:
     rows_p = ctypes.POINTER(DsaRows)
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_mfma_rate_probe.argtypes = [i32, vp, vp]
+    lib.dsa_mfma_rate_probe.restype = i32
     lib.dsa_abi_version.argtypes = []
     lib.dsa_abi_version.restype = i32
     for name in ("dsa_indexer_logits", "dsa_indexer_logits_paged"):
@@ -111,6 +114,18 @@ def load_library() -> ctypes.CDLL:
         f.restype = i32
     _lib = lib
     return lib
+
+
+def mfma_rate_probe(iters: int, out=None):
+    """Measurement aid: launch dsa_mfma_rate_probe (2048 waves x iters x 8 bf16 MFMAs of
+    16x16x32) on the current stream; returns the [2048] output it writes (time it with events)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(MFMA_PROBE_WAVES, dtype=torch.float32, device="cuda")
+    _dev(out, "out", (torch.float32,))
+    _shape(out, "out", (MFMA_PROBE_WAVES,))
+    _check(lib.dsa_mfma_rate_probe(int(iters), _ptr(out), _stream()), "dsa_mfma_rate_probe")
+    return out
 
 
 def abi_version() -> int:

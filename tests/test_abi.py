@@ -294,3 +294,11 @@ def test_noalloc_decode_rejects_batches_beyond_its_scratch(lib):
     assert lib.dsa_sparse_attention_decode_noalloc(None, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
                                                    FAKE, 100, 64, FAKE, 1, 128, 576, 512, 0.1,
                                                    FAKE, FAKE, FAKE, None, None) == INVALID
+
+
+def test_mfma_probe_validation(lib):
+    """The matrix-core rate probe rejects a loop count outside 1 .. 1,000,000 and a null
+    output before launching anything."""
+    for iters in (0, -5, 1000001):
+        assert lib.dsa_mfma_rate_probe(iters, FAKE, None) == INVALID
+    assert lib.dsa_mfma_rate_probe(10, None, None) == INVALID

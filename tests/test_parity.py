@@ -541,6 +541,19 @@ def test_mla_skips_invalid_and_empty_selections():
     assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
 
 
+def test_mfma_rate_probe_writes_every_wave():
+    """The matrix-core rate probe (a measurement aid): every one of its waves writes a finite
+    sum, and the sum grows with the loop count (the products are not folded away)."""
+    say("mfma probe")
+    out = torch.full((dsa.MFMA_PROBE_WAVES,), float("nan"), device=DEV)
+    dsa.mfma_rate_probe(4, out)
+    a = out.cpu().numpy()
+    assert np.all(np.isfinite(a))
+    dsa.mfma_rate_probe(8, out)
+    b = out.cpu().numpy()
+    assert np.allclose(b, 2 * a, rtol=1e-5, atol=1e-6) and np.abs(a).max() > 0
+
+
 def test_rows_beyond_the_grid_y_limit():
     """More query rows (70,000) than one grid dimension holds (65,535 blocks): the indexer
     that gives every row its own blocks (fp8 and f32) and the f32 attention continue the rows
