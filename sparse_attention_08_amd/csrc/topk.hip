@@ -37,18 +37,23 @@ constexpr int kFinalThreads = DSA_TOPK_FINAL_THREADS;   // >= kMaxChunks
 static_assert(kFinalThreads >= 256 && (1 << 10) % kFinalThreads == 0, "final select shape");
 constexpr int kMbThreads = 256;
 constexpr int kStageElems = 28672;         // single-row schedule: up to 112 KB of staged keys
+static_assert(kStageElems < 65536, "the staged schedule counts its histogram bins in 16 bits");
 
 // ------------------------------------------------------------------------------------
 // many-row schedule: one workgroup per row
 // ------------------------------------------------------------------------------------
+// Rows are taken from the last to the first: in a prefill batch later positions have
+// longer rows, so the longest start first and the short ones fill the end of the grid.
+// The staged form counts its histogram bins in 16 bits (rows of fewer than 65536 scores),
+// so that with rows of up to 16K scores two workgroups share a CU's LDS.
 template <bool STAGED>
 __global__ __launch_bounds__(kSmallThreads) void topk_row_kernel(const float *__restrict__ logits,
                                                                  int64_t ld,
                                                                  const int32_t *__restrict__ row_len,
                                                                  int k, int32_t *__restrict__ idx) {
   extern __shared__ uint32_t staged[];
-  __shared__ BlockScratch<kSmallThreads> sh;
-  const int r = blockIdx.x;
+  __shared__ BlockScratch<kSmallThreads, STAGED> sh;
+  const int r = (int)(gridDim.x - 1 - blockIdx.x);
   const int n = row_len[r];
   const float *row = logits + (int64_t)r * ld;
   int32_t *out = idx + (int64_t)r * k;
@@ -57,9 +62,36 @@ __global__ __launch_bounds__(kSmallThreads) void topk_row_kernel(const float *__
     return;
   }
   if constexpr (STAGED) {
-    for (int i = threadIdx.x; i < n; i += kSmallThreads) staged[i] = order_key(row[i]);
+    // the first digit's histogram is counted while the row is staged; every load of a
+    // round is issued before any is used
+    constexpr int kU = 16;
+    for (int i = threadIdx.x; i < kBins / 2; i += kSmallThreads) sh.hist[i] = 0;
+    if (threadIdx.x == 0) {
+      sh.prefix = 0;
+      sh.mask = 0;
+      sh.need = k;
+    }
     __syncthreads();
-    select_block<kSmallThreads>(StagedAcc{staged}, n, k, out, sh);
+    for (int i0 = threadIdx.x; i0 < n; i0 += kU * kSmallThreads) {
+      float v[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int i = i0 + q * kSmallThreads;
+        v[q] = i < n ? row[i] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int i = i0 + q * kSmallThreads;
+        if (i < n) {
+          const uint32_t u = order_key(v[q]), d = u >> (kD1Bits + kD2Bits);
+          staged[i] = u;
+          atomicAdd(&sh.hist[d >> 1], 1u << (16 * (d & 1)));
+        }
+      }
+    }
+    __syncthreads();
+    radix_resolve<kSmallThreads, kD0Bits>(kD1Bits + kD2Bits, sh);
+    select_after_first_digit<kSmallThreads>(StagedAcc{staged}, n, out, sh);
   } else {
     select_block<kSmallThreads>(RowAcc{row}, n, k, out, sh);
   }

@@ -22,9 +22,11 @@ constexpr int kSurvLoads = 8192;           // survivors per workgroup loaded wit
 // ------------------------------------------------------------------------------------
 // block-wide helpers
 // ------------------------------------------------------------------------------------
-template <int NT>
+// P16: two 16-bit bin counts per word (every count stays below 65536, i.e. fewer than
+// 65536 keys), which halves the histogram's LDS.
+template <int NT, bool P16 = false>
 struct BlockScratch {
-  uint32_t hist[kBins];
+  uint32_t hist[P16 ? kBins / 2 : kBins];
   uint32_t wsum[NT / kWave];
   uint32_t wcnt[2][NT / kWave];
   uint32_t prefix, mask;
@@ -33,9 +35,9 @@ struct BlockScratch {
 };
 
 // Exclusive prefix sum over the block's threads of v; returns it and the block total.
-template <int NT>
+template <int NT, bool P16>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
-                                                    BlockScratch<NT> &sh) {
+                                                    BlockScratch<NT, P16> &sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t inc = wave_incl_scan(v);
   if (lane == 63) sh.wsum[wave] = inc;
@@ -52,32 +54,22 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
   return before + inc - v;
 }
 
-// One radix digit: histogram of digit (key >> shift) & (2^BITS - 1) over the keys that
-// match (key & mask) == prefix, then the digit holding the need-th largest key.
-template <int NT, int BITS, class Acc>
-__device__ void radix_digit(const Acc &acc, int n, int shift, BlockScratch<NT> &sh) {
+// The digit holding the need-th largest key among those matching (key & mask) == prefix,
+// from a histogram of the digit (key >> shift) & (2^BITS - 1) already counted in sh.hist;
+// updates prefix, mask and need.
+template <int NT, int BITS, bool P16>
+__device__ void radix_resolve(int shift, BlockScratch<NT, P16> &sh) {
   constexpr int NB = 1 << BITS;
   constexpr int PER = NB / NT;             // consecutive bins owned per thread
   static_assert(NB % NT == 0, "bins must split evenly");
-  for (int i = threadIdx.x; i < NB; i += NT) sh.hist[i] = 0;
-  __syncthreads();
   const uint32_t prefix = sh.prefix, mask = sh.mask;
-  // four keys a thread per round, their reads issued together
-  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
-    uint32_t u[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) u[q] = i0 + q * NT < n ? acc.key(i0 + q * NT) : 0u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (i0 + q * NT < n && (u[q] & mask) == prefix)
-        atomicAdd(&sh.hist[(u[q] >> shift) & (NB - 1)], 1u);
-  }
-  __syncthreads();
   // thread t owns bins NB-1-PER*t-j (j < PER): descending digit order across threads
   uint32_t c[PER], tot = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    c[j] = sh.hist[NB - 1 - PER * threadIdx.x - j];
+    const int b = NB - 1 - PER * threadIdx.x - j;
+    if constexpr (P16) c[j] = (sh.hist[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
+    else c[j] = sh.hist[b];
     tot += c[j];
   }
   uint32_t all;
@@ -101,27 +93,37 @@ __device__ void radix_digit(const Acc &acc, int n, int shift, BlockScratch<NT> &
   __syncthreads();
 }
 
-// Exact top-k of n keys given by acc (key(i), pos(i); items in ascending position
-// order), written to out[0..k) in ascending position order.  Requires n > k.
-// When first_digit >= 0 the caller already knows the 12-bit digit of T and that
-// `need_in_digit` keys with that digit belong to the result.
-template <int NT, class Acc>
-__device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__ out,
-                             BlockScratch<NT> &sh, int first_digit = -1, int need_in_digit = 0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (threadIdx.x == 0) {
-    if (first_digit >= 0) {
-      sh.prefix = (uint32_t)first_digit << (kD1Bits + kD2Bits);
-      sh.mask = (uint32_t)(kBins - 1) << (kD1Bits + kD2Bits);
-      sh.need = need_in_digit;
-    } else {
-      sh.prefix = 0;
-      sh.mask = 0;
-      sh.need = k;
-    }
+// One radix digit: histogram of digit (key >> shift) & (2^BITS - 1) over the keys that
+// match (key & mask) == prefix, then the digit holding the need-th largest key.
+template <int NT, int BITS, bool P16, class Acc>
+__device__ void radix_digit(const Acc &acc, int n, int shift, BlockScratch<NT, P16> &sh) {
+  constexpr int NB = 1 << BITS;
+  constexpr int NW = P16 ? NB / 2 : NB;    // histogram words
+  for (int i = threadIdx.x; i < NW; i += NT) sh.hist[i] = 0;
+  __syncthreads();
+  const uint32_t prefix = sh.prefix, mask = sh.mask;
+  // four keys a thread per round, their reads issued together
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {
+    uint32_t u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = i0 + q * NT < n ? acc.key(i0 + q * NT) : 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (i0 + q * NT < n && (u[q] & mask) == prefix) {
+        const uint32_t d = (u[q] >> shift) & (NB - 1);
+        if constexpr (P16) atomicAdd(&sh.hist[d >> 1], 1u << (16 * (d & 1)));
+        else atomicAdd(&sh.hist[d], 1u);
+      }
   }
   __syncthreads();
-  if (first_digit < 0) radix_digit<NT, kD0Bits>(acc, n, kD1Bits + kD2Bits, sh);
+  radix_resolve<NT, BITS>(shift, sh);
+}
+
+// The rest of select_block once sh holds the prefix, mask and need after the first digit.
+template <int NT, bool P16, class Acc>
+__device__ void select_after_first_digit(const Acc &acc, int n, int32_t *__restrict__ out,
+                                         BlockScratch<NT, P16> &sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   radix_digit<NT, kD1Bits>(acc, n, kD2Bits, sh);
   radix_digit<NT, kD2Bits>(acc, n, 0, sh);
   const uint32_t T = sh.prefix;
@@ -180,6 +182,31 @@ __device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__
       sel_before += __popcll(sel_mask);
     }
   }
+}
+
+// Exact top-k of n keys given by acc (key(i), pos(i); items in ascending position
+// order), written to out[0..k) in ascending position order.  Requires n > k, and
+// n < 65536 with a 16-bit histogram (P16).
+// When first_digit >= 0 the caller already knows the 12-bit digit of T and that
+// `need_in_digit` keys with that digit belong to the result.
+template <int NT, bool P16, class Acc>
+__device__ void select_block(const Acc &acc, int n, int k, int32_t *__restrict__ out,
+                             BlockScratch<NT, P16> &sh, int first_digit = -1,
+                             int need_in_digit = 0) {
+  if (threadIdx.x == 0) {
+    if (first_digit >= 0) {
+      sh.prefix = (uint32_t)first_digit << (kD1Bits + kD2Bits);
+      sh.mask = (uint32_t)(kBins - 1) << (kD1Bits + kD2Bits);
+      sh.need = need_in_digit;
+    } else {
+      sh.prefix = 0;
+      sh.mask = 0;
+      sh.need = k;
+    }
+  }
+  __syncthreads();
+  if (first_digit < 0) radix_digit<NT, kD0Bits>(acc, n, kD1Bits + kD2Bits, sh);
+  select_after_first_digit<NT>(acc, n, out, sh);
 }
 
 struct RowAcc {            // keys computed on the fly from a score row in global memory

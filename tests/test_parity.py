@@ -512,6 +512,16 @@ def test_topk_edge_cases():
         rows[5] = rng.standard_normal(n)
         _topk_case(rows, [n, n, n, 5000, 30000, 1], k)
         _topk_case(rows[:, :3000], [3000, 2048, 2049, 1, 17, 3000], k)
+    # the longest rows staged in LDS, whose histogram counts bins in 16 bits: one bin holding
+    # every key, and two neighbouring bins that share one histogram word
+    n = 28672
+    rows = np.zeros((4, n), dtype=np.float32)
+    rows[0] = 3.5
+    rows[1] = np.where(np.arange(n) % 2 == 0, 1.0, 1.125)
+    rows[2] = rng.standard_normal(n)
+    rows[3] = rng.integers(-3, 4, size=n)
+    for k in (7, 2048):
+        _topk_case(rows, [n, n, 16384, 20000], k)
     # rows up to 2^18 scores are selected by one workgroup each; longer ones take the chunked
     # filter and a final workgroup
     n = 300000
