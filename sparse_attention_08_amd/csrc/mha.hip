@@ -492,7 +492,7 @@ hipError_t launch_mha_prefill(const RowsHost &rh, bool paged, int H, float scale
       idx ? reinterpret_cast<uint32_t *>(wsb + reach_bytes + 2 * dec_bytes) : nullptr;
   const int mask_words = (L + 31) / 32;
   mha_reach_kernel<<<B, 256, 0, stream>>>(rh.row_seq, rh.row_len, rh.num_rows, reach);
-  const dim3 dgrid((unsigned)H, (unsigned)(((int64_t)B * L + kGemmTile - 1) / kGemmTile), 2);
+  const dim3 dgrid((unsigned)H, (unsigned)(((int64_t)B * L + kGemmTileM - 1) / kGemmTileM), 2);
   const auto *kv16 = static_cast<const uint16_t *>(kv);
   const auto *wk = static_cast<const uint16_t *>(w_uk);
   const auto *wv = static_cast<const uint16_t *>(w_uv);

@@ -90,7 +90,7 @@ hipError_t launch_absorb_query(int R, int H, const void *q, const void *w_uk,
   const int64_t pairs = (int64_t)R * H;
   copy_rope_kernel<<<(unsigned)((pairs * 8 + 255) / 256), 256, 0, stream>>>(q16, b.q_abs, pairs);
   const AbsorbProb pr{R, 512, 128, H, q16, b.wuk_t, b.q_abs};
-  gemm_nt_kernel<<<dim3(512 / kGemmTile, (R + kGemmTile - 1) / kGemmTile, H), kGemmThreads, 0,
+  gemm_nt_kernel<<<dim3(512 / kGemmTile, (R + kGemmTileM - 1) / kGemmTileM, H), kGemmThreads, 0,
                    stream>>>(pr);
   return hipGetLastError();
 }
@@ -99,7 +99,7 @@ hipError_t launch_expand_output(int R, int H, const uint16_t *o_lat, const void 
                                 hipStream_t stream) {
   const ExpandProb pr{R, 128, 512, H, o_lat, static_cast<const uint16_t *>(w_uv),
                       static_cast<uint16_t *>(out)};
-  gemm_nt_kernel<<<dim3(1, (R + kGemmTile - 1) / kGemmTile, H), kGemmThreads, 0, stream>>>(pr);
+  gemm_nt_kernel<<<dim3(1, (R + kGemmTileM - 1) / kGemmTileM, H), kGemmThreads, 0, stream>>>(pr);
   return hipGetLastError();
 }
 
