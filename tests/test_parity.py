@@ -425,6 +425,22 @@ def test_attention_decode_other_schedules_and_full_size():
         torch.cuda.empty_cache()
 
 
+def test_decode_at_the_longest_chunked_row():
+    """A row of 2^20 positions, the longest the chunked top-k schedule takes (256 chunks of
+    4096 scores), beside a mid-length row, through the one-call decode (fused indexer with
+    histograms, chunk filter, selecting attention, combine): every stage against the oracle."""
+    wl = workloads.decode([1 << 20, 70001], idx_dtype="fp8", seed=97, device=DEV, name="decode_1m")
+    say("fused decode, a 2^20-position row")
+    g, idx = _attention_decode_vs_separate(wl)
+    lens = wl.row_len.cpu().numpy()
+    exp = oracle.topk(np.nan_to_num(g.cpu().numpy(), nan=0.0).astype(np.float32), lens, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), exp)
+    _check_indexer(wl, [0, 1], TOL["fp8"])
+    _check_mla(wl, idx, [0, 1], TOL["bf16"])
+    del wl
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------------ full-size configs
 
 def selection_recall(idx_gpu, ref_scores, lens, k):
