@@ -425,6 +425,21 @@ def test_attention_decode_other_schedules_and_full_size():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("k,idx_dtype", [(1, "bf16"), (100, "fp8"), (700, "bf16")])
+def test_attention_decode_other_topk_sizes(k, idx_dtype):
+    """k below 2048 through the one-call decode: one split of one slot (k = 1), one split of a
+    partial tile (k = 100), six splits with a short last one (k = 700); rows shorter than k,
+    longer than k, and long enough for the chunked schedule."""
+    wl = workloads.decode([1, 150, 9000, 40961, 70000], idx_dtype=idx_dtype, topk=k, seed=98 + k,
+                          device=DEV, name=f"decode_k{k}_{idx_dtype}")
+    say(f"fused decode k={k} {idx_dtype}")
+    g, idx = _attention_decode_vs_separate(wl)
+    lens = wl.row_len.cpu().numpy()
+    exp = oracle.topk(np.nan_to_num(g.cpu().numpy(), nan=0.0).astype(np.float32), lens, k)
+    assert np.array_equal(idx.cpu().numpy(), exp)
+    _check_mla(wl, idx, [0, 1, 2, 4], TOL["bf16"])
+
+
 def test_decode_at_the_longest_chunked_row():
     """A row of 2^20 positions, the longest the chunked top-k schedule takes (256 chunks of
     4096 scores), beside a mid-length row, through the one-call decode (fused indexer with
