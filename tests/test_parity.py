@@ -505,6 +505,26 @@ def test_c3_prefill_16k_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
+def test_prefill_other_topk_size(idx_dtype):
+    """A 3000-token prefill with k = 300: rows below, at and above k; the fused indexer + top-k
+    call against separate calls bit for bit, every row's selection against the oracle on the
+    kernel's scores, sampled rows of the indexer and the attention against the oracle."""
+    wl = workloads.prefill(3000, idx_dtype=idx_dtype, topk=300, seed=110, device=DEV,
+                           name=f"prefill_k300_{idx_dtype}")
+    say(f"prefill k=300 {idx_dtype}")
+    which = [0, 1, 298, 299, 300, 301, 1500, 2999]
+    g, ref, _ = _check_indexer(wl, which, TOL[idx_dtype])
+    _check_topk_on_oracle_scores(wl, ref, which)
+    idx = _check_topk_on_gpu_scores(wl, g.copy())
+    rows = dev_rows(wl)
+    logits = torch.full((wl.num_rows, wl.max_row_len), float("nan"), dtype=torch.float32, device=DEV)
+    idx_f = dsa.indexer_topk(rows, wl.q_idx, wl.w, wl.k_idx, logits, wl.topk, q_scale=wl.q_scale,
+                             k_scale=wl.k_scale)
+    assert torch.equal(idx_f, idx)
+    _check_mla(wl, idx, which, TOL["bf16"])
+
+
 # ------------------------------------------------------------------------ determinism, edges
 
 def test_two_runs_bitwise_equal():
