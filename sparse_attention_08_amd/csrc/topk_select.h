@@ -17,7 +17,10 @@ constexpr int kChunk = 4096;               // scores per workgroup in the few-ro
 constexpr int kSurvivorCap = 10240;        // survivors selected in LDS (80 KB)
 constexpr int kMaxChunks = 256;            // chunked schedule handles rows up to 1M scores
 constexpr int kListHead = 8;               // histogram entries per thread loaded with the counts
-constexpr int kSurvLoads = 8192;           // survivors per workgroup loaded with the chunk counts
+#ifndef DSA_SURV_LOADS
+#define DSA_SURV_LOADS 8192
+#endif
+constexpr int kSurvLoads = DSA_SURV_LOADS;  // survivors per workgroup loaded with the chunk counts
 
 // ------------------------------------------------------------------------------------
 // block-wide helpers
