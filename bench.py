@@ -733,44 +733,56 @@ def main():
     # serving loop the step is one layer's share of a model-wide graph, whose launch latency
     # (~10 us here) is paid once per forward pass; every kernel of the step and every boundary
     # between them stays in the difference, and the caches are cold at each step's start.
-    marginal = None
+    marginal = idx_marginal = None
     if mode == "hip_graph" and flush is not None:
         rows_view = flush.view(-1, 4096)
 
         def flush_op():   # reads the 1 GiB (a per-row reduction: no memset node in the graph)
             return rows_view.amax(dim=1)
 
+        def in_sequence(fn, unchanged):
+            """Per batch, the ms of fn inside a captured sequence after the flush: K replays of
+            a graph [flush, fn] minus K replays of a graph [flush]; unchanged() checks, after
+            every batch, that the replays left fn's results as the standalone launches did."""
+            g_flush, g_both = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_flush):
+                flush_op()
+            with torch.cuda.graph(g_both):
+                flush_op()
+                fn()
+            g_flush.replay(); g_both.replay()
+            torch.cuda.synchronize()
+            batches = max(1, min(5, args.steps // 10))
+            per = max(1, args.steps // batches)
+            res = []
+            for _ in range(batches):
+                tt = []
+                for g in (g_flush, g_both):
+                    x0 = torch.cuda.Event(enable_timing=True); x1 = torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    x0.record()
+                    for _ in range(per):
+                        g.replay()
+                    x1.record()
+                    torch.cuda.synchronize()
+                    tt.append(x0.elapsed_time(x1) / per)
+                res.append(tt[1] - tt[0])
+                if not unchanged():
+                    raise SystemExit("a launch replayed inside the flush graph changed its results")
+            return res
+
         ref_idx, ref_out = idx.clone(), out.clone()   # the standalone launches' results
-        g_flush, g_both = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_flush):
-            flush_op()
-        with torch.cuda.graph(g_both):
-            flush_op()
-            step()
-        g_flush.replay(); g_both.replay()
-        torch.cuda.synchronize()
-        batches = max(1, min(5, args.steps // 10))
-        per = max(1, args.steps // batches)
-        marginal = []
-        for _ in range(batches):
-            tt = []
-            for g in (g_flush, g_both):
-                x0 = torch.cuda.Event(enable_timing=True); x1 = torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                x0.record()
-                for _ in range(per):
-                    g.replay()
-                x1.record()
-                torch.cuda.synchronize()
-                tt.append(x0.elapsed_time(x1) / per)
-            marginal.append(tt[1] - tt[0])
-            # every batch of replays leaves the step's results as the standalone launches did
-            if not (torch.equal(idx, ref_idx) and torch.equal(out, ref_out)):
-                raise SystemExit("the step replayed inside the flush graph changed its results")
-        del g_flush, g_both, ref_idx, ref_out
+        marginal = in_sequence(step, lambda: torch.equal(idx, ref_idx) and torch.equal(out, ref_out))
+        del ref_idx, ref_out
         standalone_mean = mean
         mean = statistics.fmean(marginal)
         timing = "in a captured sequence (flush + step graph minus flush graph)"
+        if not prefill:
+            # the roofline's kernel the same way: the scores-only indexer launch
+            ref_logits = torch.nan_to_num(logits, nan=-1.0)
+            idx_marginal = in_sequence(
+                stage_indexer, lambda: torch.equal(torch.nan_to_num(logits, nan=-1.0), ref_logits))
+            del ref_logits
 
     # back-to-back steps with warm caches, for reference
     torch.cuda.synchronize()
@@ -793,14 +805,19 @@ def main():
         roof["traffic"] = None
         roof["kernel"] = "whole path (indexer + top-k + sparse MLA), algorithmic flops"
     else:
-        achieved = idx_b / (idx_mean * 1e-3) / 1e9
+        idx_ms_used = statistics.fmean(idx_marginal) if idx_marginal else idx_mean
+        achieved = idx_b / (idx_ms_used * 1e-3) / 1e9
         path_gbs = (idx_b + mla_b) / (mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic("indexer_mfma_kernel", args.config),
                 "kernel": "indexer_mfma_kernel",
-                "kernel_timed": "the scores-only launch (dsa_indexer_logits, event-bracketed "
-                                "eager call); the one-call decode step runs the instantiation "
-                                "that also builds the top-k's first-digit histograms",
+                "kernel_timed": ("the scores-only launch (dsa_indexer_logits) " +
+                                 ("inside a captured sequence after the cache flush, like the step"
+                                  if idx_marginal else "event-bracketed, eager") +
+                                 "; the one-call decode step runs the instantiation that also "
+                                 "builds the top-k's first-digit histograms"),
+                "kernel_ms": idx_ms_used,
+                "kernel_ms_event_bracketed_eager": idx_mean,
                 "algorithmic_bytes_per_launch": idx_b,
                 # the metric itself: indexer + top-k + sparse-MLA bytes over the whole step
                 "path_achieved": path_gbs, "path_frac": path_gbs / HBM_PEAK_GBS,
