@@ -15,8 +15,8 @@ the step and every boundary between them, without the latency of a graph launch 
 (a serving loop pays that once per model-wide graph).  The same step launched as a graph of
 its own per step, HIP events on the launch stream around each launch, is reported beside it
 (path.standalone_launch_ms_per_step).  --no-graph: eager launches, events around each step.
-An eager pass with events between separate stage calls gives the per-stage attribution and
-the indexer's roofline.  value = rows (tokens) / mean step time.  roofline.path_frac is the metric's own
+An eager pass with events between separate stage calls gives the per-stage attribution; the
+roofline's kernel, the indexer, is timed inside a captured sequence like the step.  value = rows (tokens) / mean step time.  roofline.path_frac is the metric's own
 fraction: the whole path's algorithmic bytes (indexer inputs and keys, gathered latent
 entries, queries and outputs) over the step time, against 8 TB/s.  A decode run also times
 the 16K-token prefill workload (key prefill_c3: step time and bf16 MFMA fraction).
