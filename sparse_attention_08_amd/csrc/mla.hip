@@ -594,11 +594,15 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
 }
 
 // Merge split partials: out = sum_s 2^(lse_s - lse) o_s with lse = log2 sum_s 2^lse_s.
-// A workgroup of 256 threads merges 4 heads of one row (thread: 8 dims of one head);
-// workgroups are dealt to XCDs like the split workgroups of their row.
-constexpr int kCombHeads = 4;
+// A workgroup merges kCombHeads heads of one row, one wave per head (thread: 8 dims of one
+// head); workgroups are dealt to XCDs like the split workgroups of their row.
+#ifndef DSA_COMB_HEADS
+#define DSA_COMB_HEADS 4
+#endif
+constexpr int kCombHeads = DSA_COMB_HEADS;
+constexpr int kCombThreads = kCombHeads * kWave;
 constexpr int kMaxCombine = 32;   // largest split count
-__global__ __launch_bounds__(256) void mla_combine_kernel(int R, int H, int splits,
+__global__ __launch_bounds__(kCombThreads) void mla_combine_kernel(int R, int H, int splits,
                                                           const uint16_t *__restrict__ part_o,
                                                           const float *__restrict__ part_lse,
                                                           uint16_t *__restrict__ out,
@@ -720,7 +724,7 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
               : launch_mla_kernel<false, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
                                                 splits, o16, lse, part_o, part_lse, none);
   if (e != hipSuccess || splits == 1) return e;
-  mla_combine_kernel<<<8u * (unsigned)((R + 7) / 8) * (H / kCombHeads), 256, 0, stream>>>(
+  mla_combine_kernel<<<8u * (unsigned)((R + 7) / 8) * (H / kCombHeads), kCombThreads, 0, stream>>>(
       R, H, splits, part_o, part_lse, o16, lse);
   return hipGetLastError();
 }
