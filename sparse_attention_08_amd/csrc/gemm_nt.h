@@ -16,6 +16,13 @@
 
 namespace dsa {
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+struct GemmRow {
+  const uint16_t *ptr;
+  bool live;
+};
+
 constexpr int kGemmTile = 128;                      // columns of C per workgroup (N % 128 == 0)
 constexpr int kGemmTileM = 256;                     // rows of C per workgroup
 constexpr int kGemmK = 32;                          // contraction step
@@ -31,10 +38,12 @@ constexpr int kGemmAPer = kGemmTileM * 4 / kGemmThreads;   // A pieces per threa
 constexpr int kGemmBPer = kGemmTile * 4 / kGemmThreads;    // B pieces: 2
 
 // Prob: the problem, with (z = blockIdx.z, a batch index)
-//   int M, N, K                        (N % 128 == 0, K % 32 == 0)
-//   bool live(int m, int z)            row m of C is computed and written
-//   const uint16_t *a(int m, int z)    row m of A (K contiguous, 16-byte aligned); only
-//                                      called for live rows
+//   int M, N, K                        (N % 128 == 0, K % 32 == 0, K >= 32)
+//   GemmRow a(int m, int z)            {row m of A (K contiguous, 16-byte aligned), live}: live
+//                                      false when row m of C is not wanted (not computed, not
+//                                      written; the pointer is then never read); called for
+//                                      every m < M, best without branches, so that its loads
+//                                      for a thread's rows go out together
 //   const uint16_t *b(int n, int z)    row n of B (K contiguous, 16-byte aligned)
 //   uint16_t *c(int m, int z)          row m of C (16-byte aligned); only called for live rows
 // Grid: (N / 128, ceil(M / 256), batches).
@@ -42,6 +51,7 @@ template <class Prob>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 gemm_nt_kernel(Prob p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
+  __shared__ uint8_t live_row[kGemmTileM];
   auto opA = [&](int buf) { return lds + buf * kGemmOpA; };
   auto opB = [&](int buf) { return lds + 2 * kGemmOpA + buf * kGemmOpB; };
   const int t = threadIdx.x, lane = t & 63;
@@ -51,23 +61,29 @@ gemm_nt_kernel(Prob p) {
   const int m0 = blockIdx.y * kGemmTileM, n0 = blockIdx.x * kGemmTile, z = blockIdx.z;
   // thread t stages 16-byte piece (t & 3) of A rows (t >> 2) + 64 j and B rows (t >> 2) + 64 j
   const int lr = t >> 2, lc = t & 3;
+  // A row that is not live reads a B row instead: its products only reach C rows that are not
+  // written, and every load stays unconditional (no exec-masked branches in the loop, which
+  // make the compiler wait for the A loads before it issues the B loads).
   const uint16_t *arow[kGemmAPer], *brow[kGemmBPer];
-  bool any_live = false;
+#pragma unroll
+  for (int j = 0; j < kGemmBPer; ++j) brow[j] = p.b(n0 + lr + 64 * j, z) + 8 * lc;
+  bool lv[kGemmAPer], any_live = false;
 #pragma unroll
   for (int j = 0; j < kGemmAPer; ++j) {
     const int m = m0 + lr + 64 * j;
-    const bool lv = m < p.M && p.live(m, z);
-    any_live |= lv;
-    arow[j] = lv ? p.a(m, z) + 8 * lc : nullptr;
+    const GemmRow a = p.a(m < p.M ? m : p.M - 1, z);
+    lv[j] = m < p.M && a.live;
+    any_live |= lv[j];
+    arow[j] = lv[j] ? a.ptr + 8 * lc : brow[0];
   }
+  if (lc == 0)
 #pragma unroll
-  for (int j = 0; j < kGemmBPer; ++j) brow[j] = p.b(n0 + lr + 64 * j, z) + 8 * lc;
+    for (int j = 0; j < kGemmAPer; ++j) live_row[lr + 64 * j] = lv[j];
   if (!__syncthreads_or(any_live)) return;   // nothing of this block is wanted
   i32x4 ra[kGemmAPer], rb[kGemmBPer];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < kGemmAPer; ++j)
-      ra[j] = arow[j] ? *reinterpret_cast<const i32x4 *>(arow[j] + k0) : i32x4{0, 0, 0, 0};
+    for (int j = 0; j < kGemmAPer; ++j) ra[j] = *reinterpret_cast<const i32x4 *>(arow[j] + k0);
 #pragma unroll
     for (int j = 0; j < kGemmBPer; ++j) rb[j] = *reinterpret_cast<const i32x4 *>(brow[j] + k0);
   };
@@ -84,14 +100,8 @@ gemm_nt_kernel(Prob p) {
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  fetch(0);
-  stage(0);
-  __syncthreads();
-  const int steps = p.K / kGemmK;
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < steps) fetch((s + 1) * kGemmK);   // in flight during the products
-    // operands: A rows 128 wm + 16 i + c and B rows 64 wn + 16 j + c, k = 8 g .. 8 g + 7
+  // operands: A rows 128 wm + 16 i + c and B rows 64 wn + 16 j + c, k = 8 g .. 8 g + 7
+  auto products = [&](int buf) {
     bf16x8 bv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -102,21 +112,35 @@ gemm_nt_kernel(Prob p) {
           *reinterpret_cast<const bf16x8 *>(opA(buf) + (128 * wm + 16 * i + c) * kGemmRow + 16 * g);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], av, acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < steps) stage(buf ^ 1);   // that buffer's last readers passed the barrier below
+  };
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  // the last step is peeled off so that the loop body is one straight block
+  const int steps = p.K / kGemmK;
+  for (int s = 0; s + 1 < steps; ++s) {
+    fetch((s + 1) * kGemmK);   // in flight during the products
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products
+    products(s & 1);
+    __builtin_amdgcn_sched_barrier(0);   // and the stores (which wait for them) after
+    stage((s & 1) ^ 1);        // that buffer's last readers passed the barrier below
     __syncthreads();
   }
-  // result tile (i, j): lane (g, c) holds rows 128 wm + 16 i + 4 g + q, column 64 wn + 16 j + c
+  products((steps - 1) & 1);
+  __syncthreads();             // the result staging below overwrites both buffers
+  // result tile (i, j) (B is the products' first operand): lane (g, c) holds row
+  // 128 wm + 16 i + c, columns 64 wn + 16 j + 4 g + q, q = 0..3 -- one 8-byte LDS write
   uint8_t *out = lds;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint16_t *>(out + (128 * wm + 16 * i + 4 * g + q) * kGemmOutRow +
-                                      (64 * wn + 16 * j + c) * 2) = f32_to_bf16_bits(acc[i][j][q]);
+      *reinterpret_cast<i32x2 *>(out + (128 * wm + 16 * i + c) * kGemmOutRow +
+                                 (64 * wn + 16 * j + 4 * g) * 2) =
+          i32x2{(int)pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                (int)pack_bf16x2(acc[i][j][2], acc[i][j][3])};
   __syncthreads();
   // 16 threads per row, 16 bytes each
 #pragma unroll
@@ -124,7 +148,7 @@ gemm_nt_kernel(Prob p) {
     const int id = u * kGemmThreads + t;
     const int row = id >> 4, piece = id & 15;
     const int m = m0 + row;
-    if (m < p.M && p.live(m, z))
+    if (live_row[row])
       *reinterpret_cast<i32x4 *>(p.c(m, z) + n0 + 8 * piece) =
           *reinterpret_cast<const i32x4 *>(out + row * kGemmOutRow + 16 * piece);
   }

@@ -444,7 +444,8 @@ __global__ __launch_bounds__(256) void mha_reach_kernel(const int32_t *__restric
 // The decompression as a gather GEMM: C row m = compact row (b = m / lmax, s = m % lmax),
 // live while s < reach[b]; its A row is the latent c (first 512 of 576) at the cache row of
 // (b, s); B row n = row n of W_UK (z = 0) or W_UV (z = 1) viewed as [H * 128, 512]; C row m
-// of K_nope (z = 0) or V (z = 1), [B * lmax, H * 128].
+// of K_nope (z = 0) or V (z = 1), [B * lmax, H * 128].  The lookups are unconditional (b < B
+// and s >> 6 < max_pages for every m < M), so a thread's rows load them together.
 template <bool PAGED>
 struct MhaDecompress {
   int M, N, K;
@@ -455,15 +456,16 @@ struct MhaDecompress {
   const int32_t *reach;
   const uint16_t *w[2];
   uint16_t *dst[2];
-  __device__ bool live(int m, int) const { return m % lmax < reach[m / lmax]; }
-  __device__ const uint16_t *a(int m, int) const {
-    const int b = m / lmax, s = m % lmax;
+  __device__ GemmRow a(int m, int) const {
+    const int b = m / lmax, s = m - b * lmax;
     int64_t row;
     if constexpr (PAGED)
       row = (int64_t)page_table[(int64_t)b * max_pages + (s >> 6)] * 64 + (s & 63);
     else
       row = seq_start[b] + s;
-    return kv + row * 576;
+    // the live test reads the row lookup too (a cache row is never negative), so neither
+    // load can be moved under the test: a thread's lookups go out together, not one by one
+    return {kv + row * 576, (s < reach[b]) && (row >= 0)};
   }
   __device__ const uint16_t *b(int n, int z) const { return w[z] + (int64_t)n * 512; }
   __device__ uint16_t *c(int m, int z) const { return dst[z] + (int64_t)m * N; }

@@ -45,8 +45,7 @@ struct AbsorbProb {
   int M, N, K, H;
   const uint16_t *q, *wt;
   uint16_t *q_abs;
-  __device__ bool live(int, int) const { return true; }
-  __device__ const uint16_t *a(int m, int z) const { return q + ((int64_t)m * H + z) * 192; }
+  __device__ GemmRow a(int m, int z) const { return {q + ((int64_t)m * H + z) * 192, true}; }
   __device__ const uint16_t *b(int n, int z) const { return wt + ((int64_t)z * 512 + n) * 128; }
   __device__ uint16_t *c(int m, int z) const { return q_abs + ((int64_t)m * H + z) * 576; }
 };
@@ -56,8 +55,7 @@ struct ExpandProb {
   int M, N, K, H;
   const uint16_t *o, *w;
   uint16_t *out;
-  __device__ bool live(int, int) const { return true; }
-  __device__ const uint16_t *a(int m, int z) const { return o + ((int64_t)m * H + z) * 512; }
+  __device__ GemmRow a(int m, int z) const { return {o + ((int64_t)m * H + z) * 512, true}; }
   __device__ const uint16_t *b(int n, int z) const { return w + ((int64_t)z * 128 + n) * 512; }
   __device__ uint16_t *c(int m, int z) const { return out + ((int64_t)m * H + z) * 128; }
 };
