@@ -19,6 +19,10 @@
 // transposing LDS read (ds_read_b64_tr_b16), so the tile is stored once, row-major, for
 // both products.  Few-row (decode) batches split the slots over several workgroups; each
 // writes a normalised bf16 partial and its log-sum-exp, and a combine kernel merges them.
+// When a split batch is small enough (at most 256 workgroups either way), each (row, split)
+// gets two workgroups of 64 heads: four waves own the heads and four only share the
+// selection and the tile loads, so each CU moves half the query block and the tile loop
+// carries half the products.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 #include "topk_select.h"
@@ -125,6 +129,9 @@ hipError_t launch_mla_f32(const RowsHost &rh, bool paged, int H, int Dqk, int Dv
 #ifndef DSA_MLA_PV_PREFETCH
 #define DSA_MLA_PV_PREFETCH 3
 #endif
+#ifndef DSA_MLA_HEAD_GROUPS
+#define DSA_MLA_HEAD_GROUPS 2
+#endif
 #ifndef DSA_MLA_DEPTH
 #define DSA_MLA_DEPTH 4
 #endif
@@ -136,6 +143,7 @@ constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB = 36 DMA instructions o
 constexpr int kMlaWaves = 8;                 // 16 heads each
 constexpr int kMlaThreads = kMlaWaves * kWave;
 constexpr int kHeadsPerBlock = 128;
+constexpr int kMlaHeadGroups = DSA_MLA_HEAD_GROUPS;   // 1 or 2
 constexpr int kRing = DSA_MLA_DEPTH;          // LDS tile slots (kRing - 1 tiles in flight)
 constexpr int kMaxSlotsPerSplit = 2048;
 constexpr int kSlotRounds = kMaxSlotsPerSplit / kMlaThreads;   // 4
@@ -245,12 +253,16 @@ __device__ __forceinline__ void wait_younger(int younger) {
 // Without a split (many rows, one workgroup each) the rows are taken from the last to the
 // first: in a prefill batch later positions select more entries, so the longest rows start
 // first and the short ones fill the end of the grid.
-struct MlaCoord { int r, split; };
-__device__ __forceinline__ bool mla_coord(int bid, int R, int S, MlaCoord &c) {
+// With G head groups a (row, split) has G workgroups, each over 128 / G of the heads.
+struct MlaCoord { int r, split, group; };
+__device__ __forceinline__ bool mla_coord(int bid, int R, int S, int G, MlaCoord &c) {
   const int x = bid & 7, j = bid >> 3;
-  c.r = (j / S) * 8 + x;
-  c.split = j % S;
-  if (S == 1) c.r = R - 1 - c.r;   // the grid holds 8 * ceil(R / 8) >= R workgroups
+  const int sg = S * G;
+  c.r = (j / sg) * 8 + x;
+  const int rem = j % sg;
+  c.split = rem / G;
+  c.group = rem - c.split * G;
+  if (sg == 1) c.r = R - 1 - c.r;   // the grid holds 8 * ceil(R / 8) >= R workgroups
   return c.r >= 0 && c.r < R;
 }
 
@@ -270,8 +282,9 @@ constexpr size_t kSelListOff =
 static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing * kTileBytes,
               "selection scratch fits the tile ring");
 
-// One workgroup: all 128 heads of query row r over one split of its top-k slots.
-// Wave w owns heads 16w .. 16w+15 over the full contractions.  Per tile of 32 entries it
+// One workgroup: the heads of head group `group` (all 128, or 64 of them) of query row r over
+// one split of its top-k slots.  Wave w owns heads group * 128 / hgroups + 16w .. +15 over the
+// full contractions.  Per tile of 32 entries it
 // forms S^T = C . Q^T (entries as MFMA rows, 2 blocks of 16 entries x its 16 heads, q in
 // registers), runs the online softmax, and accumulates O^T += V^T . P^T over all 512
 // value dims, V^T read from the same LDS tile with the transposing LDS read.  Entry rows
@@ -285,7 +298,7 @@ static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing
 // the launch can preload them into registers).
 template <bool PAGED, bool SEL>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
-    int R, int splits, int k, int slots_per_split, int32_t *__restrict__ idx,
+    int R, int splits, int k, int slots_per_split, int hgroups, int32_t *__restrict__ idx,
     const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
     const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
@@ -295,12 +308,15 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared &sh = *reinterpret_cast<MlaShared *>(mla_smem);
   MlaCoord co;
-  if (!mla_coord(blockIdx.x, R, splits, co)) return;
+  if (!mla_coord(blockIdx.x, R, splits, hgroups, co)) return;
   const int r = co.r, split = co.split;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int h0 = wave * 16;
+  // waves below 8 / hgroups own 16 heads each; with two head groups waves 4-7 only take
+  // their part in the selection and in the tile loads
+  const bool mma = wave < kMlaWaves / hgroups;
+  const int h0 = co.group * (kHeadsPerBlock / hgroups) + (mma ? wave : 0) * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
   int32_t *idx_row = idx + (int64_t)r * k + slot_begin;   // read, or written when SEL
@@ -333,13 +349,13 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
             reinterpret_cast<uint32_t *>(sh.tiles[0] + kSelCoffOff));
         __syncthreads();
       }
-      load_q();
+      if (mma) load_q();
 #pragma unroll
       for (int j = 0; j < kSlotRounds; ++j) {
         const int t = j * kMlaThreads + threadIdx.x;
         const int slot = slot_begin + t;
         sv[j] = t < n_slots ? (n > k ? lst[slot] : (slot < n ? slot : -1)) : -1;
-        if (t < n_slots) idx_row[t] = sv[j];
+        if (t < n_slots && co.group == 0) idx_row[t] = sv[j];
       }
     } else {
       // the slot loads go out first (they need only the launch arguments), then the query
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
         sv[j] = t < n_slots ? idx_row[t] : -1;
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_q();
+      if (mma) load_q();
     }
     __builtin_amdgcn_sched_barrier(0);
     const RowsDev rows{row_seq, row_len, seq_start, page_table, max_pages};
@@ -541,13 +557,17 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     // (whose slot the next load overwrites)
     lds_barrier();
     const uint8_t *tile = sh.tiles[0] + slot_use;
-    f32x4 sc0, sc1;
-    scores(tile, sc0, sc1);
-    // the next tile's loads go out after the score product (measured faster than before it:
-    // the score loads of every wave start right at the barrier)
-    if (it + kAhead < n_tiles)
+    if (mma) {
+      f32x4 sc0, sc1;
+      scores(tile, sc0, sc1);
+      // the next tile's loads go out after the score product (measured faster than before
+      // it: the score loads of every wave start right at the barrier)
+      if (it + kAhead < n_tiles)
+        issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kAhead) * kTile, kv, td, n_dma, wave);
+      accumulate(tile, weights(sc0, sc1, it));
+    } else if (it + kAhead < n_tiles) {
       issue_tile(sh.tiles[0] + slot_issue, sh.crow + (it + kAhead) * kTile, kv, td, n_dma, wave);
-    accumulate(tile, weights(sc0, sc1, it));
+    }
     // ring slots advance by one tile and wrap (uniform, loop-carried: no division)
     slot_use = slot_use + kTileBytes == kRing * kTileBytes ? 0u : slot_use + kTileBytes;
     slot_issue = slot_issue + kTileBytes == kRing * kTileBytes ? 0u : slot_issue + kTileBytes;
@@ -555,6 +575,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   // every wave is done with the ring before it is reused for staging (no load is in flight:
   // the last iteration waited for all of them)
   lds_barrier();
+  if (!mma) return;
 
   // ---- epilogue.  Lane (g, c) holds head h0 + c, dims 16nb + 4g + i.  The wave stages its
   // 16 x 512 block in LDS (the ring is free now) and writes it with 16-byte stores.  The
@@ -679,7 +700,7 @@ size_t mla_workspace_bytes(int num_rows, int n_heads, int d_v, int k) {
 template <bool PAGED, bool SEL>
 static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const RowsDev &rows, int R,
                                     float sl2, const uint16_t *q16, const uint8_t *kv8,
-                                    int32_t *idx, int k, int per, int splits, uint16_t *o16,
+                                    int32_t *idx, int k, int per, int splits, int hg, uint16_t *o16,
                                     float *lse, uint16_t *part_o, float *part_lse,
                                     const MlaSel &sel) {
   static std::atomic<uint64_t> lds_set{0};
@@ -687,7 +708,7 @@ static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const Row
       ensure_dynamic_lds(&mla_bf16_kernel<PAGED, SEL>, (int)sizeof(MlaShared), lds_set);
   if (e != hipSuccess) return e;
   mla_bf16_kernel<PAGED, SEL><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
-      R, splits, k, per, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
+      R, splits, k, per, hg, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
       rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse, sel);
   return hipGetLastError();
 }
@@ -706,7 +727,9 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
     part_lse = reinterpret_cast<float *>(part_o + (size_t)rh.num_rows * splits * H * kDv);
   }
   const int R = rh.num_rows;
-  const unsigned grid = 8u * (unsigned)((R + 7) / 8) * splits;
+  // a split batch small enough gives each (row, split) two workgroups of 64 heads
+  const int hg = (kMlaHeadGroups > 1 && splits > 1 && 8 * ((R + 7) / 8) * splits * 2 <= 256) ? 2 : 1;
+  const unsigned grid = 8u * (unsigned)((R + 7) / 8) * splits * hg;
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
   const uint8_t *kv8 = static_cast<const uint8_t *>(kv);
   uint16_t *o16 = static_cast<uint16_t *>(out);
@@ -715,14 +738,14 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
   hipError_t e;
   if (sel)
     e = paged ? launch_mla_kernel<true, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                              splits, o16, lse, part_o, part_lse, *sel)
+                                              splits, hg, o16, lse, part_o, part_lse, *sel)
               : launch_mla_kernel<false, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                               splits, o16, lse, part_o, part_lse, *sel);
+                                               splits, hg, o16, lse, part_o, part_lse, *sel);
   else
     e = paged ? launch_mla_kernel<true, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                               splits, o16, lse, part_o, part_lse, none)
+                                               splits, hg, o16, lse, part_o, part_lse, none)
               : launch_mla_kernel<false, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                                splits, o16, lse, part_o, part_lse, none);
+                                                splits, hg, o16, lse, part_o, part_lse, none);
   if (e != hipSuccess || splits == 1) return e;
   mla_combine_kernel<<<8u * (unsigned)((R + 7) / 8) * (H / kCombHeads), kCombThreads, 0, stream>>>(
       R, H, splits, part_o, part_lse, o16, lse);
