@@ -390,6 +390,49 @@ def test_attention_decode_matches_separate_calls(idx_dtype, paged):
     assert np.array_equal(idx.cpu().numpy(), exp)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_head_groups_are_bit_identical(paged):
+    """A split batch of at most 8 rows (rows x splits x 2 <= 256 workgroups) gives each (row,
+    split) two 64-head attention workgroups; 16 rows give it one 128-head workgroup.  Each
+    head's wave runs the same operations either way, so the 8 rows alone and the same 8 rows
+    twice over in one 16-row batch must give bit-identical outputs, through the attention call
+    and through the one-call decode (whose attention also finishes the selection).  The 8-row
+    results are checked against the oracle by the tests above."""
+    wl = workloads.decode(FUSED_LENS, idx_dtype="fp8", paged=paged, seed=94, device=DEV,
+                          name=f"head_groups_{'paged' if paged else 'contig'}")
+    say(f"head groups {wl.name}")
+    idx = dsa.topk(gpu_indexer(wl), wl.row_len, wl.topk, wl.max_row_len)
+    o8, l8 = gpu_mla(wl, idx)
+    wl2 = workloads.Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+    for f in ("row_seq", "row_len", "q_idx", "q_scale", "w", "q"):
+        setattr(wl2, f, torch.cat([getattr(wl, f), getattr(wl, f)]).contiguous())
+    o16, l16 = gpu_mla(wl2, torch.cat([idx, idx]).contiguous())
+    for h in (0, 1):
+        assert torch.equal(o16[8 * h:8 * h + 8], o8)
+        assert torch.equal(l16[8 * h:8 * h + 8], l8)
+
+    def one_call(w):
+        R = w.num_rows
+        ws = torch.empty(max(dsa.sparse_attention_decode_workspace_size(
+            R, w.max_row_len, w.q_idx.dtype, w.topk, w.H, w.D_v), 1), dtype=torch.uint8,
+            device=DEV)
+        logits = torch.empty((R, w.max_row_len), dtype=torch.float32, device=DEV)
+        ix = torch.empty((R, w.topk), dtype=torch.int32, device=DEV)
+        lse = torch.empty((R, w.H), dtype=torch.float32, device=DEV)
+        out = dsa.sparse_attention_decode(dev_rows(w), w.q_idx, w.w, w.k_idx, logits, w.topk, w.q,
+                                          w.kv, w.scale, w.D_v, idx=ix, lse=lse,
+                                          q_scale=w.q_scale, k_scale=w.k_scale, ws=ws)
+        return out, lse, ix
+
+    a8, b8, i8 = one_call(wl)
+    assert torch.equal(i8, idx) and torch.equal(a8, o8) and torch.equal(b8, l8)
+    a16, b16, i16 = one_call(wl2)
+    for h in (0, 1):
+        assert torch.equal(i16[8 * h:8 * h + 8], idx)
+        assert torch.equal(a16[8 * h:8 * h + 8], o8)
+        assert torch.equal(b16[8 * h:8 * h + 8], l8)
+
+
 @pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
 def test_attention_decode_all_scores_tied(idx_dtype):
     """Zero head weights make every score +0: every position of a row ties, the rows' survivor
