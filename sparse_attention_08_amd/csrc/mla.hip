@@ -283,8 +283,8 @@ static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing
               "selection scratch fits the tile ring");
 
 // One workgroup: the heads of head group `group` (all 128, or 64 of them) of query row r over
-// one split of its top-k slots.  Wave w owns heads group * 128 / hgroups + 16w .. +15 over the
-// full contractions.  Per tile of 32 entries it
+// one split of its top-k slots.  Wave w owns heads group * 128 / HG + 16w .. +15 over the full
+// contractions.  Per tile of 32 entries it
 // forms S^T = C . Q^T (entries as MFMA rows, 2 blocks of 16 entries x its 16 heads, q in
 // registers), runs the online softmax, and accumulates O^T += V^T . P^T over all 512
 // value dims, V^T read from the same LDS tile with the transposing LDS read.  Entry rows
@@ -296,9 +296,9 @@ static_assert(kSelListOff + sizeof(int32_t) * kMaxSlotsPerSplit <= (size_t)kRing
 //
 // The leading arguments are the ones the prologue needs first (scalars and pointers, so
 // the launch can preload them into registers).
-template <bool PAGED, bool SEL>
+template <bool PAGED, bool SEL, int HG>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
-    int R, int splits, int k, int slots_per_split, int hgroups, int32_t *__restrict__ idx,
+    int R, int splits, int k, int slots_per_split, int32_t *__restrict__ idx,
     const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_len, const int64_t *__restrict__ seq_start,
     const int32_t *__restrict__ page_table, int max_pages, float scale_log2,
@@ -308,15 +308,16 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared &sh = *reinterpret_cast<MlaShared *>(mla_smem);
   MlaCoord co;
-  if (!mla_coord(blockIdx.x, R, splits, hgroups, co)) return;
+  static_assert(HG == 1 || HG == 2, "one or two head groups");
+  if (!mla_coord(blockIdx.x, R, splits, HG, co)) return;
   const int r = co.r, split = co.split;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  // waves below 8 / hgroups own 16 heads each; with two head groups waves 4-7 only take
-  // their part in the selection and in the tile loads
-  const bool mma = wave < kMlaWaves / hgroups;
-  const int h0 = co.group * (kHeadsPerBlock / hgroups) + (mma ? wave : 0) * 16;
+  // waves below 8 / HG own 16 heads each; with two head groups waves 4-7 only take their
+  // part in the selection and in the tile loads (one head group: a compile-time true)
+  const bool mma = HG == 1 || wave < kMlaWaves / HG;
+  const int h0 = co.group * (kHeadsPerBlock / HG) + (mma ? wave : 0) * 16;
   const int slot_begin = split * slots_per_split;
   const int n_slots = max(0, min(k, slot_begin + slots_per_split) - slot_begin);
   int32_t *idx_row = idx + (int64_t)r * k + slot_begin;   // read, or written when SEL
@@ -697,18 +698,18 @@ size_t mla_workspace_bytes(int num_rows, int n_heads, int d_v, int k) {
   return (size_t)num_rows * splits * n_heads * (sizeof(uint16_t) * (size_t)d_v + sizeof(float));
 }
 
-template <bool PAGED, bool SEL>
+template <bool PAGED, bool SEL, int HG>
 static hipError_t launch_mla_kernel(unsigned grid, hipStream_t stream, const RowsDev &rows, int R,
                                     float sl2, const uint16_t *q16, const uint8_t *kv8,
-                                    int32_t *idx, int k, int per, int splits, int hg, uint16_t *o16,
+                                    int32_t *idx, int k, int per, int splits, uint16_t *o16,
                                     float *lse, uint16_t *part_o, float *part_lse,
                                     const MlaSel &sel) {
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e =
-      ensure_dynamic_lds(&mla_bf16_kernel<PAGED, SEL>, (int)sizeof(MlaShared), lds_set);
+      ensure_dynamic_lds(&mla_bf16_kernel<PAGED, SEL, HG>, (int)sizeof(MlaShared), lds_set);
   if (e != hipSuccess) return e;
-  mla_bf16_kernel<PAGED, SEL><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
-      R, splits, k, per, hg, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
+  mla_bf16_kernel<PAGED, SEL, HG><<<grid, kMlaThreads, sizeof(MlaShared), stream>>>(
+      R, splits, k, per, idx, q16, rows.row_seq, rows.row_len, rows.seq_start, rows.page_table,
       rows.max_pages, sl2, kv8, o16, lse, part_o, part_lse, sel);
   return hipGetLastError();
 }
@@ -735,17 +736,18 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
   uint16_t *o16 = static_cast<uint16_t *>(out);
   const float sl2 = scale * kLog2e;
   const MlaSel none{};
+  const MlaSel &sl = sel ? *sel : none;
   hipError_t e;
-  if (sel)
-    e = paged ? launch_mla_kernel<true, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                              splits, hg, o16, lse, part_o, part_lse, *sel)
-              : launch_mla_kernel<false, true>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                               splits, hg, o16, lse, part_o, part_lse, *sel);
+#define DSA_LAUNCH_MLA(P, S, G)                                                                 \
+  launch_mla_kernel<P, S, G>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per, splits, o16, lse, \
+                             part_o, part_lse, sl)
+  if (hg == 2)
+    e = sel ? (paged ? DSA_LAUNCH_MLA(true, true, 2) : DSA_LAUNCH_MLA(false, true, 2))
+            : (paged ? DSA_LAUNCH_MLA(true, false, 2) : DSA_LAUNCH_MLA(false, false, 2));
   else
-    e = paged ? launch_mla_kernel<true, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                               splits, hg, o16, lse, part_o, part_lse, none)
-              : launch_mla_kernel<false, false>(grid, stream, rows, R, sl2, q16, kv8, idx, k, per,
-                                                splits, hg, o16, lse, part_o, part_lse, none);
+    e = sel ? (paged ? DSA_LAUNCH_MLA(true, true, 1) : DSA_LAUNCH_MLA(false, true, 1))
+            : (paged ? DSA_LAUNCH_MLA(true, false, 1) : DSA_LAUNCH_MLA(false, false, 1));
+#undef DSA_LAUNCH_MLA
   if (e != hipSuccess || splits == 1) return e;
   mla_combine_kernel<<<8u * (unsigned)((R + 7) / 8) * (H / kCombHeads), kCombThreads, 0, stream>>>(
       R, H, splits, part_o, part_lse, o16, lse);
