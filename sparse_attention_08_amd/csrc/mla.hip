@@ -720,6 +720,17 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
                               const void *kv, int32_t *idx, int k, void *out, float *lse,
                               int splits, void *ws, const MlaSel *sel, hipStream_t stream) {
   RowsDev rows{rh.row_seq, rh.row_len, rh.seq_start, rh.page_table, rh.max_pages};
+  const int R = rh.num_rows;
+  // A split batch small enough gives each (row, split) two workgroups of 64 heads.  A batch
+  // of 8 or more splits per row that is too large for that trades half its splits for the two
+  // head groups (half the partials to write and merge; measured faster at 32 rows of up to
+  // 64K, the same at 64 rows of 8K with 4 splits, so batches of fewer splits keep them).
+  int hg = (kMlaHeadGroups > 1 && splits > 1 && 8 * ((R + 7) / 8) * splits * 2 <= 256) ? 2 : 1;
+  if (hg == 1 && kMlaHeadGroups > 1 && splits >= 8 &&
+      8 * ((R + 7) / 8) * (splits / 2) * 2 <= 256) {
+    splits /= 2;
+    hg = 2;
+  }
   const int per = (((k + splits - 1) / splits) + kTile - 1) / kTile * kTile;
   uint16_t *part_o = nullptr;
   float *part_lse = nullptr;
@@ -727,9 +738,6 @@ static hipError_t launch_bf16(const RowsHost &rh, bool paged, int H, float scale
     part_o = static_cast<uint16_t *>(ws);
     part_lse = reinterpret_cast<float *>(part_o + (size_t)rh.num_rows * splits * H * kDv);
   }
-  const int R = rh.num_rows;
-  // a split batch small enough gives each (row, split) two workgroups of 64 heads
-  const int hg = (kMlaHeadGroups > 1 && splits > 1 && 8 * ((R + 7) / 8) * splits * 2 <= 256) ? 2 : 1;
   const unsigned grid = 8u * (unsigned)((R + 7) / 8) * splits * hg;
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
   const uint8_t *kv8 = static_cast<const uint8_t *>(kv);

@@ -392,24 +392,24 @@ def test_attention_decode_matches_separate_calls(idx_dtype, paged):
 
 @pytest.mark.parametrize("paged", [False, True])
 def test_head_groups_are_bit_identical(paged):
-    """A split batch of at most 8 rows (rows x splits x 2 <= 256 workgroups) gives each (row,
-    split) two 64-head attention workgroups; 16 rows give it one 128-head workgroup.  Each
-    head's wave runs the same operations either way, so the 8 rows alone and the same 8 rows
-    twice over in one 16-row batch must give bit-identical outputs, through the attention call
-    and through the one-call decode (whose attention also finishes the selection).  The 8-row
-    results are checked against the oracle by the tests above."""
+    """The decode attention gives a (row, split) two 64-head workgroups when the batch is small
+    enough (16 rows: their 16 splits halved to 8, with two head groups) and one 128-head
+    workgroup otherwise (33 rows: 8 splits, one group).  Each head's wave runs the same
+    operations either way, so with the same 8 splits per row the outputs of the same rows must
+    be bit-identical, through the attention call and through the one-call decode (whose
+    attention also finishes the selection in the 16-row batch).  The rows' results are
+    checked against the oracle by the tests above."""
     wl = workloads.decode(FUSED_LENS, idx_dtype="fp8", paged=paged, seed=94, device=DEV,
                           name=f"head_groups_{'paged' if paged else 'contig'}")
     say(f"head groups {wl.name}")
     idx = dsa.topk(gpu_indexer(wl), wl.row_len, wl.topk, wl.max_row_len)
-    o8, l8 = gpu_mla(wl, idx)
-    wl2 = workloads.Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
-    for f in ("row_seq", "row_len", "q_idx", "q_scale", "w", "q"):
-        setattr(wl2, f, torch.cat([getattr(wl, f), getattr(wl, f)]).contiguous())
-    o16, l16 = gpu_mla(wl2, torch.cat([idx, idx]).contiguous())
-    for h in (0, 1):
-        assert torch.equal(o16[8 * h:8 * h + 8], o8)
-        assert torch.equal(l16[8 * h:8 * h + 8], l8)
+
+    def repeat(n, extra):   # the 8 rows n times over, then `extra` copies of row 0
+        w2 = workloads.Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+        for f in ("row_seq", "row_len", "q_idx", "q_scale", "w", "q"):
+            t = getattr(wl, f)
+            setattr(w2, f, torch.cat([t] * n + [t[:1]] * extra).contiguous())
+        return w2, torch.cat([idx] * n + [idx[:1]] * extra).contiguous()
 
     def one_call(w):
         R = w.num_rows
@@ -424,13 +424,18 @@ def test_head_groups_are_bit_identical(paged):
                                           q_scale=w.q_scale, k_scale=w.k_scale, ws=ws)
         return out, lse, ix
 
-    a8, b8, i8 = one_call(wl)
-    assert torch.equal(i8, idx) and torch.equal(a8, o8) and torch.equal(b8, l8)
-    a16, b16, i16 = one_call(wl2)
-    for h in (0, 1):
-        assert torch.equal(i16[8 * h:8 * h + 8], idx)
-        assert torch.equal(a16[8 * h:8 * h + 8], o8)
-        assert torch.equal(b16[8 * h:8 * h + 8], l8)
+    w16, i16 = repeat(2, 0)    # 16 rows: two head groups
+    w33, i33 = repeat(4, 1)    # 33 rows: one head group
+    assert w16.num_rows == 16 and w33.num_rows == 33
+    o16, l16 = gpu_mla(w16, i16)
+    o33, l33 = gpu_mla(w33, i33)
+    assert torch.equal(o16, o33[:16]) and torch.equal(l16, l33[:16])
+    assert torch.equal(o16[:8], o16[8:]) and torch.equal(o33[:8], o33[16:24])
+    a16, b16, x16 = one_call(w16)
+    a33, b33, x33 = one_call(w33)
+    assert torch.equal(x16, i16) and torch.equal(x33, i33)
+    assert torch.equal(a16, o16) and torch.equal(b16, l16)
+    assert torch.equal(a33, o33) and torch.equal(b33, l33)
 
 
 @pytest.mark.parametrize("idx_dtype", ["bf16", "fp8"])
